@@ -1,0 +1,224 @@
+"""Pins for oracle/gemm.py and oracle/bounds.py, independent of the oracle itself.
+
+* brute force: a pure-Python triple loop over exact rationals (fractions) on
+  tiny inputs, for fp16, int8 and the tile-wise indexed form;
+* the int8 epilogue checked against exact rational rounding to float32;
+* closed forms: one-hot weights select a column of A, zero weights give zero,
+  2:4 with positions (0, 1) everywhere is a dense GEMM on a column subset;
+* the two tile-wise formulations (masked dense vs indexed) agree;
+* planted mistakes in copies of the oracle functions make these checks fail.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------- helpers
+def exact_product(A, W):
+    """Pure-Python sum of exact rational products: the definition of A . W."""
+    M, K = len(A), len(A[0])
+    N = len(W[0])
+    Af = [[Fraction(float(A[m][k])) for k in range(K)] for m in range(M)]
+    Wf = [[Fraction(float(W[k][n])) for n in range(N)] for k in range(K)]
+    return [[sum((Af[m][k] * Wf[k][n] for k in range(K)), Fraction(0)) for n in range(N)]
+            for m in range(M)]
+
+
+def check_gemm_bruteforce(gemm_fn, seed=0, trials=6):
+    """True iff gemm_fn(A, W) matches the exact rational product to f64 accuracy."""
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        M, K, N = rng.integers(1, 9), 4 * rng.integers(1, 6), rng.integers(1, 9)
+        case = wl.random_24_f16(rng, M, K, N, std_w=0.5)
+        A, Wp = case["A"], case["Wp"]
+        got = gemm_fn(A, Wp)
+        ex = exact_product(A.tolist(), Wp.tolist())
+        S = np.abs(A.astype(np.float64)) @ np.abs(Wp.astype(np.float64))
+        for m in range(M):
+            for n in range(N):
+                if abs(Fraction(float(got[m, n])) - ex[m][n]) > Fraction(K * 2.0 ** -52 * S[m, n]):
+                    return False
+    return True
+
+
+def round_to_f32(x: Fraction):
+    """Nearest float32 to the rational x, ties to even (pure rational search)."""
+    f = np.float32(float(x))
+    best = None
+    for cand in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        d = abs(Fraction(float(cand)) - x)
+        if best is None or d < best[0] or (d == best[0] and
+                                           (int(cand.view(np.uint32)) & 1) == 0):
+            best = (d, cand)
+    return best[1]
+
+
+# ---------------------------------------------------------------- brute force
+def test_f16_gemm_matches_exact_rationals():
+    assert check_gemm_bruteforce(oracle.ref_gemm_f64)
+
+
+def test_f16_output_is_rne_of_exact_value():
+    rng = np.random.default_rng(1)
+    case = wl.random_24_f16(rng, 5, 16, 7, std_w=0.3)
+    C64, C16 = oracle.ref_gemm_f16(case["A"], case["Wp"])
+    # the fp16 result is within half an ulp of C64 (nearest), checked by neighbours
+    for c64, c16 in zip(C64.ravel(), C16.ravel()):
+        lo = np.nextafter(c16, np.float16(-np.inf))
+        hi = np.nextafter(c16, np.float16(np.inf))
+        d = abs(float(c16) - c64)
+        assert d <= abs(float(lo) - c64) and d <= abs(float(hi) - c64)
+
+
+def test_i8_accumulator_matches_python_ints():
+    rng = np.random.default_rng(2)
+    for _ in range(5):
+        M, K, N = rng.integers(1, 7), 4 * rng.integers(1, 9), rng.integers(1, 7)
+        case = wl.random_24_i8(rng, M, K, N)
+        acc = oracle.ref_gemm_i8(case["A"], case["Wp"])
+        assert acc.dtype == np.int32
+        A, W = case["A"].astype(int).tolist(), case["Wp"].astype(int).tolist()
+        for m in range(M):
+            for n in range(N):
+                assert acc[m, n] == sum(A[m][k] * W[k][n] for k in range(K))
+
+
+def test_i8_scaled_output_is_two_roundings():
+    rng = np.random.default_rng(3)
+    case = wl.random_24_i8(rng, 4, 64, 6)
+    acc = oracle.ref_gemm_i8(case["A"], case["Wp"])
+    C = oracle.ref_gemm_i8(case["A"], case["Wp"], case["scale"])
+    assert C.dtype == np.float32
+    for m in range(4):
+        for n in range(6):
+            a32 = round_to_f32(Fraction(int(acc[m, n])))
+            want = round_to_f32(Fraction(float(a32)) * Fraction(float(case["scale"][n])))
+            assert C[m, n].view(np.uint32) == want.view(np.uint32)
+
+
+def test_i8_large_k_accumulator_still_exact():
+    # K = 4096 with extreme values: |acc| up to 2048 * 127 * 127 > 2^24
+    K, N = 4096, 3
+    A = np.full((2, K), 127, dtype=np.int8)
+    A[1] = -127
+    W = np.zeros((K, N), dtype=np.int8)
+    W[0::4] = 127
+    W[1::4] = 127
+    acc = oracle.ref_gemm_i8(A, W)
+    assert acc[0, 0] == 2048 * 127 * 127 and acc[1, 2] == -2048 * 127 * 127
+
+
+def test_tw_indexed_matches_exact_rationals():
+    rng = np.random.default_rng(4)
+    M, K, N, G = 3, 12, 8, 4
+    case = wl.random_tw_f16(rng, M, K, N, G, [0.5, 0.3])
+    packed = oracle.ref_tw_pack(case["Wp"], G)
+    got = oracle.ref_tw_gemm_indexed(case["A"], packed, N, G)
+    ex = exact_product(case["A"].tolist(), case["Wp"].tolist())
+    for m in range(M):
+        for n in range(N):
+            assert abs(Fraction(float(got[m, n])) - ex[m][n]) < Fraction(1, 2 ** 40)
+
+
+# ---------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("dtype", [np.float16, np.int8])
+def test_one_hot_selects_column(dtype):
+    rng = np.random.default_rng(5)
+    case = wl.one_hot_24(rng, 9, 64, 40, dtype=dtype)
+    if dtype == np.int8:
+        C = oracle.ref_gemm_i8(case["A"], case["Wp"])
+        assert np.array_equal(C, case["A"][:, case["k_of_n"]].astype(np.int32))
+    else:
+        _, C16 = oracle.ref_gemm_f16(case["A"], case["Wp"])
+        assert np.array_equal(C16.view(np.uint16), case["A"][:, case["k_of_n"]].view(np.uint16))
+
+
+def test_zero_weights_give_zero():
+    A = np.ones((3, 8), np.float16)
+    assert not oracle.ref_gemm_f64(A, np.zeros((8, 5), np.float16)).any()
+
+
+def test_fixed_positions_reduce_to_dense_subset():
+    # 2:4 with kept positions (0, 1) in every group equals a dense GEMM on the
+    # columns {4g, 4g+1} of A against the compressed rows.
+    rng = np.random.default_rng(6)
+    M, K, N = 7, 32, 5
+    A = wl.f16_normal(rng, (M, K))
+    dense_half = wl.f16_normal(rng, (K // 2, N))
+    Wp = np.zeros((K, N), np.float16)
+    Wp[0::4] = dense_half[0::2]
+    Wp[1::4] = dense_half[1::2]
+    sub = np.sort(np.concatenate([np.arange(0, K, 4), np.arange(1, K, 4)]))
+    want = A[:, sub].astype(np.float64) @ dense_half.astype(np.float64)
+    np.testing.assert_allclose(oracle.ref_gemm_f64(A, Wp), want, rtol=0, atol=1e-12)
+
+
+def test_tw_indexed_equals_masked_dense():
+    rng = np.random.default_rng(7)
+    case = wl.random_tw_f16(rng, 33, 96, 64, 16, [0.2, 0.9, 0.0, 0.5])
+    packed = oracle.ref_tw_pack(case["Wp"], 16)
+    a = oracle.ref_tw_gemm_indexed(case["A"], packed, 64, 16)
+    b = oracle.ref_gemm_f64(case["A"], case["Wp"])
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+    assert not a[:, 32:48].any()  # the empty tile's window is zero
+
+
+def test_transpose():
+    A = np.arange(12, dtype=np.float16).reshape(3, 4)
+    At = oracle.ref_transpose(A)
+    assert At.shape == (4, 3) and At.flags["C_CONTIGUOUS"] and At[2, 1] == A[1, 2]
+
+
+# ---------------------------------------------------------------- bounds
+def test_strict_bound_catches_one_dropped_term():
+    rng = np.random.default_rng(8)
+    case = wl.random_24_f16(rng, 64, 768, 64)
+    C_ref, C16 = oracle.ref_gemm_f16(case["A"], case["Wp"])
+    S = oracle.ref_abs_gemm(case["A"], case["Wp"])
+    assert oracle.strict_ok_f16(C16, C_ref, S, 384)
+    assert oracle.loose_ok(C16, C_ref)
+    # drop a single product from one output: the loose bound misses it, the strict one does not
+    Wd = case["Wp"].copy()
+    k = int(np.argmax(np.abs(case["Wp"][:, 0].astype(np.float64))))
+    Wd[k, 0] = 0
+    _, Cd = oracle.ref_gemm_f16(case["A"], Wd)
+    assert not oracle.strict_ok_f16(Cd, C_ref, S, 384)
+
+
+def test_loose_rejects_nan():
+    assert not oracle.loose_ok(np.array([np.nan, 1.0]), np.array([1.0, 1.0]))
+    assert oracle.loose_err(np.zeros(3), np.zeros(3)) == 0.0
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _mut_transposed(A, W):
+    return oracle.ref_gemm_f64(A, np.asarray(W)[::-1])
+
+
+def _mut_dropped_last_k(A, W):
+    W = np.array(W, copy=True)
+    W[-1] = 0
+    return oracle.ref_gemm_f64(A, W)
+
+
+def _mut_sign(A, W):
+    C = oracle.ref_gemm_f64(A, W)
+    C[0, 0] = -C[0, 0]
+    return C
+
+
+def _mut_f32_accumulate(A, W):
+    return (np.asarray(A).astype(np.float16) @ np.asarray(W).astype(np.float16)).astype(np.float64)
+
+
+@pytest.mark.parametrize("mutant", [_mut_transposed, _mut_dropped_last_k, _mut_sign,
+                                    _mut_f32_accumulate])
+def test_bruteforce_catches_planted_mistakes(mutant):
+    assert not check_gemm_bruteforce(mutant)
