@@ -1,0 +1,286 @@
+"""Benchmark of the structured-sparse weight GEMM on one MI355X.
+
+Default run (the headline line): the 2:4 int8 GEMM at the ViT-Base MLP fc1
+shape -- A [64*197 = 12608 x 768] int8, W [768 x 3072] int8 pruned 2:4 along
+K, int32 accumulate, per-output-channel fp32 scale, fp32 output.  One step is
+one w24_gemm_i8 launch over that batch with every input already resident in
+HBM.  Input/output sets rotate over more than twice the 256 MB Infinity Cache
+so every step streams from HBM.  The same-shape dense int8 GEMM (unpruned W)
+is timed the same way for the speedup.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --all        # one JSON line per workload and kernel (table mode)
+
+stdout carries exactly one JSON line in the default mode; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOPS/TOPS of sparse GEMM + speedup vs dense MFMA GEMM, same shape"
+CACHE_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_w24_gemm_i8_vit_base_fc1.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "structured_sparse_gemm_w24_amd", "csrc", "kernels", f)
+                  for f in ("gemm.hip", "common.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """Per-launch HBM bytes measured with rocprofv3 counters for the current kernel source, else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sha") != kernel_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream the kernels are launched on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __call__(self, fn, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(steps):
+            fn(i)
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps  # ms per call
+
+
+def rotation(bytes_per_set):
+    return max(2, int(np.ceil(2 * CACHE_BYTES / max(1, bytes_per_set))))
+
+
+# ---------------------------------------------------------------- workloads
+def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
+    dev = torch.device("cuda")
+    M, K, N = c["M"], c["K"], c["N"]
+    vals, meta = ssg.w24_pack_i8(c["Wp"])
+    sets_bytes = perf.w24_bytes(M, N, K, 1, 1, 4, scale=True)
+    R = rotation(sets_bytes) if rotate else 1
+    A0 = torch.from_numpy(c["A"]).to(dev)
+    sets = []
+    for r in range(R):
+        sets.append(dict(A=A0.clone() if r else A0, vals=torch.from_numpy(vals).to(dev),
+                         meta=torch.from_numpy(meta.view(np.int32)).to(dev),
+                         scale=torch.from_numpy(c["scale"]).to(dev),
+                         C=torch.empty((M, N), dtype=torch.float32, device=dev),
+                         Wt=torch.from_numpy(np.ascontiguousarray(c["W"].T)).to(dev)))
+    sp = lambda i: ssg.w24_gemm_i8(sets[i % R]["A"], sets[i % R]["vals"], sets[i % R]["meta"],
+                                   sets[i % R]["scale"], out=sets[i % R]["C"])
+    de = lambda i: ssg.dense_gemm_i8(sets[i % R]["A"], sets[i % R]["Wt"], sets[i % R]["scale"],
+                                     out=sets[i % R]["C"])
+    t_sp = timer(sp, steps, warmup)
+    t_de = timer(de, steps, warmup)
+    return dict(t_sparse_ms=t_sp, t_dense_ms=t_de, rotate_sets=R, sets=sets)
+
+
+def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
+    dev = torch.device("cuda")
+    M, K, N = c["M"], c["K"], c["N"]
+    vals, meta = ssg.w24_pack_f16(c["Wp"])
+    R = rotation(perf.w24_bytes(M, N, K, 2, 2, 2)) if rotate else 1
+    sets = [dict(A=torch.from_numpy(c["A"]).to(dev), vals=torch.from_numpy(vals).to(dev),
+                 meta=torch.from_numpy(meta.view(np.int32)).to(dev),
+                 C=torch.empty((M, N), dtype=torch.float16, device=dev),
+                 Wt=torch.from_numpy(np.ascontiguousarray(c["W"].T)).to(dev)) for _ in range(R)]
+    sp = lambda i: ssg.w24_gemm_f16(sets[i % R]["A"], sets[i % R]["vals"], sets[i % R]["meta"], out=sets[i % R]["C"])
+    de = lambda i: ssg.dense_gemm_f16(sets[i % R]["A"], sets[i % R]["Wt"], out=sets[i % R]["C"])
+    tm = lambda i: torch.matmul(sets[i % R]["A"], sets[i % R]["Wt"].T)
+    return dict(t_sparse_ms=timer(sp, steps, warmup), t_dense_ms=timer(de, steps, warmup),
+                t_torch_ms=timer(tm, steps, warmup), rotate_sets=R)
+
+
+def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
+    dev = torch.device("cuda")
+    M, K, N, G = c["M"], c["K"], c["N"], c["G"]
+    host = ssg.tw_pack_f16(c["Wp"], G)
+    union = int(np.unique(host.offset_k).size)
+    bytes_ = perf.tw_bytes(M, N, union, host.vals.size, host.offset_k.size, host.offset_n.size, host.T)
+    R = rotation(bytes_ + M * K * 2) if rotate else 1
+    A = torch.from_numpy(c["A"]).to(dev)
+    sets = [dict(A=A, At=ssg.ssg_transpose_f16(A), packed=host.to(dev),
+                 C=torch.empty((M, N), dtype=torch.float16, device=dev),
+                 Wt=torch.from_numpy(np.ascontiguousarray(c["W"].T)).to(dev)) for _ in range(R)]
+    sp = lambda i: ssg.tw_gemm_f16(sets[i % R]["At"], sets[i % R]["packed"], out=sets[i % R]["C"])
+    tr = lambda i: ssg.ssg_transpose_f16(sets[i % R]["A"], out=sets[i % R]["At"])
+    de = lambda i: ssg.dense_gemm_f16(sets[i % R]["A"], sets[i % R]["Wt"], out=sets[i % R]["C"])
+    nnz = int((np.diff(host.k_ptr) * np.diff(host.n_ptr)).sum())
+    return dict(t_sparse_ms=timer(sp, steps, warmup), t_transpose_ms=timer(tr, steps, warmup),
+                t_dense_ms=timer(de, steps, warmup), rotate_sets=R, bytes=bytes_,
+                ops=perf.tw_ops(M, nnz), union_rows=union)
+
+
+# ---------------------------------------------------------------- cpu baseline
+def cpu_baseline(c, perf, budget_s=12.0):
+    """The oracle as it stands, on the host cores, over a bounded number of full repetitions."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ref_gemm_i8(c["A"], c["Wp"], c["scale"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 10:
+            break
+    nz, _ = perf.w24_ops(c["M"], c["N"], c["K"])
+    return {"value": nz * reps / el / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"full {c['M']}x{c['K']}x{c['N']} int8 GEMM + epilogue (numpy float64 BLAS), "
+                      f"{reps} repetition(s), {el:.1f} s; host {platform.processor() or platform.machine()}"}
+
+
+# ---------------------------------------------------------------- main
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--all", action="store_true", help="table mode: every workload and kernel")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--warm", action="store_true", help="one input set (cache-resident) instead of rotating")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {a.gpus}); the sparse GEMM "
+              "is measured on one GPU's share and multi-GPU sharding is not part of it", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import structured_sparse_gemm_w24_amd as ssg
+    import workloads as wl
+    from structured_sparse_gemm_w24_amd import perf
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    timer = Timer(torch)
+    log("device", ssg.ssg_device_arch())
+    if a.all:
+        return table(a, torch, ssg, perf, wl, timer)
+
+    c = wl.make_cfg2()
+    M, K, N = c["M"], c["K"], c["N"]
+    log(f"workload vit_base_mlp_fc1 2:4 int8 {M}x{K}x{N}, steps {a.steps}, warmup {a.warmup}")
+    r = w24_i8_case(torch, ssg, perf, c, a.steps, a.warmup, timer, rotate=not a.warm)
+    nz, de = perf.w24_ops(M, N, K)
+    t = r["t_sparse_ms"] / 1e3
+    bytes_ = perf.w24_bytes(M, N, K, 1, 1, 4, scale=True)
+    achieved = bytes_ / t / 1e9
+    traffic = read_traffic()
+    line = {
+        "metric": METRIC,
+        "value": nz / t / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": r["t_sparse_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded; ViT-Base MLP fc1 shape, int8 U[-127,127] activations, "
+                "round(N(0,32)) weights 2:4-pruned by magnitude, U(1e-3,1e-2) scales)",
+        "config": {"workload": "vit_base_mlp_fc1_w24_i8", "M": M, "K": K, "N": N,
+                   "pattern": "2:4 along K", "accumulate": "int32", "output": "fp32 (per-channel scale)",
+                   "inputs": "rotating HBM-resident sets" if not a.warm else "one cache-resident set",
+                   "rotate_sets": r["rotate_sets"]},
+        "dense_equivalent_tops": de / t / 1e12,
+        "speedup_vs_dense": perf.speedup(r["t_dense_ms"], r["t_sparse_ms"]),
+        "dense_i8_ms": r["t_dense_ms"],
+        "roofline": perf.roofline(achieved, perf.PEAK_HBM_GBS, "GB/s", "hbm", traffic),
+        "cpu_baseline": None,
+    }
+    del r
+    torch.cuda.empty_cache()
+    if not a.no_cpu:
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = cpu_baseline(c, perf)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def table(a, torch, ssg, perf, wl, timer):
+    rotate = not a.warm
+    steps, warmup = a.steps, a.warmup
+
+    def emit(d):
+        print(json.dumps(d), flush=True)
+
+    c = wl.make_cfg1()
+    r = w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate)
+    nz, de = perf.w24_ops(c["M"], c["N"], c["K"])
+    emit(dict(workload="cfg1_w24_f16", shape=[c["M"], c["K"], c["N"]], **r,
+              tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
+              speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
+    c = wl.make_cfg2()
+    r = w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate)
+    r.pop("sets")
+    nz, de = perf.w24_ops(c["M"], c["N"], c["K"])
+    b = perf.w24_bytes(c["M"], c["N"], c["K"], 1, 1, 4, True)
+    emit(dict(workload="cfg2_w24_i8", shape=[c["M"], c["K"], c["N"]], **r,
+              tops_nonzero=nz / r["t_sparse_ms"] / 1e9, tops_dense_eq=de / r["t_sparse_ms"] / 1e9,
+              gbs=b / r["t_sparse_ms"] / 1e6, speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
+    torch.cuda.empty_cache()
+    c3 = wl.make_cfg3()
+    c4 = wl.make_cfg4()
+    for c in (c3, c4["fc1"], c4["fc2"]):
+        r = tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate)
+        emit(dict(workload=c["name"] + "_tw_f16", shape=[c["M"], c["K"], c["N"]], **r,
+                  tflops_nonzero=r["ops"] / r["t_sparse_ms"] / 1e9, gbs=r["bytes"] / r["t_sparse_ms"] / 1e6,
+                  speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
+                  speedup_vs_dense_incl_transpose=r["t_dense_ms"] / (r["t_sparse_ms"] + r["t_transpose_ms"])))
+        torch.cuda.empty_cache()
+    for g in wl.cfg5_layers("f16", layers=1):
+        r = w24_f16_case(torch, ssg, perf, g, steps, warmup, timer, rotate)
+        nz, de = perf.w24_ops(g["M"], g["N"], g["K"])
+        emit(dict(workload=g["name"] + "_w24_f16", shape=[g["M"], g["K"], g["N"]], **r,
+                  tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
+                  speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
+        torch.cuda.empty_cache()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

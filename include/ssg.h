@@ -1,0 +1,188 @@
+/*
+ * ssg.h -- C ABI of libssg: structured-sparse weight GEMM for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library computes C = A x W for a pruned linear layer (A: M x K
+ * activations, W: K x N weight, C: M x N) with W sparse in one of two
+ * patterns:
+ *
+ *   2:4    at most two nonzeros in every group of four consecutive K entries
+ *          of an output column.  GPUSQ-ViT ("Boost Vision Transformer with
+ *          GPU-Friendly Sparsity and Quantization", abstract) prunes to this
+ *          pattern for fp16 and then quantises for the integer 2:4 path.
+ *   TW     tile-wise: W is cut into tiles of G consecutive output columns
+ *          spanning all of K; each tile keeps its own whole rows and columns
+ *          ("Accelerating Sparse DNN Models without Hardware-Support via
+ *          Tile-Wise Sparsity", tile-wise pattern slide) and runs as a
+ *          condensed dense tile whose A rows are read through offset_k and
+ *          whose C columns are written through offset_n (run-time slide).
+ *
+ * The pages split the method into offline preprocessing and a run-time GEMM
+ * fed by the preprocessed arrays; the ABI mirrors that split:
+ *
+ *   - pack functions: host, synchronous, CPU only.  Every pointer is
+ *     caller-owned host memory.
+ *   - GEMM / transpose functions: asynchronous on `stream` (a hipStream_t
+ *     passed as void*; NULL = the legacy default stream).  Every pointer is
+ *     caller-owned device memory of the current HIP device, contiguous and
+ *     16-byte aligned.  Nothing is allocated.  The call returns after the
+ *     launch is enqueued; results are visible after the stream synchronises.
+ *
+ * Conventions for every function:
+ *   - the return value is a status code (SSG_OK = 0);
+ *   - on failure nothing has been written to any output or enqueued, except
+ *     SSG_EHIP from a failed launch;
+ *   - arguments are validated on the host before any HIP call; a failure
+ *     returns SSG_EINVAL (or the code named below) and sets a message that
+ *     ssg_last_error() returns on the same thread;
+ *   - packed arrays handed to a GEMM are trusted: offsets or positions out of
+ *     range are undefined behaviour (they are not re-validated on device);
+ *   - all functions are re-entrant; the only state is a per-device cache of
+ *     the architecture check and the thread-local error message.
+ *
+ * Shapes are int64_t element counts.  fp16 data travel as uint16_t bit
+ * patterns on the host side and as untyped device pointers.
+ */
+#ifndef SSG_H
+#define SSG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SSG_OK = 0,
+    SSG_EINVAL = 1, /* bad shape, alignment, pointer or parameter            */
+    SSG_ENOT24 = 2, /* a 4-group holds more than two nonzeros                */
+    SSG_ENOSPC = 3, /* caller capacity smaller than tw_pack_query's result   */
+    SSG_ENODEV = 4, /* no HIP device visible                                 */
+    SSG_EARCH = 5,  /* current device is not gfx950                          */
+    SSG_EHIP = 6    /* a HIP runtime call or kernel launch failed            */
+};
+
+/* Message describing the last failing call on this thread ("" if none).
+ * The pointer stays valid until the next failing call on the same thread. */
+const char *ssg_last_error(void);
+
+/* Library version string, e.g. "ssg 0.1.0 gfx950". */
+const char *ssg_version(void);
+
+/* Writes the current device's architecture name (e.g. "gfx950:sramecc+:xnack-")
+ * into buf (NUL-terminated, truncated to len).  SSG_ENODEV without a device. */
+int ssg_device_arch(char *buf, int64_t len);
+
+/* ------------------------------------------------------------------------
+ * 2:4 pack stage (GPUSQ-ViT abstract: 2:4 fine-grained structured pruning,
+ * FP16 and integer).  The pages fix no storage format; this one is:
+ *
+ *   W     [K][N] row-major (N contiguous), the densified pruned weight W_p.
+ *   vals  [N][K/2]: for column n and group g (k = 4g .. 4g+3) the two kept
+ *         values in slots 2g, 2g+1, in ascending k.  Zeros are stored as +0.
+ *   meta  [N][ceil(K/32)] uint32: slot j of column n holds its position in
+ *         the group (0..3) at bits 2*(j%16) of word j/16.
+ *
+ * Kept positions: the group's nonzero positions (-0.0 counts as zero),
+ * topped up with its lowest-index zero positions to exactly two, ascending.
+ * Requires K % 4 == 0, K > 0, N > 0.  A group with more than two nonzeros
+ * returns SSG_ENOT24 naming the first offending (group, column).
+ * ------------------------------------------------------------------------ */
+int w24_pack_f16(const uint16_t *W, int64_t K, int64_t N, uint16_t *vals, uint32_t *meta);
+int w24_pack_i8(const int8_t *W, int64_t K, int64_t N, int8_t *vals, uint32_t *meta);
+
+/* Inverse: W[4g + pos][n] = vals[n][slot]; every other entry +0.
+ * Positions are checked (each group's two positions must be distinct and
+ * ascending) and a violation returns SSG_EINVAL. */
+int w24_unpack_f16(const uint16_t *vals, const uint32_t *meta, int64_t K, int64_t N, uint16_t *W);
+int w24_unpack_i8(const int8_t *vals, const uint32_t *meta, int64_t K, int64_t N, int8_t *W);
+
+/* ------------------------------------------------------------------------
+ * Tile-wise pack stage ("Accelerating Sparse DNN Models without
+ * Hardware-Support via Tile-Wise Sparsity": offline re-organisation into
+ * condensed tiles, run-time GEMM through offset_k / offset_n).
+ *
+ * Tile t covers output columns [t*G, min(N, t*G+G)), T = ceil(N/G).
+ *   offset_n  kept columns of tile t, tile-local, ascending (columns with a
+ *             nonzero in the tile);
+ *   offset_k  kept rows of tile t, global k, ascending (rows with a nonzero
+ *             among the tile's columns);
+ *   vals      tile t's block V_t[j][kk] = W[offset_k[kk]][t*G + offset_n[j]],
+ *             stored [N_t][ld_t] with ld_t = K_t rounded up to a multiple of
+ *             8 (zero padded), tiles back to back;
+ *   v_ptr, k_ptr, n_ptr  [T+1] prefix sums (elements of vals, of offset_k,
+ *             of offset_n);
+ *   tile_order [T] tiles by K_t*N_t descending, ties to the lower t
+ *             (longest-processing-time order for the grouped launch).
+ * tw_pack_query fills the sizes; tw_pack_f16 returns SSG_ENOSPC when a
+ * capacity in *cap is smaller than needed.  Requires G > 0, K > 0, N > 0,
+ * K < 2^31, and sum of tile sizes < 2^31.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int64_t T;          /* number of tiles                 */
+    int64_t sum_kt;     /* length of offset_k              */
+    int64_t sum_nt;     /* length of offset_n              */
+    int64_t vals_elems; /* length of vals (padded rows)    */
+} tw_sizes;
+
+int tw_pack_query(const uint16_t *W, int64_t K, int64_t N, int32_t G, tw_sizes *out);
+int tw_pack_f16(const uint16_t *W, int64_t K, int64_t N, int32_t G, const tw_sizes *cap,
+                uint16_t *vals, int32_t *offset_k, int32_t *offset_n,
+                int32_t *v_ptr, int32_t *k_ptr, int32_t *n_ptr, int32_t *tile_order);
+int tw_unpack_f16(const uint16_t *vals, const int32_t *offset_k, const int32_t *offset_n,
+                  const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
+                  int64_t K, int64_t N, int32_t G, uint16_t *W);
+
+/* ------------------------------------------------------------------------
+ * Device GEMMs (gfx950 only: SSG_EARCH elsewhere, SSG_ENODEV without a GPU).
+ * A is [M][K] row-major (K contiguous); C is [M][N] row-major.
+ * M >= 1 is arbitrary; M == 0 is a no-op returning SSG_OK.
+ * ------------------------------------------------------------------------ */
+
+/* Dense baseline, fp16 in, fp32 accumulate, fp16 out (round to nearest even).
+ * Wt is the weight stored [N][K] (K contiguous).  K % 64 == 0, N % 64 == 0.
+ * The pages' dense baseline is a vendor GEMM ("Accelerating Sparse DNN
+ * Models ..." pattern-comparison table); this is the same-shape MFMA one. */
+int dense_gemm_f16(const void *A, const void *Wt, void *C,
+                   int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Dense baseline, int8 in, int32 accumulate.  scale == NULL: C is int32 [M][N].
+ * Otherwise C is fp32 [M][N] with C = float(acc) * scale[n] (each step
+ * rounded to nearest even, no fused multiply-add).  K % 128 == 0, N % 64 == 0. */
+int dense_gemm_i8(const int8_t *A, const int8_t *Wt, const float *scale, void *C,
+                  int64_t M, int64_t N, int64_t K, void *stream);
+
+/* 2:4 GEMM, fp16 in, fp32 accumulate, fp16 out (nearest even), from the
+ * packed vals / meta of w24_pack_f16.  Runs on the gfx950 sparse matrix
+ * cores, which pick the matching activations by the 2-bit positions.
+ * K % 64 == 0, N % 64 == 0. */
+int w24_gemm_f16(const void *A, const void *vals, const uint32_t *meta, void *C,
+                 int64_t M, int64_t N, int64_t K, void *stream);
+
+/* 2:4 GEMM, int8 in, exact int32 accumulate; epilogue as dense_gemm_i8
+ * (scale == NULL -> int32 C, else fp32 C = float(acc) * scale[n]).
+ * K % 128 == 0, N % 64 == 0. */
+int w24_gemm_i8(const int8_t *A, const int8_t *vals, const uint32_t *meta, const float *scale,
+                void *C, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Tile-wise GEMM, fp16 in, fp32 accumulate, fp16 out.  At is A stored
+ * K-major ([K][M], M contiguous) so that the rows picked by offset_k are
+ * contiguous reads (the tile-wise slides transpose A to avoid uncoalesced
+ * access).  The packed arrays are tw_pack_f16's, in device memory, with
+ * T = ceil(N/G).  Every column of C is written: kept columns get the tile
+ * product, pruned columns +0.  Requires G % 16 == 0, G <= 128, N % G == 0,
+ * M % 8 == 0, K >= 1. */
+int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_k,
+                const int32_t *offset_n, const int32_t *v_ptr, const int32_t *k_ptr,
+                const int32_t *n_ptr, const int32_t *tile_order, int32_t T, int32_t G,
+                void *C, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Explicit transpose At[k][m] = A[m][k] (fp16), the "explicit transpose"
+ * variant of the tile-wise slides.  M % 8 == 0, K % 8 == 0. */
+int ssg_transpose_f16(const void *A, void *At, int64_t M, int64_t K, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSG_H */

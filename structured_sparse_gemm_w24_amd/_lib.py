@@ -1,0 +1,328 @@
+"""ctypes binding of libssg.so: argument marshalling only.
+
+Pack functions take and return numpy arrays (host memory).  GEMM functions
+take torch tensors on the current HIP device and launch on torch's current
+stream; outputs are allocated with torch unless ``out`` is given.  Every step
+of the computation runs inside the library; a nonzero status raises
+``SsgError`` carrying the library's message.  If the library is not built,
+every call raises: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes as ct
+import os
+import threading
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LOCK = threading.Lock()
+_LIB = None
+
+STATUS = {0: "SSG_OK", 1: "SSG_EINVAL", 2: "SSG_ENOT24", 3: "SSG_ENOSPC", 4: "SSG_ENODEV",
+          5: "SSG_EARCH", 6: "SSG_EHIP"}
+SSG_OK, SSG_EINVAL, SSG_ENOT24, SSG_ENOSPC, SSG_ENODEV, SSG_EARCH, SSG_EHIP = range(7)
+
+
+class SsgError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"{STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+class TwSizes(ct.Structure):
+    _fields_ = [("T", ct.c_int64), ("sum_kt", ct.c_int64), ("sum_nt", ct.c_int64), ("vals_elems", ct.c_int64)]
+
+
+_P = ct.c_void_p
+_I64 = ct.c_int64
+_I32 = ct.c_int32
+
+# name -> argument types (every function returns int)
+SIGNATURES = {
+    "w24_pack_f16": [_P, _I64, _I64, _P, _P],
+    "w24_pack_i8": [_P, _I64, _I64, _P, _P],
+    "w24_unpack_f16": [_P, _P, _I64, _I64, _P],
+    "w24_unpack_i8": [_P, _P, _I64, _I64, _P],
+    "tw_pack_query": [_P, _I64, _I64, _I32, ct.POINTER(TwSizes)],
+    "tw_pack_f16": [_P, _I64, _I64, _I32, ct.POINTER(TwSizes), _P, _P, _P, _P, _P, _P, _P],
+    "tw_unpack_f16": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _P],
+    "dense_gemm_f16": [_P, _P, _P, _I64, _I64, _I64, _P],
+    "dense_gemm_i8": [_P, _P, _P, _P, _I64, _I64, _I64, _P],
+    "w24_gemm_f16": [_P, _P, _P, _P, _I64, _I64, _I64, _P],
+    "w24_gemm_i8": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P],
+    "tw_gemm_f16": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _I64, _I64, _I64, _P],
+    "ssg_transpose_f16": [_P, _P, _I64, _I64, _P],
+    "ssg_device_arch": [ct.c_char_p, _I64],
+}
+
+
+def lib_path():
+    return os.environ.get("SSG_LIB", os.path.join(_HERE, "libssg.so"))
+
+
+def load():
+    """Load libssg.so once (raises if it has not been built)."""
+    global _LIB
+    with _LOCK:
+        if _LIB is None:
+            path = lib_path()
+            if not os.path.exists(path):
+                raise RuntimeError(f"{path} is missing: build it with "
+                                   f"`python -m structured_sparse_gemm_w24_amd.build`")
+            lib = ct.CDLL(path, mode=ct.RTLD_LOCAL)
+            for name, argtypes in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.argtypes = argtypes
+                fn.restype = ct.c_int
+            lib.ssg_last_error.argtypes = []
+            lib.ssg_last_error.restype = ct.c_char_p
+            lib.ssg_version.argtypes = []
+            lib.ssg_version.restype = ct.c_char_p
+            _LIB = lib
+    return _LIB
+
+
+def _check(rc):
+    if rc != SSG_OK:
+        raise SsgError(rc, load().ssg_last_error().decode())
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ct.c_void_p) if a is not None else None
+
+
+def _host(a, dtype, ndim=None):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    if ndim is not None and a.ndim != ndim:
+        raise ValueError(f"expected a {ndim}-d array, got shape {a.shape}")
+    return a
+
+
+# ---------------------------------------------------------------- pack stage
+def w24_pack_f16(W):
+    """W [K, N] float16 (2:4 along K) -> (vals [N, K/2] float16, meta [N, ceil(K/32)] uint32)."""
+    W = _host(W, np.float16, 2)
+    K, N = W.shape
+    vals = np.empty((N, K // 2), np.float16)
+    meta = np.empty((N, -(-K // 32)), np.uint32)
+    _check(load().w24_pack_f16(_np_ptr(W), K, N, _np_ptr(vals), _np_ptr(meta)))
+    return vals, meta
+
+
+def w24_pack_i8(W):
+    W = _host(W, np.int8, 2)
+    K, N = W.shape
+    vals = np.empty((N, K // 2), np.int8)
+    meta = np.empty((N, -(-K // 32)), np.uint32)
+    _check(load().w24_pack_i8(_np_ptr(W), K, N, _np_ptr(vals), _np_ptr(meta)))
+    return vals, meta
+
+
+def w24_unpack_f16(vals, meta, K, N):
+    vals = _host(vals, np.float16, 2)
+    meta = _host(meta, np.uint32, 2)
+    if vals.shape != (N, K // 2) or meta.shape != (N, -(-K // 32)):
+        raise ValueError("vals/meta shape does not match K, N")
+    W = np.empty((K, N), np.float16)
+    _check(load().w24_unpack_f16(_np_ptr(vals), _np_ptr(meta), K, N, _np_ptr(W)))
+    return W
+
+
+def w24_unpack_i8(vals, meta, K, N):
+    vals = _host(vals, np.int8, 2)
+    meta = _host(meta, np.uint32, 2)
+    if vals.shape != (N, K // 2) or meta.shape != (N, -(-K // 32)):
+        raise ValueError("vals/meta shape does not match K, N")
+    W = np.empty((K, N), np.int8)
+    _check(load().w24_unpack_i8(_np_ptr(vals), _np_ptr(meta), K, N, _np_ptr(W)))
+    return W
+
+
+@dataclass
+class TwPacked:
+    """Condensed tile-wise weight (host numpy arrays, or torch tensors after ``to``)."""
+    K: int
+    N: int
+    G: int
+    T: int
+    vals: object
+    offset_k: object
+    offset_n: object
+    v_ptr: object
+    k_ptr: object
+    n_ptr: object
+    tile_order: object
+
+    def arrays(self):
+        return dict(vals=self.vals, offset_k=self.offset_k, offset_n=self.offset_n, v_ptr=self.v_ptr,
+                    k_ptr=self.k_ptr, n_ptr=self.n_ptr, tile_order=self.tile_order)
+
+    def to(self, device):
+        """Copy every array to a torch device (int32 / float16 tensors)."""
+        import torch
+
+        def conv(a):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            return t.to(device) if t.numel() else torch.zeros(1, dtype=t.dtype, device=device)
+        return TwPacked(self.K, self.N, self.G, self.T, *[conv(a) for a in self.arrays().values()])
+
+
+def tw_pack_query(W, G):
+    W = _host(W, np.float16, 2)
+    K, N = W.shape
+    sz = TwSizes()
+    _check(load().tw_pack_query(_np_ptr(W), K, N, G, ct.byref(sz)))
+    return dict(T=sz.T, sum_kt=sz.sum_kt, sum_nt=sz.sum_nt, vals_elems=sz.vals_elems)
+
+
+def tw_pack_f16(W, G):
+    """W [K, N] float16 -> TwPacked (host arrays)."""
+    W = _host(W, np.float16, 2)
+    K, N = W.shape
+    sz = TwSizes()
+    _check(load().tw_pack_query(_np_ptr(W), K, N, G, ct.byref(sz)))
+    vals = np.empty(sz.vals_elems, np.float16)
+    ok = np.empty(sz.sum_kt, np.int32)
+    on = np.empty(sz.sum_nt, np.int32)
+    vp = np.empty(sz.T + 1, np.int32)
+    kp = np.empty(sz.T + 1, np.int32)
+    np_ = np.empty(sz.T + 1, np.int32)
+    order = np.empty(sz.T, np.int32)
+    _check(load().tw_pack_f16(_np_ptr(W), K, N, G, ct.byref(sz), _np_ptr(vals), _np_ptr(ok), _np_ptr(on),
+                              _np_ptr(vp), _np_ptr(kp), _np_ptr(np_), _np_ptr(order)))
+    return TwPacked(K, N, G, int(sz.T), vals, ok, on, vp, kp, np_, order)
+
+
+def tw_unpack_f16(p: TwPacked):
+    W = np.empty((p.K, p.N), np.float16)
+    arrs = [_host(p.vals, np.float16), _host(p.offset_k, np.int32), _host(p.offset_n, np.int32),
+            _host(p.v_ptr, np.int32), _host(p.k_ptr, np.int32), _host(p.n_ptr, np.int32)]
+    _check(load().tw_unpack_f16(*[_np_ptr(a) for a in arrs], p.K, p.N, p.G, _np_ptr(W)))
+    return W
+
+
+# ---------------------------------------------------------------- device side
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, dtype, shape=None, name="tensor"):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on a HIP device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return ct.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(t):
+    torch = _torch()
+    return ct.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _out(out, shape, dtype, like):
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    return _dev(out, dtype, shape, "out")
+
+
+def ssg_device_arch():
+    buf = ct.create_string_buffer(256)
+    _check(load().ssg_device_arch(buf, 256))
+    return buf.value.decode()
+
+
+def dense_gemm_f16(A, Wt, out=None):
+    """C = A . Wt^T; A [M, K] fp16, Wt [N, K] fp16 -> C [M, N] fp16."""
+    torch = _torch()
+    M, K = A.shape
+    N = Wt.shape[0]
+    _dev(A, torch.float16, (M, K), "A")
+    _dev(Wt, torch.float16, (N, K), "Wt")
+    C = _out(out, (M, N), torch.float16, A)
+    _check(load().dense_gemm_f16(_ptr(A), _ptr(Wt), _ptr(C), M, N, K, _stream(A)))
+    return C
+
+
+def dense_gemm_i8(A, Wt, scale=None, out=None):
+    """int8 dense GEMM; scale None -> int32 C, else fp32 C = float(acc) * scale[n]."""
+    torch = _torch()
+    M, K = A.shape
+    N = Wt.shape[0]
+    _dev(A, torch.int8, (M, K), "A")
+    _dev(Wt, torch.int8, (N, K), "Wt")
+    if scale is not None:
+        _dev(scale, torch.float32, (N,), "scale")
+    C = _out(out, (M, N), torch.int32 if scale is None else torch.float32, A)
+    _check(load().dense_gemm_i8(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(C), M, N, K, _stream(A)))
+    return C
+
+
+def w24_gemm_f16(A, vals, meta, out=None):
+    """2:4 GEMM; A [M, K] fp16, vals [N, K/2] fp16, meta [N, K/32] int32 (uint32 bits)."""
+    torch = _torch()
+    M, K = A.shape
+    N = vals.shape[0]
+    _dev(A, torch.float16, (M, K), "A")
+    _dev(vals, torch.float16, (N, K // 2), "vals")
+    _dev(meta, torch.int32, (N, -(-K // 32)), "meta")
+    C = _out(out, (M, N), torch.float16, A)
+    _check(load().w24_gemm_f16(_ptr(A), _ptr(vals), _ptr(meta), _ptr(C), M, N, K, _stream(A)))
+    return C
+
+
+def w24_gemm_i8(A, vals, meta, scale=None, out=None):
+    torch = _torch()
+    M, K = A.shape
+    N = vals.shape[0]
+    _dev(A, torch.int8, (M, K), "A")
+    _dev(vals, torch.int8, (N, K // 2), "vals")
+    _dev(meta, torch.int32, (N, -(-K // 32)), "meta")
+    if scale is not None:
+        _dev(scale, torch.float32, (N,), "scale")
+    C = _out(out, (M, N), torch.int32 if scale is None else torch.float32, A)
+    _check(load().w24_gemm_i8(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), _ptr(C), M, N, K, _stream(A)))
+    return C
+
+
+def tw_gemm_f16(At, packed: TwPacked, out=None):
+    """Tile-wise GEMM; At [K, M] fp16 (K-major A), packed arrays on the device."""
+    torch = _torch()
+    K, M = At.shape
+    if K != packed.K:
+        raise ValueError(f"At has K={K}, packed weight has K={packed.K}")
+    _dev(At, torch.float16, (K, M), "At")
+    arrs = packed.arrays()
+    _dev(arrs["vals"], torch.float16, None, "vals")
+    for key in ("offset_k", "offset_n", "v_ptr", "k_ptr", "n_ptr", "tile_order"):
+        _dev(arrs[key], torch.int32, None, key)
+    C = _out(out, (M, packed.N), torch.float16, At)
+    _check(load().tw_gemm_f16(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
+                              _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]),
+                              _ptr(arrs["tile_order"]), packed.T, packed.G, _ptr(C), M, packed.N, K, _stream(At)))
+    return C
+
+
+def ssg_transpose_f16(A, out=None):
+    """At [K, M] = A^T for A [M, K] fp16."""
+    torch = _torch()
+    M, K = A.shape
+    _dev(A, torch.float16, (M, K), "A")
+    At = _out(out, (K, M), torch.float16, A)
+    _check(load().ssg_transpose_f16(_ptr(A), _ptr(At), M, K, _stream(A)))
+    return At

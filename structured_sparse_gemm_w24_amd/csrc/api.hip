@@ -1,0 +1,162 @@
+// Exported device entry points of libssg: argument validation on the host,
+// a cached per-device architecture check, then one kernel launch on the
+// caller's stream.  Nothing is allocated and nothing is synchronised.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "kernels/launch.h"
+#include "status.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+int g_arch_state[kMaxDevices] = {0};
+std::mutex g_arch_mu;
+
+// SSG_OK if a gfx950 device is current; SSG_ENODEV / SSG_EARCH / SSG_EHIP otherwise.
+int check_device() {
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count <= 0) return ssg::fail(SSG_ENODEV, "no HIP device visible");
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return ssg::fail(SSG_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return ssg::fail(SSG_ENODEV, "device id %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_arch_mu);
+    if (g_arch_state[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return ssg::fail(SSG_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        g_arch_state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        if (g_arch_state[dev] == 2)
+            return ssg::fail(SSG_EARCH, "device %d is %s, this library targets gfx950", dev, prop.gcnArchName);
+    }
+    if (g_arch_state[dev] != 1) return ssg::fail(SSG_EARCH, "device %d is not gfx950", dev);
+    return SSG_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return ssg::fail(SSG_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    ssg::clear_error();
+    return SSG_OK;
+}
+
+bool fits_int(int64_t v) { return v >= 0 && v < (int64_t(1) << 31); }
+
+// Common shape / pointer checks for the row-major GEMMs.
+int check_gemm(const char *fn, const void *A, const void *W, const void *C, int64_t M, int64_t N, int64_t K,
+               int k_mult, int n_mult) {
+    if (M < 0 || N <= 0 || K <= 0)
+        return ssg::fail(SSG_EINVAL, "%s: M=%lld N=%lld K=%lld (need M >= 0, N > 0, K > 0)", fn, (long long)M,
+                         (long long)N, (long long)K);
+    if (!fits_int(M) || !fits_int(N) || !fits_int(K) || !fits_int(M / 64 * N / 64))
+        return ssg::fail(SSG_EINVAL, "%s: dimensions too large", fn);
+    if (K % k_mult) return ssg::fail(SSG_EINVAL, "%s: K=%lld must be a multiple of %d", fn, (long long)K, k_mult);
+    if (N % n_mult) return ssg::fail(SSG_EINVAL, "%s: N=%lld must be a multiple of %d", fn, (long long)N, n_mult);
+    if (M == 0) return SSG_OK;
+    if (!A || !W || !C) return ssg::fail(SSG_EINVAL, "%s: null pointer", fn);
+    if (!ssg::aligned16(A) || !ssg::aligned16(W) || !ssg::aligned16(C))
+        return ssg::fail(SSG_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    return SSG_OK;
+}
+
+}  // namespace
+
+SSG_API int ssg_device_arch(char *buf, int64_t len) {
+    if (!buf || len <= 0) return ssg::fail(SSG_EINVAL, "ssg_device_arch: bad buffer");
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return ssg::fail(SSG_ENODEV, "no HIP device visible");
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return ssg::fail(SSG_EHIP, "cannot query the current device");
+    std::strncpy(buf, prop.gcnArchName, size_t(len) - 1);
+    buf[len - 1] = '\0';
+    ssg::clear_error();
+    return SSG_OK;
+}
+
+SSG_API int dense_gemm_f16(const void *A, const void *Wt, void *C, int64_t M, int64_t N, int64_t K, void *stream) {
+    int rc = check_gemm("dense_gemm_f16", A, Wt, C, M, N, K, 64, 64);
+    if (rc || M == 0) return rc ? rc : (ssg::clear_error(), SSG_OK);
+    if ((rc = check_device())) return rc;
+    return launched(ssg::launch_dense_f16(A, Wt, C, int(M), int(N), int(K), hipStream_t(stream)), "dense_gemm_f16");
+}
+
+SSG_API int dense_gemm_i8(const int8_t *A, const int8_t *Wt, const float *scale, void *C, int64_t M, int64_t N,
+                          int64_t K, void *stream) {
+    int rc = check_gemm("dense_gemm_i8", A, Wt, C, M, N, K, 128, 64);
+    if (rc || M == 0) return rc ? rc : (ssg::clear_error(), SSG_OK);
+    if (scale && !ssg::aligned16(scale)) return ssg::fail(SSG_EINVAL, "dense_gemm_i8: scale must be 16-byte aligned");
+    if ((rc = check_device())) return rc;
+    return launched(ssg::launch_dense_i8(A, Wt, scale, C, int(M), int(N), int(K), hipStream_t(stream)),
+                    "dense_gemm_i8");
+}
+
+SSG_API int w24_gemm_f16(const void *A, const void *vals, const uint32_t *meta, void *C, int64_t M, int64_t N,
+                         int64_t K, void *stream) {
+    int rc = check_gemm("w24_gemm_f16", A, vals, C, M, N, K, 64, 64);
+    if (rc || M == 0) return rc ? rc : (ssg::clear_error(), SSG_OK);
+    if (!meta || !ssg::aligned16(meta)) return ssg::fail(SSG_EINVAL, "w24_gemm_f16: meta null or misaligned");
+    if ((rc = check_device())) return rc;
+    return launched(ssg::launch_w24_f16(A, vals, meta, C, int(M), int(N), int(K), hipStream_t(stream)),
+                    "w24_gemm_f16");
+}
+
+SSG_API int w24_gemm_i8(const int8_t *A, const int8_t *vals, const uint32_t *meta, const float *scale, void *C,
+                        int64_t M, int64_t N, int64_t K, void *stream) {
+    int rc = check_gemm("w24_gemm_i8", A, vals, C, M, N, K, 128, 64);
+    if (rc || M == 0) return rc ? rc : (ssg::clear_error(), SSG_OK);
+    if (!meta || !ssg::aligned16(meta)) return ssg::fail(SSG_EINVAL, "w24_gemm_i8: meta null or misaligned");
+    if (scale && !ssg::aligned16(scale)) return ssg::fail(SSG_EINVAL, "w24_gemm_i8: scale must be 16-byte aligned");
+    if ((rc = check_device())) return rc;
+    return launched(ssg::launch_w24_i8(A, vals, meta, scale, C, int(M), int(N), int(K), hipStream_t(stream)),
+                    "w24_gemm_i8");
+}
+
+SSG_API int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
+                        const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr, const int32_t *tile_order,
+                        int32_t T, int32_t G, void *C, int64_t M, int64_t N, int64_t K, void *stream) {
+    const char *fn = "tw_gemm_f16";
+    if (M < 0 || N <= 0 || K <= 0 || !fits_int(M) || !fits_int(N) || !fits_int(K))
+        return ssg::fail(SSG_EINVAL, "%s: bad shape M=%lld N=%lld K=%lld", fn, (long long)M, (long long)N,
+                         (long long)K);
+    if (G <= 0 || G % 16 || G > 128)
+        return ssg::fail(SSG_EINVAL, "%s: G=%d must be a positive multiple of 16, at most 128", fn, G);
+    if (N % G) return ssg::fail(SSG_EINVAL, "%s: N=%lld must be a multiple of G=%d", fn, (long long)N, G);
+    if (T != N / G) return ssg::fail(SSG_EINVAL, "%s: T=%d must equal N/G=%lld", fn, T, (long long)(N / G));
+    if (M % 8) return ssg::fail(SSG_EINVAL, "%s: M=%lld must be a multiple of 8", fn, (long long)M);
+    if (!fits_int((M + 127) / 128 * int64_t(T))) return ssg::fail(SSG_EINVAL, "%s: too many work items", fn);
+    if (M == 0) {
+        ssg::clear_error();
+        return SSG_OK;
+    }
+    if (!At || !C || !v_ptr || !k_ptr || !n_ptr || !tile_order || !offset_k || !offset_n || !vals)
+        return ssg::fail(SSG_EINVAL, "%s: null pointer", fn);
+    if (!ssg::aligned16(At) || !ssg::aligned16(C) || !ssg::aligned16(vals))
+        return ssg::fail(SSG_EINVAL, "%s: At, vals and C must be 16-byte aligned", fn);
+    int rc = check_device();
+    if (rc) return rc;
+    return launched(ssg::launch_tw_f16(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G, C, int(M),
+                                       int(N), hipStream_t(stream)),
+                    fn);
+}
+
+SSG_API int ssg_transpose_f16(const void *A, void *At, int64_t M, int64_t K, void *stream) {
+    const char *fn = "ssg_transpose_f16";
+    if (M < 0 || K <= 0 || !fits_int(M) || !fits_int(K) || M % 8 || K % 8)
+        return ssg::fail(SSG_EINVAL, "%s: M=%lld K=%lld must be multiples of 8 (K > 0)", fn, (long long)M,
+                         (long long)K);
+    if (M == 0) {
+        ssg::clear_error();
+        return SSG_OK;
+    }
+    if (!A || !At || !ssg::aligned16(A) || !ssg::aligned16(At))
+        return ssg::fail(SSG_EINVAL, "%s: pointers must be non-null and 16-byte aligned", fn);
+    int rc = check_device();
+    if (rc) return rc;
+    return launched(ssg::launch_transpose_f16(A, At, int(M), int(K), hipStream_t(stream)), fn);
+}

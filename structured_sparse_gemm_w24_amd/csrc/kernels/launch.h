@@ -1,0 +1,23 @@
+// Internal launch entry points of the gfx950 kernels (not exported).
+// Arguments are validated by the C-ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssg {
+
+hipError_t launch_dense_f16(const void *A, const void *Wt, void *C, int M, int N, int K, hipStream_t st);
+hipError_t launch_dense_i8(const void *A, const void *Wt, const float *scale, void *C, int M, int N,
+                           int K, hipStream_t st);
+hipError_t launch_w24_f16(const void *A, const void *vals, const uint32_t *meta, void *C, int M, int N,
+                          int K, hipStream_t st);
+hipError_t launch_w24_i8(const void *A, const void *vals, const uint32_t *meta, const float *scale,
+                         void *C, int M, int N, int K, hipStream_t st);
+hipError_t launch_tw_f16(const void *At, const void *vals, const int32_t *offset_k,
+                         const int32_t *offset_n, const int32_t *v_ptr, const int32_t *k_ptr,
+                         const int32_t *n_ptr, const int32_t *tile_order, int T, int G, void *C,
+                         int M, int N, hipStream_t st);
+hipError_t launch_transpose_f16(const void *A, void *At, int M, int K, hipStream_t st);
+
+}  // namespace ssg

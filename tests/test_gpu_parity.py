@@ -1,0 +1,301 @@
+"""HIP kernels vs the oracle, element by element, through the C ABI.
+
+Bars (from the arithmetic; see oracle/bounds.py):
+* int8 / int32 paths: bit-exact (int32 accumulators and fp32 scaled outputs);
+* fp16 paths: max|C - C_ref| <= 1e-2 * max|C_ref| (acceptance) and the strict
+  per-element bound |C - C_ref| <= 2^-11 |C_ref| + 2^-25 + 2 n 2^-24 S;
+* exact-integer inputs and one-hot weights: bit-exact for fp16 too (every fp32
+  partial sum is an exact integer, so the single fp16 rounding is the
+  oracle's round-to-nearest-even of the exact value);
+* transpose: bit-exact.
+Shapes span several tiles with ragged token tails (M = 1, 17, 200, ...).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def T(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def H(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def meta_t(meta):
+    return T(meta.view(np.int32))
+
+
+def run_w24_f16(lib, A, Wp, out=None):
+    vals, meta = lib.w24_pack_f16(Wp)
+    return H(lib.w24_gemm_f16(T(A), T(vals), meta_t(meta), out=out))
+
+
+def run_w24_i8(lib, A, Wp, scale):
+    vals, meta = lib.w24_pack_i8(Wp)
+    return H(lib.w24_gemm_i8(T(A), T(vals), meta_t(meta), None if scale is None else T(scale)))
+
+
+def check_f16(C, A, Wp, n_terms, what=""):
+    C_ref, _ = oracle.ref_gemm_f16(A, Wp)
+    S = oracle.ref_abs_gemm(A, Wp)
+    err = oracle.loose_err(C, C_ref)
+    assert err <= 1e-2, f"{what}: loose error {err}"
+    assert oracle.strict_ok_f16(C, C_ref, S, n_terms), f"{what}: strict bound violated"
+
+
+def check_f16_exact(C, A, Wp, what=""):
+    _, C16 = oracle.ref_gemm_f16(A, Wp)
+    bad = np.flatnonzero(C.view(np.uint16) != C16.view(np.uint16))
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {np.unravel_index(bad[0], C.shape)}"
+
+
+SMALL = [(1, 64, 64), (17, 128, 256), (200, 512, 320), (129, 256, 64), (64, 192, 128)]
+
+
+# ---------------------------------------------------------------- 2:4 fp16
+@pytest.mark.parametrize("M,K,N", SMALL)
+def test_w24_f16_random(lib, gpu, M, K, N):
+    case = wl.random_24_f16(np.random.default_rng(M * 7 + K), M, K, N)
+    C = run_w24_f16(lib, case["A"], case["Wp"])
+    check_f16(C, case["A"], case["Wp"], K // 2, f"w24 f16 {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M,K,N", SMALL + [(300, 1024, 256)])
+def test_w24_f16_exact_integers(lib, gpu, M, K, N):
+    case = wl.exact_int_24_f16(np.random.default_rng(K + N), M, K, N)
+    check_f16_exact(run_w24_f16(lib, case["A"], case["Wp"]), case["A"], case["Wp"], "w24 f16 exact")
+
+
+def test_w24_f16_one_hot(lib, gpu):
+    case = wl.one_hot_24(np.random.default_rng(3), 77, 256, 192)
+    C = run_w24_f16(lib, case["A"], case["Wp"])
+    assert np.array_equal(C.view(np.uint16), case["A"][:, case["k_of_n"]].view(np.uint16))
+
+
+def test_w24_f16_every_position_pair(lib, gpu):
+    # Each column walks all six position pairs across its groups, with exact integers.
+    M, K, N = 40, 384, 64
+    rng = np.random.default_rng(4)
+    A = rng.integers(-3, 4, size=(M, K)).astype(np.float16)
+    Wp = np.zeros((K, N), np.float16)
+    pairs = [(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)]
+    for n in range(N):
+        for g in range(K // 4):
+            p0, p1 = pairs[(g + n) % 6]
+            Wp[4 * g + p0, n] = rng.integers(1, 3) * (1 if (g + n) % 2 else -1)
+            Wp[4 * g + p1, n] = rng.integers(-2, 3)
+    check_f16_exact(run_w24_f16(lib, A, Wp), A, Wp, "position pairs")
+
+
+def test_w24_f16_cfg1(lib, gpu):
+    c = wl.make_cfg1()
+    check_f16(run_w24_f16(lib, c["A"], c["Wp"]), c["A"], c["Wp"], c["K"] // 2, "cfg1")
+
+
+@pytest.mark.parametrize("gname", ["qkv", "proj", "fc1", "fc2"])
+def test_w24_f16_cfg5_layer0(lib, gpu, gname):
+    for g in wl.cfg5_layers("f16", layers=1):
+        if g["name"].endswith(gname):
+            check_f16(run_w24_f16(lib, g["A"], g["Wp"]), g["A"], g["Wp"], g["K"] // 2, g["name"])
+
+
+# ---------------------------------------------------------------- 2:4 int8
+@pytest.mark.parametrize("M,K,N", [(1, 128, 64), (17, 256, 256), (200, 768, 320), (129, 512, 64)])
+@pytest.mark.parametrize("scaled", [False, True])
+def test_w24_i8_bit_exact(lib, gpu, M, K, N, scaled):
+    case = wl.random_24_i8(np.random.default_rng(M + K + N), M, K, N)
+    scale = case["scale"] if scaled else None
+    C = run_w24_i8(lib, case["A"], case["Wp"], scale)
+    ref = oracle.ref_gemm_i8(case["A"], case["Wp"], scale)
+    assert C.dtype == ref.dtype
+    assert np.array_equal(C.view(np.uint32), ref.view(np.uint32))
+
+
+def test_w24_i8_one_hot(lib, gpu):
+    case = wl.one_hot_24(np.random.default_rng(5), 65, 256, 128, dtype=np.int8)
+    C = run_w24_i8(lib, case["A"], case["Wp"], None)
+    assert np.array_equal(C, case["A"][:, case["k_of_n"]].astype(np.int32))
+
+
+def test_w24_i8_extreme_values(lib, gpu):
+    # +-127 everywhere, K = 4096: |acc| = 2048 * 127^2 > 2^24 exercises int32 range and fp32 rounding.
+    M, K, N = 16, 4096, 64
+    A = np.full((M, K), 127, np.int8)
+    A[1::2] = -127
+    Wp = np.zeros((K, N), np.int8)
+    Wp[0::4] = 127
+    Wp[3::4] = -127
+    Wp[3::4, ::3] = 127
+    scale = np.random.default_rng(6).uniform(1e-3, 1e-2, N).astype(np.float32)
+    for s in (None, scale):
+        C = run_w24_i8(lib, A, Wp, s)
+        ref = oracle.ref_gemm_i8(A, Wp, s)
+        assert np.array_equal(C.view(np.uint32), ref.view(np.uint32))
+
+
+def test_w24_i8_cfg2(lib, gpu):
+    c = wl.make_cfg2()
+    for s in (None, c["scale"]):
+        C = run_w24_i8(lib, c["A"], c["Wp"], s)
+        ref = oracle.ref_gemm_i8(c["A"], c["Wp"], s)
+        assert np.array_equal(C.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("gname", ["qkv", "fc2"])
+def test_w24_i8_cfg5_layer0(lib, gpu, gname):
+    for g in wl.cfg5_layers("i8", layers=1):
+        if g["name"].endswith(gname):
+            C = run_w24_i8(lib, g["A"], g["Wp"], g["scale"])
+            ref = oracle.ref_gemm_i8(g["A"], g["Wp"], g["scale"])
+            assert np.array_equal(C.view(np.uint32), ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------- dense baselines
+@pytest.mark.parametrize("M,K,N", SMALL)
+def test_dense_f16(lib, gpu, M, K, N):
+    rng = np.random.default_rng(M + 3 * K)
+    A = wl.f16_normal(rng, (M, K))
+    W = wl.f16_normal(rng, (K, N), 0.02)
+    C = H(lib.dense_gemm_f16(T(A), T(W.T)))
+    check_f16(C, A, W, K, f"dense f16 {M}x{K}x{N}")
+    ex = wl.exact_int_24_f16(rng, M, K, N)
+    check_f16_exact(H(lib.dense_gemm_f16(T(ex["A"]), T(ex["W"].T))), ex["A"], ex["W"], "dense exact")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 64), (200, 768, 320), (129, 512, 64)])
+@pytest.mark.parametrize("scaled", [False, True])
+def test_dense_i8(lib, gpu, M, K, N, scaled):
+    case = wl.random_24_i8(np.random.default_rng(M * K), M, K, N)
+    scale = case["scale"] if scaled else None
+    C = H(lib.dense_gemm_i8(T(case["A"]), T(case["W"].T), None if scale is None else T(scale)))
+    ref = oracle.ref_gemm_i8(case["A"], case["W"], scale)
+    assert np.array_equal(C.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dense_equals_sparse_on_pruned_weight(lib, gpu):
+    # Identity from the definition: the 2:4 result equals the dense GEMM on W_p (int8: bit-exact).
+    case = wl.random_24_i8(np.random.default_rng(8), 96, 512, 256)
+    Cs = run_w24_i8(lib, case["A"], case["Wp"], case["scale"])
+    Cd = H(lib.dense_gemm_i8(T(case["A"]), T(case["Wp"].T), T(case["scale"])))
+    assert np.array_equal(Cs.view(np.uint32), Cd.view(np.uint32))
+
+
+# ---------------------------------------------------------------- tile-wise
+def run_tw(lib, A, Wp, G, prefill_nan=True):
+    import torch
+    packed = lib.tw_pack_f16(Wp, G).to("cuda")
+    At = lib.ssg_transpose_f16(T(A))
+    out = torch.full((A.shape[0], Wp.shape[1]), float("nan"), dtype=torch.float16, device="cuda") \
+        if prefill_nan else None
+    return H(lib.tw_gemm_f16(At, packed, out=out))
+
+
+TW_SMALL = [(8, 64, 32, 16, [0.5, 1.0]), (136, 200, 96, 32, [0.3, 0.0, 0.9]),
+            (256, 768, 384, 128, [0.1, 0.25, 0.4]), (24, 1000, 64, 64, 0.6), (200, 96, 128, 128, 1.0)]
+
+
+@pytest.mark.parametrize("M,K,N,G,d", TW_SMALL)
+def test_tw_random(lib, gpu, M, K, N, G, d):
+    case = wl.random_tw_f16(np.random.default_rng(M + K + G), M, K, N, G, d)
+    C = run_tw(lib, case["A"], case["Wp"], G)
+    packed = oracle.ref_tw_pack(case["Wp"], G)
+    n_terms = int(max(np.diff(packed["k_ptr"]).max(), 1))
+    check_f16(C, case["A"], case["Wp"], n_terms, f"tw {M}x{K}x{N} G={G}")
+    # pruned columns are exact +0
+    kept = np.zeros(N, bool)
+    for t in range(packed["T"]):
+        kept[t * G + packed["offset_n"][packed["n_ptr"][t]:packed["n_ptr"][t + 1]]] = True
+    assert (C[:, ~kept].view(np.uint16) == 0).all()
+
+
+@pytest.mark.parametrize("M,K,N,G,d", TW_SMALL)
+def test_tw_exact_integers(lib, gpu, M, K, N, G, d):
+    case = wl.exact_int_tw_f16(np.random.default_rng(K), M, K, N, G, d)
+    check_f16_exact(run_tw(lib, case["A"], case["Wp"], G), case["A"], case["Wp"], "tw exact")
+
+
+def test_tw_one_hot(lib, gpu):
+    case = wl.one_hot_tw(np.random.default_rng(9), 64, 512, 256, 128)
+    C = run_tw(lib, case["A"], case["Wp"], 128)
+    for n in range(256):
+        if case["k_of_n"][n] >= 0:
+            assert np.array_equal(C[:, n].view(np.uint16), case["A"][:, case["k_of_n"][n]].view(np.uint16))
+        else:
+            assert (C[:, n].view(np.uint16) == 0).all()
+
+
+def test_tw_all_zero_weight(lib, gpu):
+    A = wl.f16_normal(np.random.default_rng(10), (32, 64))
+    C = run_tw(lib, A, np.zeros((64, 256), np.float16), 128)
+    assert (C.view(np.uint16) == 0).all()
+
+
+def test_tw_cfg3(lib, gpu):
+    c = wl.make_cfg3()
+    C = run_tw(lib, c["A"], c["Wp"], c["G"])
+    check_f16(C, c["A"], c["Wp"], 512, "cfg3")
+
+
+@pytest.mark.parametrize("which", ["fc1", "fc2"])
+def test_tw_cfg4(lib, gpu, which):
+    c = wl.make_cfg4()[which]
+    C = run_tw(lib, c["A"], c["Wp"], c["G"])
+    check_f16(C, c["A"], c["Wp"], 1311, c["name"])
+
+
+def test_tw_indexed_oracle_agrees(lib, gpu):
+    # The kernel against the slide's indexed formulation (not the masked dense one).
+    case = wl.random_tw_f16(np.random.default_rng(11), 64, 256, 256, 128, [0.2, 0.5])
+    C = run_tw(lib, case["A"], case["Wp"], 128)
+    ref = oracle.ref_tw_gemm_indexed(case["A"], oracle.ref_tw_pack(case["Wp"], 128), 256, 128)
+    assert oracle.loose_err(C, ref) <= 1e-2
+
+
+# ---------------------------------------------------------------- transpose, determinism, errors
+@pytest.mark.parametrize("M,K", [(8, 8), (136, 200), (4096, 768), (1000, 1024)])
+def test_transpose_bit_exact(lib, gpu, M, K):
+    A = wl.f16_normal(np.random.default_rng(M), (M, K))
+    At = H(lib.ssg_transpose_f16(T(A)))
+    assert np.array_equal(At.view(np.uint16), oracle.ref_transpose(A).view(np.uint16))
+
+
+def test_determinism(lib, gpu):
+    case = wl.random_24_f16(np.random.default_rng(12), 300, 1024, 512)
+    a = run_w24_f16(lib, case["A"], case["Wp"])
+    b = run_w24_f16(lib, case["A"], case["Wp"])
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    c = wl.make_cfg3()
+    x = run_tw(lib, c["A"][:512], c["Wp"], 128)
+    y = run_tw(lib, c["A"][:512], c["Wp"], 128)
+    assert np.array_equal(x.view(np.uint16), y.view(np.uint16))
+
+
+def test_w24_writes_every_output(lib, gpu):
+    import torch
+    case = wl.random_24_f16(np.random.default_rng(13), 77, 256, 192)
+    vals, meta = lib.w24_pack_f16(case["Wp"])
+    out = torch.full((77, 192), float("nan"), dtype=torch.float16, device="cuda")
+    C = H(lib.w24_gemm_f16(T(case["A"]), T(vals), meta_t(meta), out=out))
+    assert np.isfinite(C.astype(np.float32)).all()
+
+
+def test_device_arch_is_gfx950(lib, gpu):
+    assert lib.ssg_device_arch().startswith("gfx950")
+
+
+def test_zero_tokens_is_noop(lib, gpu):
+    import torch
+    A = torch.empty((0, 128), dtype=torch.float16, device="cuda")
+    vals, meta = lib.w24_pack_f16(np.zeros((128, 64), np.float16))
+    C = lib.w24_gemm_f16(A, T(vals), meta_t(meta))
+    assert C.shape == (0, 64)

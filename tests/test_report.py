@@ -1,0 +1,60 @@
+"""The bench's report arithmetic, pinned by the one detailed table on the pages
+(tile-wise slides, BERT-Base 75 % time breakdown; see tests/golden)."""
+
+import os
+
+import pytest
+
+from structured_sparse_gemm_w24_amd import perf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tw_bert_base_time_breakdown.txt")
+
+
+def load_table():
+    rows, printed = {}, {}
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        parts = line.split()
+        if len(parts) == 7:
+            rows[parts[0]] = dict(gemm=float(parts[1]), non_gemm=float(parts[2]),
+                                  transpose=float(parts[3]), total=float(parts[4]),
+                                  speedup=float(parts[5]),
+                                  share=None if parts[6] == "-" else float(parts[6]))
+        else:
+            printed[parts[0]] = float(parts[1])
+    return rows, printed
+
+
+def test_totals_add_up():
+    rows, _ = load_table()
+    for r in rows.values():
+        assert r["gemm"] + r["non_gemm"] + r["transpose"] == pytest.approx(r["total"], abs=0.006)
+
+
+def test_speedups_and_shares_reproduce_printed_values():
+    rows, printed = load_table()
+    base = rows["dense"]["total"]
+    for name, r in rows.items():
+        s = perf.speedup(base, r["total"])
+        digits = len(str(r["speedup"]).split(".")[1]) if "." in str(r["speedup"]) else 0
+        assert round(s, digits) == r["speedup"], name
+        if r["share"] is not None:
+            assert round(100 * perf.share(r["gemm"], r["total"])) == r["share"], name
+    g = perf.speedup(rows["dense"]["gemm"], rows["fused_transpose"]["gemm"])
+    assert round(g, 2) == pytest.approx(printed["gemm_speedup_vs_dense"], abs=0.011)
+    g2 = perf.speedup(rows["without_transpose"]["gemm"], rows["fused_transpose"]["gemm"])
+    assert round(g2, 2) == printed["gemm_speedup_vs_without_transpose"]
+
+
+def test_work_models_closed_form():
+    M, N, K = 12608, 3072, 768
+    nz, de = perf.w24_ops(M, N, K)
+    assert de == 2 * nz == 2 * M * N * K
+    b = perf.w24_bytes(M, N, K, 1, 1, 4, scale=True)
+    assert b == M * K + N * K // 2 + N * K // 8 + 4 * N + 4 * M * N
+    assert perf.dense_bytes(4, 8, 16, 2, 2, 2) == 4 * 16 * 2 + 16 * 8 * 2 + 4 * 8 * 2
+    assert perf.transpose_bytes(3, 5) == 60
+    r = perf.roofline(4000.0, perf.PEAK_HBM_GBS, "GB/s", "hbm")
+    assert r["frac"] == 0.5 and r["traffic"] is None
