@@ -30,12 +30,15 @@
 // Instruction operand layouts (64-lane wave, h = lane / 32, r = lane % 32):
 //   dense f16 32x32x16 : row-op lane holds k = 8h .. 8h+7 of its row r
 //   dense i8  32x32x32 : k = 16h .. 16h+15
-//   sparse f16 32x32x32: dense column-op lane holds k = 16h .. 16h+15 of
-//                        column r; sparse row-op lane holds the 8 kept values
-//                        of those 16 k (4 groups) with 8 two-bit positions in
-//                        the low 16 bits of the index operand
-//   sparse i8 32x32x64 : dense lane holds k = 32h .. 32h+31; sparse lane the
-//                        16 kept values of those 32 k, 16 positions = 32 bits
+//   sparse f16 32x32x32: sparse row-op lane holds the 8 kept values of row r
+//                        for k in [16h, 16h+16) (4 groups, ascending), slot c's
+//                        two-bit position at bits 2c of the index operand; the
+//                        dense column-op lane holds, as elements 0..7 and
+//                        8..15, k = 8h .. 8h+7 and k = 16+8h .. 16+8h+7 of
+//                        column r (measured on gfx950 with one-wave probes)
+//   sparse i8 32x32x64 : sparse lane: 16 kept values for k in [32h, 32h+32),
+//                        16 positions = 32 index bits; dense lane: elements
+//                        0..15 = k 16h .., elements 16..31 = k 32+16h ..
 //   accumulator        : lane holds rows 8*(i/4) + 4h + i%4 (i = 0..15) of
 //                        column r
 // The compressed pack stores slot j's position at bits 2*(j%16) of word j/16,
@@ -245,8 +248,9 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
             for (int tm = 0; tm < TM; ++tm) {
                 const int row = wm * TM * 32 + tm * 32 + r;
                 if constexpr (KT::kSparse) {
-                    af0[tm] = lds16(bA + row * 128 + swz128(row, 4 * kk + 2 * h) * 16);
-                    af1[tm] = lds16(bA + row * 128 + swz128(row, 4 * kk + 2 * h + 1) * 16);
+                    // two 16-byte pieces of the 64-byte window: bytes 16h.. and 32+16h..
+                    af0[tm] = lds16(bA + row * 128 + swz128(row, 4 * kk + h) * 16);
+                    af1[tm] = lds16(bA + row * 128 + swz128(row, 4 * kk + 2 + h) * 16);
                 } else {
                     af0[tm] = lds16(bA + row * 128 + swz128(row, 2 * kk + h) * 16);
                     af1[tm] = af0[tm];

@@ -5,7 +5,9 @@ The 2:4 kernels assume (h = lane / 32, r = lane % 32):
   sparse operand   lane holds the kept values of row r for k in [16h, 16h+16)
                    (f16) or [32h, 32h+32) (i8), two per group of four, with
                    slot c's 2-bit position at bits 2c of the index operand;
-  dense operand    lane holds k = 16h .. (f16) / 32h .. (i8) of column r;
+  dense operand    lane holds two runs of column r: elements 0..7 are
+                   k = 8h .. 8h+7 and elements 8..15 are k = 16+8h .. (f16);
+                   for i8 the runs are 16 long (k = 16h .., k = 32+16h ..);
   accumulator      register i of lane l is D[8*(i/4) + 4h + i%4][r].
 The dense kernels only need that element e of a lane's row operand and of its
 column operand refer to the same k, plus the accumulator layout.
@@ -85,7 +87,12 @@ def model(op, a, b, idx):
                 Am[r, h * (span // 2) + (c // 2) * 4 + pos] += a[l, c]
         else:
             Am[r, h * (span // 2):(h + 1) * (span // 2)] = a[l]
-        Bm[h * (span // 2):(h + 1) * (span // 2), r] = b[l]
+        if op in (0, 1):
+            run = nb // 2
+            for e in range(nb):
+                Bm[2 * run * (e // run) + run * h + e % run, r] = b[l, e]
+        else:
+            Bm[h * (span // 2):(h + 1) * (span // 2), r] = b[l]
     D = Am @ Bm
     return np.array([[D[8 * (i // 4) + 4 * (l // 32) + i % 4, l % 32] for i in range(16)] for l in range(64)])
 
