@@ -163,7 +163,7 @@ def cpu_baseline(c, perf, budget_s=12.0):
         oracle.ref_gemm_i8(c["A"], c["Wp"], c["scale"])
         reps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 10:
+        if el >= budget_s or reps >= 200:
             break
     nz, _ = perf.w24_ops(c["M"], c["N"], c["K"])
     return {"value": nz * reps / el / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
@@ -180,7 +180,16 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="table mode: every workload and kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--warm", action="store_true", help="one input set (cache-resident) instead of rotating")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain device copy of known size (for scaling HBM byte counters)")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="summarise rocprofv3 CSV output under DIR into --out (no GPU needed)")
+    ap.add_argument("--kernel", default="gemm_kernel<3", help="kernel-name substring for --summarize-profile")
+    ap.add_argument("--out", help="summary file for --summarize-profile")
+    ap.add_argument("--command", default="", help="the profiled command line, recorded in the summary")
     a = ap.parse_args(argv)
+    if a.summarize_profile:
+        return summarize_profile(a)
     if a.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {a.gpus}); the sparse GEMM "
               "is measured on one GPU's share and multi-GPU sharding is not part of it", file=sys.stderr)
@@ -195,6 +204,8 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     timer = Timer(torch)
+    if a.copy_calibration:
+        return copy_calibration(torch, a.steps)
     log("device", ssg.ssg_device_arch())
     if a.all:
         return table(a, torch, ssg, perf, wl, timer)
@@ -238,6 +249,78 @@ def main(argv=None):
         log("timing the CPU oracle ...")
         line["cpu_baseline"] = cpu_baseline(c, perf)
     print(json.dumps(line), flush=True)
+    return 0
+
+
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration(torch, steps):
+    """A plain device-to-device copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES) per launch."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(max(1, steps)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {steps} copies of {COPY_BYTES} bytes")
+    return 0
+
+
+def _csv_rows(root, suffix):
+    import csv
+    rows = []
+    for d, _, files in os.walk(root):
+        for f in files:
+            if f.endswith(suffix):
+                with open(os.path.join(d, f)) as fh:
+                    rows += list(csv.DictReader(fh))
+    return rows
+
+
+def summarize_profile(a):
+    """Writes a short text summary of rocprofv3 CSV output found under DIR:
+    DIR/trace (--kernel-trace --stats), DIR/fetch and DIR/write (--pmc FETCH_SIZE,
+    --pmc WRITE_SIZE on the same command), DIR/copy_fetch and DIR/copy_write (the
+    same counters on --copy-calibration).  The counters are KiB per dispatch; the
+    copy of COPY_BYTES gives the scale from counted to true bytes."""
+    root = a.summarize_profile
+    out = []
+    for r in _csv_rows(os.path.join(root, "trace"), "kernel_stats.csv"):
+        out.append(f"kernel: {r.get('Name', '')[:160]}")
+        out.append(f"  calls {r.get('Calls')}  avg_ns {r.get('AverageNs')}  min_ns {r.get('MinNs')}  "
+                   f"max_ns {r.get('MaxNs')}  share_pct {r.get('Percentage')}")
+
+    def counter(sub, cname, match):
+        vals = []
+        for r in _csv_rows(os.path.join(root, sub), "counter_collection.csv"):
+            name = r.get("Kernel_Name", "")
+            if r.get("Counter_Name") == cname and match(name):
+                try:
+                    vals.append(float(r.get("Counter_Value")))
+                except (TypeError, ValueError):
+                    pass
+        return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+    is_target = lambda n: a.kernel in n
+    is_copy = lambda n: "copy" in n.lower() and "elementwise" not in n.lower()
+    tf, ntf = counter("fetch", "FETCH_SIZE", is_target)
+    tw, ntw = counter("write", "WRITE_SIZE", is_target)
+    cf, ncf = counter("copy_fetch", "FETCH_SIZE", is_copy)
+    cw, ncw = counter("copy_write", "WRITE_SIZE", is_copy)
+    out.append(f"target '{a.kernel}': FETCH_SIZE {tf} KiB ({ntf} dispatches), WRITE_SIZE {tw} KiB ({ntw})")
+    out.append(f"copy of {COPY_BYTES} B: FETCH_SIZE {cf} KiB ({ncf}), WRITE_SIZE {cw} KiB ({ncw})")
+    if None not in (cf, cw, tf, tw) and cf > 0 and cw > 0:
+        kf, kw = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+        out.append(f"scale (true bytes per counted byte): fetch {kf:.4f} write {kw:.4f}")
+        out.append(f"kernel_sha: {kernel_hash()}")
+        out.append(f"hbm_read_bytes_per_launch: {tf * 1024 * kf:.0f}")
+        out.append(f"hbm_write_bytes_per_launch: {tw * 1024 * kw:.0f}")
+        out.append(f"hbm_bytes_per_launch: {tf * 1024 * kf + tw * 1024 * kw:.0f}")
+    text = "\n".join([f"# rocprofv3 summary; command: {a.command}"] + out) + "\n"
+    if a.out:
+        with open(a.out, "w") as fh:
+            fh.write(text)
+    print(text)
     return 0
 
 

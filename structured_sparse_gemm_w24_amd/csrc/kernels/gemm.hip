@@ -15,17 +15,25 @@
 // instruction.
 //
 // Work decomposition
-//   * workgroup = WM x WN waves; tile = BM tokens x BN channels with
-//     BM = WM*TM*32, BN = WN*TN*32; every wave owns TM x TN 32x32 blocks;
+//   * workgroup = 4 waves (2 x 2); tile = BM tokens x BN channels; every wave
+//     owns TM x TN 32x32 blocks (BM = 64*TM, BN = 64*TN);
 //   * K advances in stages of 128 bytes of an A row (f16: 64 k, i8: 128 k);
-//     each stage is staged global -> registers -> LDS, double-buffered in LDS
-//     with one barrier per stage; the next stage's global loads are in flight
-//     while the current one feeds the matrix cores;
-//   * LDS rows are XOR-swizzled in 16-byte chunks so that the 32 rows read by
-//     one fragment load fall into distinct banks;
+//     every stage is copied global -> LDS with direct-to-LDS loads (no
+//     register staging), STAGES buffers deep: the loads of stage
+//     s+STAGES-1 are issued while stage s feeds the matrix cores, and one
+//     explicit wait on the vector-memory counter plus one barrier per stage
+//     hand a stage over;
+//   * LDS rows are XOR-swizzled in 16-byte chunks so that the rows read by one
+//     fragment load fall into distinct banks; the direct-to-LDS lane order is
+//     fixed (lane i writes bytes 16i..16i+15 of the wave's 1 KiB), so each lane
+//     fetches the global chunk that belongs at its swizzled position;
 //   * block ids are remapped so each XCD works on a contiguous range of tiles
 //     (grouped GM tile-rows at a time), which keeps shared A rows and W
-//     columns in that XCD's L2.
+//     columns in that XCD's L2;
+//   * epilogue: the accumulators go through LDS as row-major [token][channel]
+//     slabs, so C is written as whole contiguous row segments, 16 bytes per
+//     lane (fp16 rounded to nearest even; int8 path: int32 or
+//     float(acc) * scale[n]).
 //
 // Instruction operand layouts (64-lane wave, h = lane / 32, r = lane % 32):
 //   dense f16 32x32x16 : row-op lane holds k = 8h .. 8h+7 of its row r
@@ -94,6 +102,26 @@ struct AccOf {
 
 __device__ __forceinline__ u32x4 lds16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Direct-to-LDS loads: lane i of the wave writes its 16 (4) bytes to
+// wave_base + 16*i (4*i).  wave_base must be uniform across the wave.
+__device__ __forceinline__ void dma16(const void *g, uint8_t *wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, uint8_t *wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)wave_base, 4, 0, 0);
+}
+
+// Waits until at most N vector-memory operations of this wave are
+// outstanding, then synchronises the workgroup (no memory fence: LDS data
+// here is produced by direct-to-LDS loads, which the counter tracks).
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 template <int KIND>
 __device__ __forceinline__ void mma(typename AccOf<KIND>::T &acc, u32x4 w, u32x4 a0, u32x4 a1, uint32_t idx) {
     if constexpr (KIND == W24_F16) {
@@ -115,29 +143,66 @@ __device__ __forceinline__ void mma(typename AccOf<KIND>::T &acc, u32x4 w, u32x4
     }
 }
 
-template <int KIND, int EPI, int WM, int WN, int TM, int TN, int GM>
-__global__ void __launch_bounds__(WM *WN * 64)
+// Epilogue store of one 16-byte piece; nontemporal stores stream past L2.
+template <bool NTS>
+__device__ __forceinline__ void store16(void *p, u32x4 v) {
+    if constexpr (NTS) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+    else *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// Tile configuration: 2 x 2 waves, TM x TN 32x32 blocks per wave, STAGES LDS
+// buffers, GM tile-rows per L2 group, nontemporal C stores.
+template <int TM_, int TN_, int STAGES_, int GM_, bool NTS_>
+struct Cfg {
+    static constexpr int TM = TM_, TN = TN_, STAGES = STAGES_, GM = GM_;
+    static constexpr bool NTS = NTS_;
+    static constexpr int WM = 2, WN = 2;
+};
+
+template <int KIND, class CF>
+struct Layout {
+    using KT = KindTraits<KIND>;
+    static constexpr int NW = CF::WM * CF::WN;  // waves
+    static constexpr int NT = NW * kWave;
+    static constexpr int BM = CF::WM * CF::TM * 32;
+    static constexpr int BN = CF::WN * CF::TN * 32;
+    static constexpr int WB = KT::kWB;
+    static constexpr int MW = KT::kMW;
+    static constexpr int A_STAGE = BM * 128;
+    static constexpr int W_STAGE = BN * WB;
+    static constexpr int M_STAGE = BN * MW * 4;
+    static constexpr int STAGE = A_STAGE + W_STAGE + M_STAGE;
+    // direct-to-LDS instructions per wave per stage (each moves 1 KiB, or
+    // 256 bytes for the 4-byte meta loads)
+    static constexpr int LA = A_STAGE / 1024 / NW;
+    static constexpr int LW = W_STAGE / 1024 / NW;
+    static constexpr int LM = M_STAGE / 256 / NW;
+    static constexpr int L = LA + LW + LM;
+    static_assert(LA * NW * 1024 == A_STAGE && LW * NW * 1024 == W_STAGE && LM * NW * 256 == M_STAGE,
+                  "stage does not split evenly over the waves");
+};
+
+template <int KIND, int EPI, class CF>
+__global__ void __launch_bounds__(CF::WM *CF::WN * 64)
 gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const uint32_t *__restrict__ meta,
             const float *__restrict__ scale, void *__restrict__ C, int M, int N, int K) {
     using KT = KindTraits<KIND>;
+    using LY = Layout<KIND, CF>;
     using Acc = typename AccOf<KIND>::T;
-    constexpr int NT = WM * WN * kWave;
-    constexpr int BM = WM * TM * 32;
-    constexpr int BN = WN * TN * 32;
-    constexpr int WB = KT::kWB;
-    constexpr int MW = KT::kMW;
+    constexpr int TM = CF::TM, TN = CF::TN, GM = CF::GM, P = CF::STAGES - 1;
+    constexpr int WM = CF::WM;
+    constexpr int BM = LY::BM, BN = LY::BN, WB = LY::WB, MW = LY::MW;
+    constexpr int A_STAGE = LY::A_STAGE, W_STAGE = LY::W_STAGE, STAGE = LY::STAGE;
     constexpr int SA = KT::kI8 ? 1 : 2;  // bytes per element
-    constexpr int A_STAGE = BM * 128;
-    constexpr int W_STAGE = BN * WB;
-    constexpr int M_STAGE = MW > 0 ? MW * BN * 4 : 16;
-    constexpr int CA = BM * 8 / NT;           // A chunks per thread per stage
-    constexpr int CW = BN * (WB / 16) / NT;   // W chunks per thread per stage
-    static_assert(CA * NT == BM * 8 && CW * NT == BN * (WB / 16), "tile does not split evenly");
-    static_assert(BN <= NT || MW == 0, "meta load assumes one row per thread");
+    // LDS-staged epilogue: each wave owns 32 token rows x TN*32 channels per pass
+    constexpr int OB = (EPI == EPI_F16) ? 2 : 4;  // output bytes per element
+    constexpr int EROW = TN * 32 * OB + 16;       // padded LDS row (odd multiple of 16 B)
+    constexpr int EWAVE = 32 * EROW;
+    constexpr int EPASS = (TM * EWAVE * LY::NW <= CF::STAGES * STAGE) ? TM : 1;
+    constexpr int SMEM_EPI = EPASS * EWAVE * LY::NW;
+    constexpr int SMEM = (CF::STAGES * STAGE > SMEM_EPI) ? CF::STAGES * STAGE : SMEM_EPI;
 
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][A_STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t sW[2][W_STAGE];
-    __shared__ __attribute__((aligned(16))) uint32_t sM[2][M_STAGE / 4];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -161,58 +226,39 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     const int64_t m_row = K / 32;                            // meta words per row
     const int S = int(a_row / 128);
 
-    // ---- per-thread global source pointers (rows clamped into range)
-    const uint8_t *ga[CA];
-    int la[CA];
+    // ---- direct-to-LDS sources: instruction j of this wave fills the wave's
+    // j-th KiB of the A (or W) stage; lane -> (row, position) -> global chunk.
+    const uint8_t *ga[LY::LA];
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-        const int c = tid + i * NT, row = c >> 3, col = c & 7;
-        ga[i] = A + int64_t(min(m0 + row, M - 1)) * a_row + col * 16;
-        la[i] = row * 128 + swz128(row, col) * 16;
+    for (int j = 0; j < LY::LA; ++j) {
+        const int byte = (j * LY::NW + wave) * 1024 + lane * 16;
+        const int row = byte / 128, pos = (byte / 16) % 8;
+        ga[j] = A + int64_t(min(m0 + row, M - 1)) * a_row + swz128(row, pos) * 16;
     }
-    const uint8_t *gw[CW];
-    int lw[CW];
+    const uint8_t *gw[LY::LW];
 #pragma unroll
-    for (int i = 0; i < CW; ++i) {
-        constexpr int CPR = WB / 16;
-        const int c = tid + i * NT, row = c / CPR, col = c % CPR;
-        gw[i] = Wv + int64_t(min(n0 + row, N - 1)) * w_row + col * 16;
-        lw[i] = row * WB + swzw<WB>(row, col) * 16;
+    for (int j = 0; j < LY::LW; ++j) {
+        const int byte = (j * LY::NW + wave) * 1024 + lane * 16;
+        const int row = byte / WB, pos = (byte / 16) % (WB / 16);
+        gw[j] = Wv + int64_t(min(n0 + row, N - 1)) * w_row + swzw<WB>(row, pos) * 16;
     }
-    const uint32_t *gmeta = nullptr;
-    if constexpr (MW > 0) gmeta = meta + int64_t(min(n0 + min(tid, BN - 1), N - 1)) * m_row;
+    const uint32_t *gm_[LY::LM > 0 ? LY::LM : 1];
+#pragma unroll
+    for (int j = 0; j < LY::LM; ++j) {
+        const int word = (j * LY::NW + wave) * 64 + lane;  // row-major [BN][MW]
+        const int row = word / MW, w = word % MW;
+        gm_[j] = meta + int64_t(min(n0 + row, N - 1)) * m_row + w;
+    }
 
-    u32x4 ra[CA], rw[CW];
-    uint32_t rm[MW > 0 ? MW : 1];
-
-    auto load_stage = [&](int s) {
+    auto issue = [&](int s) {
+        uint8_t *base = smem + (s % CF::STAGES) * STAGE;
 #pragma unroll
-        for (int i = 0; i < CA; ++i) ra[i] = ld16(ga[i] + s * 128);
+        for (int j = 0; j < LY::LA; ++j) dma16(ga[j] + s * 128, base + (j * LY::NW + wave) * 1024);
 #pragma unroll
-        for (int i = 0; i < CW; ++i) rw[i] = ld16(gw[i] + s * WB);
-        if constexpr (MW == 2) {
-            u32x2 v = ld8(gmeta + s * 2);
-            rm[0] = v.x;
-            rm[1] = v.y;
-        } else if constexpr (MW == 4) {
-            u32x4 v = ld16(gmeta + s * 4);
-            rm[0] = v.x;
-            rm[1] = v.y;
-            rm[2] = v.z;
-            rm[3] = v.w;
-        }
-    };
-    auto store_stage = [&](int buf) {
+        for (int j = 0; j < LY::LW; ++j) dma16(gw[j] + s * WB, base + A_STAGE + (j * LY::NW + wave) * 1024);
 #pragma unroll
-        for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4 *>(&sA[buf][la[i]]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < CW; ++i) *reinterpret_cast<u32x4 *>(&sW[buf][lw[i]]) = rw[i];
-        if constexpr (MW > 0) {
-            if (tid < BN) {
-#pragma unroll
-                for (int w = 0; w < MW; ++w) sM[buf][w * BN + tid] = rm[w];
-            }
-        }
+        for (int j = 0; j < LY::LM; ++j)
+            dma4(gm_[j] + s * MW, base + A_STAGE + W_STAGE + (j * LY::NW + wave) * 256);
     };
 
     Acc acc[TN][TM];
@@ -221,16 +267,18 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
 #pragma unroll
         for (int j = 0; j < TM; ++j) acc[i][j] = Acc{};
 
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < P; ++s)
+        if (s < S) issue(s);
 
     for (int s = 0; s < S; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < S) load_stage(s + 1);
-        const uint8_t *bA = sA[buf];
-        const uint8_t *bW = sW[buf];
-        const uint32_t *bM = sM[buf];
+        // stage s is complete once at most (P-1) younger stages are in flight
+        if (s + P - 1 < S) wait_vm_barrier<(P - 1) * LY::L>();
+        else wait_vm_barrier<0>();
+        if (s + P < S) issue(s + P);  // refills the buffer that stage s-1 used
+        const uint8_t *bA = smem + (s % CF::STAGES) * STAGE;
+        const uint8_t *bW = bA + A_STAGE;
+        const uint32_t *bM = reinterpret_cast<const uint32_t *>(bA + A_STAGE + W_STAGE);
 #pragma unroll
         for (int kk = 0; kk < KT::kNI; ++kk) {
             u32x4 wf[TN];
@@ -239,8 +287,8 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
             for (int tn = 0; tn < TN; ++tn) {
                 const int row = wn * TN * 32 + tn * 32 + r;
                 wf[tn] = lds16(bW + row * WB + swzw<WB>(row, 2 * kk + h) * 16);
-                if constexpr (KIND == W24_F16) idx[tn] = bM[kk * BN + row] >> (16 * h);
-                else if constexpr (KIND == W24_I8) idx[tn] = bM[(2 * kk + h) * BN + row];
+                if constexpr (KIND == W24_F16) idx[tn] = bM[row * MW + kk] >> (16 * h);
+                else if constexpr (KIND == W24_I8) idx[tn] = bM[row * MW + 2 * kk + h];
                 else idx[tn] = 0;
             }
             u32x4 af0[TM], af1[TM];
@@ -261,81 +309,108 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm) mma<KIND>(acc[tn][tm], wf[tn], af0[tm], af1[tm], idx[tn]);
         }
-        if (s + 1 < S) store_stage(buf ^ 1);
-        __syncthreads();
     }
 
-    // ---- epilogue: lane holds, per block and q = i/4, channels n..n+3 of token m
+    // ---- epilogue.  Lane (h, r) holds, for 32x32 block (tn, tm) and q = 0..3,
+    // channels n = tn*32 + 8q + 4h .. +3 of token m = tm*32 + r.
+    auto convert = [&](const Acc &v, int q, int n) -> u32x4 {
+        u32x4 o;
+        if constexpr (EPI == EPI_F16) {
+            o.x = pack_half2_rne(v[4 * q + 0], v[4 * q + 1]);
+            o.y = pack_half2_rne(v[4 * q + 2], v[4 * q + 3]);
+            o.z = 0;
+            o.w = 0;
+        } else if constexpr (EPI == EPI_I32) {
+            o.x = uint32_t(v[4 * q + 0]);
+            o.y = uint32_t(v[4 * q + 1]);
+            o.z = uint32_t(v[4 * q + 2]);
+            o.w = uint32_t(v[4 * q + 3]);
+        } else {
+            const floatx4 sc = *reinterpret_cast<const floatx4 *>(scale + min(n, N - 4));
+            floatx4 f;
+            f.x = __fmul_rn(float(v[4 * q + 0]), sc.x);
+            f.y = __fmul_rn(float(v[4 * q + 1]), sc.y);
+            f.z = __fmul_rn(float(v[4 * q + 2]), sc.z);
+            f.w = __fmul_rn(float(v[4 * q + 3]), sc.w);
+            o = __builtin_bit_cast(u32x4, f);
+        }
+        return o;
+    };
+
+    // Stage 32-token slabs of the wave's accumulators through LDS as
+    // row-major [token][channel], then store whole row segments
+    // (TN*32*OB contiguous bytes per token) with 16 bytes per lane.
+    constexpr int CPR = TN * 32 * OB / 16;  // 16-byte chunks per token row
+    constexpr int RPI = kWave / CPR;        // token rows per store instruction
+    static_assert(RPI * CPR == kWave, "row segment must tile a wave");
+    __syncthreads();  // every wave is done reading the stage buffers
+    uint8_t *ew = smem + wave * EPASS * EWAVE;
+    const int nw = n0 + wn * TN * 32;  // first channel of the wave
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-        const int m = m0 + wm * TM * 32 + tm * 32 + r;
-        if (m >= M) continue;
+    for (int tp = 0; tp < TM; tp += EPASS) {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
+        for (int e = 0; e < EPASS; ++e) {
+            uint8_t *slab = ew + e * EWAVE + r * EROW;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * TN * 32 + tn * 32 + q * 8 + h * 4;
-                if (n >= N) continue;
-                const int64_t off = int64_t(m) * N + n;
-                if constexpr (EPI == EPI_F16) {
-                    const floatx16 &v = acc[tn][tm];
-                    u32x2 o;
-                    o.x = pack_half2_rne(v[4 * q + 0], v[4 * q + 1]);
-                    o.y = pack_half2_rne(v[4 * q + 2], v[4 * q + 3]);
-                    st8(reinterpret_cast<uint16_t *>(C) + off, o);
-                } else if constexpr (EPI == EPI_I32) {
-                    const intx16 &v = acc[tn][tm];
-                    u32x4 o;
-                    o.x = uint32_t(v[4 * q + 0]);
-                    o.y = uint32_t(v[4 * q + 1]);
-                    o.z = uint32_t(v[4 * q + 2]);
-                    o.w = uint32_t(v[4 * q + 3]);
-                    st16(reinterpret_cast<int32_t *>(C) + off, o);
-                } else {
-                    const intx16 &v = acc[tn][tm];
-                    const floatx4 sc = *reinterpret_cast<const floatx4 *>(scale + n);
-                    floatx4 f;
-                    f.x = __fmul_rn(float(v[4 * q + 0]), sc.x);
-                    f.y = __fmul_rn(float(v[4 * q + 1]), sc.y);
-                    f.z = __fmul_rn(float(v[4 * q + 2]), sc.z);
-                    f.w = __fmul_rn(float(v[4 * q + 3]), sc.w);
-                    st16(reinterpret_cast<float *>(C) + off, __builtin_bit_cast(u32x4, f));
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = tn * 32 + q * 8 + h * 4;
+                    const u32x4 o = convert(acc[tn][tp + e], q, nw + c);
+                    if constexpr (OB == 2) *reinterpret_cast<u32x2 *>(slab + c * 2) = u32x2{o.x, o.y};
+                    else *reinterpret_cast<u32x4 *>(slab + c * 4) = o;
                 }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < EPASS; ++e) {
+#pragma unroll
+            for (int i = 0; i < 32 / RPI; ++i) {
+                const int row = i * RPI + lane / CPR, ch = lane % CPR;
+                const int m = m0 + wm * TM * 32 + (tp + e) * 32 + row;
+                const int n = nw + ch * (16 / OB);
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(ew + e * EWAVE + row * EROW + ch * 16);
+                if (m < M && n < N) store16<CF::NTS>(reinterpret_cast<uint8_t *>(C) + (int64_t(m) * N + n) * OB, v);
             }
         }
+        if (tp + EPASS < TM) __syncthreads();
     }
 }
 
-template <int KIND, int EPI, int WM, int WN, int TM, int TN, int GM>
+template <int KIND, int EPI, class CF>
 static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, const float *scale, void *C,
                          int M, int N, int K, hipStream_t st) {
-    constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-    const int nb = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_kernel<KIND, EPI, WM, WN, TM, TN, GM>), dim3(nb), dim3(WM * WN * kWave), 0, st,
+    using LY = Layout<KIND, CF>;
+    const int nb = ((M + LY::BM - 1) / LY::BM) * ((N + LY::BN - 1) / LY::BN);
+    hipLaunchKernelGGL((gemm_kernel<KIND, EPI, CF>), dim3(nb), dim3(LY::NT), 0, st,
                        static_cast<const uint8_t *>(A), static_cast<const uint8_t *>(Wv), meta, scale, C, M, N, K);
     return hipGetLastError();
 }
 
-// Tile shape: 128 tokens x 256 channels, 4 waves of 64 tokens x 128 channels.
+// Tile shapes: 128 tokens x 256 channels, 4 waves of 64 tokens x 128 channels.
+using CfgF16 = Cfg<2, 4, 4, 8, false>;
+using CfgI8 = Cfg<2, 4, 4, 8, true>;
+
 hipError_t launch_dense_f16(const void *A, const void *Wt, void *C, int M, int N, int K, hipStream_t st) {
-    return launch<DENSE_F16, EPI_F16, 2, 2, 2, 4, 8>(A, Wt, nullptr, nullptr, C, M, N, K, st);
+    return launch<DENSE_F16, EPI_F16, Cfg<2, 4, 3, 8, false>>(A, Wt, nullptr, nullptr, C, M, N, K, st);
 }
 
 hipError_t launch_w24_f16(const void *A, const void *vals, const uint32_t *meta, void *C, int M, int N, int K,
                           hipStream_t st) {
-    return launch<W24_F16, EPI_F16, 2, 2, 2, 4, 8>(A, vals, meta, nullptr, C, M, N, K, st);
+    return launch<W24_F16, EPI_F16, CfgF16>(A, vals, meta, nullptr, C, M, N, K, st);
 }
 
 hipError_t launch_dense_i8(const void *A, const void *Wt, const float *scale, void *C, int M, int N, int K,
                            hipStream_t st) {
-    if (scale) return launch<DENSE_I8, EPI_F32_SCALE, 2, 2, 2, 4, 8>(A, Wt, nullptr, scale, C, M, N, K, st);
-    return launch<DENSE_I8, EPI_I32, 2, 2, 2, 4, 8>(A, Wt, nullptr, nullptr, C, M, N, K, st);
+    using CD = Cfg<2, 4, 3, 8, true>;
+    if (scale) return launch<DENSE_I8, EPI_F32_SCALE, CD>(A, Wt, nullptr, scale, C, M, N, K, st);
+    return launch<DENSE_I8, EPI_I32, CD>(A, Wt, nullptr, nullptr, C, M, N, K, st);
 }
 
 hipError_t launch_w24_i8(const void *A, const void *vals, const uint32_t *meta, const float *scale, void *C,
                          int M, int N, int K, hipStream_t st) {
-    if (scale) return launch<W24_I8, EPI_F32_SCALE, 2, 2, 2, 4, 8>(A, vals, meta, scale, C, M, N, K, st);
-    return launch<W24_I8, EPI_I32, 2, 2, 2, 4, 8>(A, vals, meta, nullptr, C, M, N, K, st);
+    if (scale) return launch<W24_I8, EPI_F32_SCALE, CfgI8>(A, vals, meta, scale, C, M, N, K, st);
+    return launch<W24_I8, EPI_I32, CfgI8>(A, vals, meta, nullptr, C, M, N, K, st);
 }
 
 }  // namespace ssg
