@@ -57,6 +57,9 @@ int check_gemm(const char *fn, const void *A, const void *W, const void *C, int6
     if (K % k_mult) return ssg::fail(SSG_EINVAL, "%s: K=%lld must be a multiple of %d", fn, (long long)K, k_mult);
     if (N % n_mult) return ssg::fail(SSG_EINVAL, "%s: N=%lld must be a multiple of %d", fn, (long long)N, n_mult);
     if (M == 0) return SSG_OK;
+    // the kernels address A and W with 32-bit byte offsets
+    if (M * K * 2 >= (int64_t(1) << 32) || N * K * 2 >= (int64_t(1) << 32))
+        return ssg::fail(SSG_EINVAL, "%s: A or W larger than 4 GiB", fn);
     if (!A || !W || !C) return ssg::fail(SSG_EINVAL, "%s: null pointer", fn);
     if (!ssg::aligned16(A) || !ssg::aligned16(W) || !ssg::aligned16(C))
         return ssg::fail(SSG_EINVAL, "%s: pointers must be 16-byte aligned", fn);

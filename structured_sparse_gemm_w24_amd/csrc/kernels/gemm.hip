@@ -15,14 +15,19 @@
 // instruction.
 //
 // Work decomposition
-//   * workgroup = 4 waves (2 x 2); tile = BM tokens x BN channels; every wave
-//     owns TM x TN 32x32 blocks (BM = 64*TM, BN = 64*TN);
+//   * workgroup = WM x WN waves (8 for the large tiles: two per SIMD); tile =
+//     BM tokens x BN channels; every wave owns TM x TN 32x32 blocks
+//     (BM = 32*WM*TM, BN = 32*WN*TN);
 //   * K advances in stages of 128 bytes of an A row (f16: 64 k, i8: 128 k);
 //     every stage is copied global -> LDS with direct-to-LDS loads (no
-//     register staging), STAGES buffers deep: the loads of stage
-//     s+STAGES-1 are issued while stage s feeds the matrix cores, and one
-//     explicit wait on the vector-memory counter plus one barrier per stage
-//     hand a stage over;
+//     register staging) into a ring of STAGES buffers: stage s+STAGES is
+//     fetched while stage s+1 is read into registers and stage s feeds the
+//     matrix cores.  One explicit wait on the vector-memory counter plus one
+//     barrier per stage hand a stage over;
+//   * fragments are double-buffered in registers: the LDS reads of the next
+//     k-step are issued between the matrix instructions of the current one
+//     (scheduling hints interleave them), so one wave per SIMD keeps its
+//     matrix pipe busy without waiting on LDS latency;
 //   * LDS rows are XOR-swizzled in 16-byte chunks so that the rows read by one
 //     fragment load fall into distinct banks; the direct-to-LDS lane order is
 //     fixed (lane i writes bytes 16i..16i+15 of the wave's 1 KiB), so each lane
@@ -121,25 +126,34 @@ __device__ __forceinline__ void wait_vm_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+// Same, after this wave's LDS reads have completed as well.
+template <int N>
+__device__ __forceinline__ void wait_lgkm_vm_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+// One matrix instruction.  w: the row operand (kept W^T values, or dense W^T
+// for the dense kinds); a: the column operand (activations).  For the sparse
+// kinds a holds 32 bytes; the dense kinds use its low 16 bytes.
 template <int KIND>
-__device__ __forceinline__ void mma(typename AccOf<KIND>::T &acc, u32x4 w, u32x4 a0, u32x4 a1, uint32_t idx) {
+__device__ __forceinline__ void mma(typename AccOf<KIND>::T &acc, u32x4 w, u32x8 a, uint32_t idx) {
     if constexpr (KIND == W24_F16) {
-        union { u32x4 u[2]; half16 h; } b;
-        b.u[0] = a0;
-        b.u[1] = a1;
-        acc = __builtin_amdgcn_smfmac_f32_32x32x32_f16(__builtin_bit_cast(half8, w), b.h, acc, int(idx), 0, 0);
+        acc = __builtin_amdgcn_smfmac_f32_32x32x32_f16(__builtin_bit_cast(half8, w), __builtin_bit_cast(half16, a),
+                                                        acc, int(idx), 0, 0);
     } else if constexpr (KIND == W24_I8) {
-        union { u32x4 u[2]; intx8 v; } b;
-        b.u[0] = a0;
-        b.u[1] = a1;
-        acc = __builtin_amdgcn_smfmac_i32_32x32x64_i8(__builtin_bit_cast(intx4, w), b.v, acc, int(idx), 0, 0);
+        acc = __builtin_amdgcn_smfmac_i32_32x32x64_i8(__builtin_bit_cast(intx4, w), __builtin_bit_cast(intx8, a), acc,
+                                                       int(idx), 0, 0);
     } else if constexpr (KIND == DENSE_F16) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, w), __builtin_bit_cast(half8, a0),
-                                                      acc, 0, 0, 0);
+        const u32x4 lo = __builtin_shufflevector(a, a, 0, 1, 2, 3);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, w), __builtin_bit_cast(half8, lo), acc,
+                                                      0, 0, 0);
     } else {
-        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(intx4, w), __builtin_bit_cast(intx4, a0),
-                                                     acc, 0, 0, 0);
+        const u32x4 lo = __builtin_shufflevector(a, a, 0, 1, 2, 3);
+        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(intx4, w), __builtin_bit_cast(intx4, lo), acc,
+                                                     0, 0, 0);
     }
 }
 
@@ -150,13 +164,16 @@ __device__ __forceinline__ void store16(void *p, u32x4 v) {
     else *reinterpret_cast<u32x4 *>(p) = v;
 }
 
-// Tile configuration: 2 x 2 waves, TM x TN 32x32 blocks per wave, STAGES LDS
-// buffers, GM tile-rows per L2 group, nontemporal C stores.
-template <int TM_, int TN_, int STAGES_, int GM_, bool NTS_>
+// Tile configuration: WM x WN waves, TM x TN 32x32 blocks per wave, STAGES
+// LDS stage buffers (prefetch distance), GM tile-rows per L2 group,
+// nontemporal C stores.  Direct-to-LDS loads are issued by every wave: their
+// throughput is limited per wavefront (about 4 bytes per clock each on
+// gfx950), so a CU needs 8 or more issuing waves to feed the sparse matrix
+// cores.
+template <int WM_, int WN_, int TM_, int TN_, int STAGES_, int GM_, bool NTS_>
 struct Cfg {
-    static constexpr int TM = TM_, TN = TN_, STAGES = STAGES_, GM = GM_;
+    static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_, STAGES = STAGES_, GM = GM_;
     static constexpr bool NTS = NTS_;
-    static constexpr int WM = 2, WN = 2;
 };
 
 template <int KIND, class CF>
@@ -189,7 +206,7 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     using KT = KindTraits<KIND>;
     using LY = Layout<KIND, CF>;
     using Acc = typename AccOf<KIND>::T;
-    constexpr int TM = CF::TM, TN = CF::TN, GM = CF::GM, P = CF::STAGES - 1;
+    constexpr int TM = CF::TM, TN = CF::TN, GM = CF::GM, NB = CF::STAGES;
     constexpr int WM = CF::WM;
     constexpr int BM = LY::BM, BN = LY::BN, WB = LY::WB, MW = LY::MW;
     constexpr int A_STAGE = LY::A_STAGE, W_STAGE = LY::W_STAGE, STAGE = LY::STAGE;
@@ -228,37 +245,83 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
 
     // ---- direct-to-LDS sources: instruction j of this wave fills the wave's
     // j-th KiB of the A (or W) stage; lane -> (row, position) -> global chunk.
-    const uint8_t *ga[LY::LA];
+    // (32-bit byte offsets from the uniform base pointers keep the per-lane
+    // address state small.)
+    uint32_t oa[LY::LA];
 #pragma unroll
     for (int j = 0; j < LY::LA; ++j) {
         const int byte = (j * LY::NW + wave) * 1024 + lane * 16;
         const int row = byte / 128, pos = (byte / 16) % 8;
-        ga[j] = A + int64_t(min(m0 + row, M - 1)) * a_row + swz128(row, pos) * 16;
+        oa[j] = uint32_t(min(m0 + row, M - 1)) * uint32_t(a_row) + swz128(row, pos) * 16;
     }
-    const uint8_t *gw[LY::LW];
+    uint32_t ow[LY::LW];
 #pragma unroll
     for (int j = 0; j < LY::LW; ++j) {
         const int byte = (j * LY::NW + wave) * 1024 + lane * 16;
         const int row = byte / WB, pos = (byte / 16) % (WB / 16);
-        gw[j] = Wv + int64_t(min(n0 + row, N - 1)) * w_row + swzw<WB>(row, pos) * 16;
+        ow[j] = uint32_t(min(n0 + row, N - 1)) * uint32_t(w_row) + swzw<WB>(row, pos) * 16;
     }
-    const uint32_t *gm_[LY::LM > 0 ? LY::LM : 1];
+    uint32_t om[LY::LM > 0 ? LY::LM : 1];
 #pragma unroll
     for (int j = 0; j < LY::LM; ++j) {
         const int word = (j * LY::NW + wave) * 64 + lane;  // row-major [BN][MW]
-        const int row = word / MW, w = word % MW;
-        gm_[j] = meta + int64_t(min(n0 + row, N - 1)) * m_row + w;
+        const int row = word / (MW > 0 ? MW : 1), w = word % (MW > 0 ? MW : 1);
+        om[j] = (uint32_t(min(n0 + row, N - 1)) * uint32_t(m_row) + w) * 4;
     }
+    const uint8_t *meta_b = reinterpret_cast<const uint8_t *>(meta);
 
+    // Row pitches are often powers of two (K = 1024, 4096), so one stage's
+    // 128-byte slice of every row falls into the same few memory channels.
+    // The K reduction may run in any order, so each tile starts at its own
+    // stage (rotation by tile id): at any moment the tiles in flight read
+    // different K slices and spread over all channels.  The order is fixed per
+    // tile, so results stay deterministic.
+    const int rot = b % S;
     auto issue = [&](int s) {
-        uint8_t *base = smem + (s % CF::STAGES) * STAGE;
+        uint8_t *base = smem + (s % NB) * STAGE;
+        const int sg = (s + rot < S) ? s + rot : s + rot - S;  // global K stage
 #pragma unroll
-        for (int j = 0; j < LY::LA; ++j) dma16(ga[j] + s * 128, base + (j * LY::NW + wave) * 1024);
+        for (int j = 0; j < LY::LA; ++j) dma16(A + (oa[j] + uint32_t(sg * 128)), base + (j * LY::NW + wave) * 1024);
 #pragma unroll
-        for (int j = 0; j < LY::LW; ++j) dma16(gw[j] + s * WB, base + A_STAGE + (j * LY::NW + wave) * 1024);
+        for (int j = 0; j < LY::LW; ++j)
+            dma16(Wv + (ow[j] + uint32_t(sg * WB)), base + A_STAGE + (j * LY::NW + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < LY::LM; ++j)
-            dma4(gm_[j] + s * MW, base + A_STAGE + W_STAGE + (j * LY::NW + wave) * 256);
+            dma4(meta_b + (om[j] + uint32_t(sg * MW * 4)), base + A_STAGE + W_STAGE + (j * LY::NW + wave) * 256);
+    };
+
+    // Fragments of one k-step (one matrix instruction deep) for the wave's
+    // TN channel blocks and TM token blocks.
+    struct Frag {
+        u32x4 w[TN];
+        uint32_t idx[TN];
+        u32x8 a[TM];
+    };
+    auto load_frag = [&](int s, int kk, Frag &F) {
+        const uint8_t *bA = smem + (s % NB) * STAGE;
+        const uint8_t *bW = bA + A_STAGE;
+        const uint32_t *bM = reinterpret_cast<const uint32_t *>(bA + A_STAGE + W_STAGE);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int row = wn * TN * 32 + tn * 32 + r;
+            F.w[tn] = lds16(bW + row * WB + swzw<WB>(row, 2 * kk + h) * 16);
+            if constexpr (KIND == W24_F16) F.idx[tn] = bM[row * MW + kk] >> (16 * h);
+            else if constexpr (KIND == W24_I8) F.idx[tn] = bM[row * MW + 2 * kk + h];
+            else F.idx[tn] = 0;
+        }
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const int row = wm * TM * 32 + tm * 32 + r;
+            if constexpr (KT::kSparse) {
+                // two 16-byte pieces of the 64-byte window: bytes 16h.. and 32+16h..
+                const u32x4 lo = lds16(bA + row * 128 + swz128(row, 4 * kk + h) * 16);
+                const u32x4 hi = lds16(bA + row * 128 + swz128(row, 4 * kk + 2 + h) * 16);
+                F.a[tm] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+                const u32x4 lo = lds16(bA + row * 128 + swz128(row, 2 * kk + h) * 16);
+                F.a[tm] = __builtin_shufflevector(lo, lo, 0, 1, 2, 3, 0, 1, 2, 3);
+            }
+        }
     };
 
     Acc acc[TN][TM];
@@ -267,49 +330,65 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
 #pragma unroll
         for (int j = 0; j < TM; ++j) acc[i][j] = Acc{};
 
+    auto mma_frag = [&](const Frag &F) {
 #pragma unroll
-    for (int s = 0; s < P; ++s)
-        if (s < S) issue(s);
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) mma<KIND>(acc[tn][tm], F.w[tn], F.a[tm], F.idx[tn]);
+    };
+    // Interleave hint: one matrix instruction, then its share of LDS reads.
+    constexpr int NMMA = TN * TM;
+    constexpr int NRD = TN * (KT::kSparse ? 2 : 1) + TM * (KT::kSparse ? 2 : 1);
+    constexpr int RPM = (NRD + NMMA - 1) / NMMA;
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < NMMA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // matrix
+            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // LDS reads
+        }
+    };
 
-    for (int s = 0; s < S; ++s) {
-        // stage s is complete once at most (P-1) younger stages are in flight
-        if (s + P - 1 < S) wait_vm_barrier<(P - 1) * LY::L>();
-        else wait_vm_barrier<0>();
-        if (s + P < S) issue(s + P);  // refills the buffer that stage s-1 used
-        const uint8_t *bA = smem + (s % CF::STAGES) * STAGE;
-        const uint8_t *bW = bA + A_STAGE;
-        const uint32_t *bM = reinterpret_cast<const uint32_t *>(bA + A_STAGE + W_STAGE);
+    // Pipeline: NB stage buffers, the stage s+NB is fetched while stage s+1 is
+    // read into registers and stage s feeds the matrix cores.  Within a stage
+    // the next k-step's fragments are read during the current k-step's
+    // instructions; the stage hand-off (wait + barrier) sits before the last
+    // k-step's instructions so that the next stage's first fragments overlap
+    // them too.
+#pragma unroll
+    for (int s = 0; s < NB; ++s)
+        if (s < S) issue(s);
+    if (NB < S) wait_vm_barrier<(NB - 1) * LY::L>();
+    else wait_vm_barrier<0>();
+    Frag F[2];
+    load_frag(0, 0, F[0]);
+
+    // One stage; STEADY: the ring still has a stage to fetch (s + NB < S).
+    // The next stage's first fragments are read unconditionally: on the last
+    // stage this reads a valid, stale buffer whose values are never used.
+    auto stage = [&](int s, auto steady) {
 #pragma unroll
         for (int kk = 0; kk < KT::kNI; ++kk) {
-            u32x4 wf[TN];
-            uint32_t idx[TN];
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const int row = wn * TN * 32 + tn * 32 + r;
-                wf[tn] = lds16(bW + row * WB + swzw<WB>(row, 2 * kk + h) * 16);
-                if constexpr (KIND == W24_F16) idx[tn] = bM[row * MW + kk] >> (16 * h);
-                else if constexpr (KIND == W24_I8) idx[tn] = bM[row * MW + 2 * kk + h];
-                else idx[tn] = 0;
-            }
-            u32x4 af0[TM], af1[TM];
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                const int row = wm * TM * 32 + tm * 32 + r;
-                if constexpr (KT::kSparse) {
-                    // two 16-byte pieces of the 64-byte window: bytes 16h.. and 32+16h..
-                    af0[tm] = lds16(bA + row * 128 + swz128(row, 4 * kk + h) * 16);
-                    af1[tm] = lds16(bA + row * 128 + swz128(row, 4 * kk + 2 + h) * 16);
+            Frag &cur = F[kk & 1];
+            Frag &nxt = F[(kk + 1) & 1];
+            if (kk + 1 < KT::kNI) {
+                load_frag(s, kk + 1, nxt);
+            } else {
+                // stage s is fully in registers; stage s+1 must be complete
+                if constexpr (decltype(steady)::value) {
+                    wait_lgkm_vm_barrier<(NB - 2) * LY::L>();
+                    issue(s + NB);  // reuses stage s's buffer
                 } else {
-                    af0[tm] = lds16(bA + row * 128 + swz128(row, 2 * kk + h) * 16);
-                    af1[tm] = af0[tm];
+                    wait_lgkm_vm_barrier<0>();
                 }
+                load_frag(s + 1, 0, nxt);
             }
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm) mma<KIND>(acc[tn][tm], wf[tn], af0[tm], af1[tm], idx[tn]);
+            mma_frag(cur);
+            interleave();
         }
-    }
+    };
+    int s = 0;
+    for (; s + NB < S; ++s) stage(s, std::true_type{});
+    for (; s < S; ++s) stage(s, std::false_type{});
 
     // ---- epilogue.  Lane (h, r) holds, for 32x32 block (tn, tm) and q = 0..3,
     // channels n = tn*32 + 8q + 4h .. +3 of token m = tm*32 + r.
@@ -387,30 +466,71 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
     return hipGetLastError();
 }
 
-// Tile shapes: 128 tokens x 256 channels, 4 waves of 64 tokens x 128 channels.
-using CfgF16 = Cfg<2, 4, 4, 8, false>;
-using CfgI8 = Cfg<2, 4, 4, 8, true>;
+// Tile shapes (measured on MI355X at the ViT / BERT / ViT-Base shapes):
+//   Big   256 x 256, 8 waves of 64 tokens x 128 channels, one workgroup per
+//         CU with eight load-issuing waves -- best once there are about as
+//         many tiles as CUs and K is long enough to amortise the prologue;
+//   Mid   128 x 256, 4 waves, 2 stages (68 KiB LDS, two workgroups per CU) --
+//         the int8 fp32-output GEMMs with short K, whose time is dominated by
+//         the output stream: two resident workgroups overlap one tile's
+//         stores with the other's loads;
+//   Small 128 x 128, 4 waves, 3 stages (two workgroups per CU) -- narrow
+//         outputs (N = 1024) that would leave CUs idle with big tiles.
+template <bool NTS>
+using CfgBig = Cfg<4, 2, 2, 4, 3, 8, NTS>;
+template <bool NTS>
+using CfgBigDense = Cfg<4, 2, 2, 4, 2, 8, NTS>;
+template <bool NTS>
+using CfgMid = Cfg<2, 2, 2, 4, 2, 8, NTS>;
+template <bool NTS>
+using CfgSmall = Cfg<2, 2, 2, 2, 3, 8, NTS>;
+
+enum Shape { SHAPE_BIG, SHAPE_MID, SHAPE_SMALL };
+
+// f16 kinds: big tiles when they still give >= 3/4 of a tile per CU.
+static Shape pick_f16(int M, int N) {
+    const long big = long((M + 255) / 256) * long((N + 255) / 256);
+    return big >= 192 ? SHAPE_BIG : SHAPE_SMALL;
+}
+// int8 kinds write 4-byte outputs: short-K problems are output-bound.
+static Shape pick_i8(int M, int N, int K) {
+    if (K <= 1024) return SHAPE_MID;
+    const long big = long((M + 255) / 256) * long((N + 255) / 256);
+    return big >= 192 ? SHAPE_BIG : SHAPE_SMALL;
+}
+
+template <int KIND, int EPI, bool NTS, bool DENSE>
+static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const uint32_t *meta, const float *scale,
+                               void *C, int M, int N, int K, hipStream_t st) {
+    if (sh == SHAPE_BIG) {
+        if constexpr (DENSE) return launch<KIND, EPI, CfgBigDense<NTS>>(A, Wv, meta, scale, C, M, N, K, st);
+        else return launch<KIND, EPI, CfgBig<NTS>>(A, Wv, meta, scale, C, M, N, K, st);
+    }
+    if (sh == SHAPE_MID) return launch<KIND, EPI, CfgMid<NTS>>(A, Wv, meta, scale, C, M, N, K, st);
+    return launch<KIND, EPI, CfgSmall<NTS>>(A, Wv, meta, scale, C, M, N, K, st);
+}
 
 hipError_t launch_dense_f16(const void *A, const void *Wt, void *C, int M, int N, int K, hipStream_t st) {
-    return launch<DENSE_F16, EPI_F16, Cfg<2, 4, 3, 8, false>>(A, Wt, nullptr, nullptr, C, M, N, K, st);
+    return launch_shape<DENSE_F16, EPI_F16, false, true>(pick_f16(M, N), A, Wt, nullptr, nullptr, C, M, N, K, st);
 }
 
 hipError_t launch_w24_f16(const void *A, const void *vals, const uint32_t *meta, void *C, int M, int N, int K,
                           hipStream_t st) {
-    return launch<W24_F16, EPI_F16, CfgF16>(A, vals, meta, nullptr, C, M, N, K, st);
+    return launch_shape<W24_F16, EPI_F16, false, false>(pick_f16(M, N), A, vals, meta, nullptr, C, M, N, K, st);
 }
 
 hipError_t launch_dense_i8(const void *A, const void *Wt, const float *scale, void *C, int M, int N, int K,
                            hipStream_t st) {
-    using CD = Cfg<2, 4, 3, 8, true>;
-    if (scale) return launch<DENSE_I8, EPI_F32_SCALE, CD>(A, Wt, nullptr, scale, C, M, N, K, st);
-    return launch<DENSE_I8, EPI_I32, CD>(A, Wt, nullptr, nullptr, C, M, N, K, st);
+    const Shape sh = pick_i8(M, N, K);
+    if (scale) return launch_shape<DENSE_I8, EPI_F32_SCALE, true, true>(sh, A, Wt, nullptr, scale, C, M, N, K, st);
+    return launch_shape<DENSE_I8, EPI_I32, true, true>(sh, A, Wt, nullptr, nullptr, C, M, N, K, st);
 }
 
 hipError_t launch_w24_i8(const void *A, const void *vals, const uint32_t *meta, const float *scale, void *C,
                          int M, int N, int K, hipStream_t st) {
-    if (scale) return launch<W24_I8, EPI_F32_SCALE, CfgI8>(A, vals, meta, scale, C, M, N, K, st);
-    return launch<W24_I8, EPI_I32, CfgI8>(A, vals, meta, nullptr, C, M, N, K, st);
+    const Shape sh = pick_i8(M, N, K);
+    if (scale) return launch_shape<W24_I8, EPI_F32_SCALE, true, false>(sh, A, vals, meta, scale, C, M, N, K, st);
+    return launch_shape<W24_I8, EPI_I32, true, false>(sh, A, vals, meta, nullptr, C, M, N, K, st);
 }
 
 }  // namespace ssg

@@ -151,6 +151,15 @@ def test_w24_i8_cfg2(lib, gpu):
         assert np.array_equal(C.view(np.uint32), ref.view(np.uint32))
 
 
+def test_i8_large_tile_path(lib, gpu):
+    # K > 1024 with many tiles selects the 256 x 256 eight-wave kernels.
+    case = wl.random_24_i8(np.random.default_rng(14), 4096, 2048, 3072)
+    C = run_w24_i8(lib, case["A"], case["Wp"], case["scale"])
+    assert np.array_equal(C.view(np.uint32), oracle.ref_gemm_i8(case["A"], case["Wp"], case["scale"]).view(np.uint32))
+    Cd = H(lib.dense_gemm_i8(T(case["A"]), T(case["W"].T), None))
+    assert np.array_equal(Cd, oracle.ref_gemm_i8(case["A"], case["W"]))
+
+
 @pytest.mark.parametrize("gname", ["qkv", "fc2"])
 def test_w24_i8_cfg5_layer0(lib, gpu, gname):
     for g in wl.cfg5_layers("i8", layers=1):
