@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "effective TFLOPS/TOPS of sparse GEMM + speedup vs dense MFMA GEMM, same shape"
 CACHE_BYTES = 256 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_w24_gemm_i8_vit_base_fc1.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w24_gemm_i8_vit_base_fc1.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "structured_sparse_gemm_w24_amd", "csrc", "kernels", f)
                   for f in ("gemm.hip", "common.h")]
 
@@ -66,10 +66,18 @@ def read_traffic():
 
 
 class Timer:
-    """HIP events on torch's current stream (the stream the kernels are launched on)."""
+    """HIP events on the stream the kernels are launched on.
 
-    def __init__(self, torch):
+    graph=True captures the `steps` launches into one HIP graph (the kernels
+    allocate nothing and record no memsets, so they capture cleanly) and
+    times its replay: the GPU then runs the launches back to back without
+    host launch gaps, so the per-step time is the kernel's own duration plus
+    the hardware's dispatch gap.  graph=False times eager launches from
+    Python."""
+
+    def __init__(self, torch, graph=True):
         self.torch = torch
+        self.graph = graph
 
     def __call__(self, fn, steps, warmup):
         torch = self.torch
@@ -77,10 +85,25 @@ class Timer:
             fn(i)
         torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for i in range(steps):
-            fn(i)
-        e.record()
+        if self.graph:
+            stream = torch.cuda.Stream()
+            stream.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(steps):
+                        fn(i)
+            torch.cuda.current_stream().wait_stream(stream)
+            g.replay()  # warm replay
+            torch.cuda.synchronize()
+            s.record()
+            g.replay()
+            e.record()
+        else:
+            s.record()
+            for i in range(steps):
+                fn(i)
+            e.record()
         torch.cuda.synchronize()
         return s.elapsed_time(e) / steps  # ms per call
 
@@ -180,6 +203,7 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="table mode: every workload and kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--warm", action="store_true", help="one input set (cache-resident) instead of rotating")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a replayed HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain device copy of known size (for scaling HBM byte counters)")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -203,7 +227,7 @@ def main(argv=None):
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    timer = Timer(torch)
+    timer = Timer(torch, graph=not a.eager)
     if a.copy_calibration:
         return copy_calibration(torch, a.steps)
     log("device", ssg.ssg_device_arch())
@@ -214,6 +238,10 @@ def main(argv=None):
     M, K, N = c["M"], c["K"], c["N"]
     log(f"workload vit_base_mlp_fc1 2:4 int8 {M}x{K}x{N}, steps {a.steps}, warmup {a.warmup}")
     r = w24_i8_case(torch, ssg, perf, c, a.steps, a.warmup, timer, rotate=not a.warm)
+    t_eager = Timer(torch, graph=False)(
+        lambda i: ssg.w24_gemm_i8(r["sets"][i % r["rotate_sets"]]["A"], r["sets"][i % r["rotate_sets"]]["vals"],
+                                  r["sets"][i % r["rotate_sets"]]["meta"], r["sets"][i % r["rotate_sets"]]["scale"],
+                                  out=r["sets"][i % r["rotate_sets"]]["C"]), a.steps, a.warmup)
     nz, de = perf.w24_ops(M, N, K)
     t = r["t_sparse_ms"] / 1e3
     bytes_ = perf.w24_bytes(M, N, K, 1, 1, 4, scale=True)
@@ -240,6 +268,8 @@ def main(argv=None):
         "dense_equivalent_tops": de / t / 1e12,
         "speedup_vs_dense": perf.speedup(r["t_dense_ms"], r["t_sparse_ms"]),
         "dense_i8_ms": r["t_dense_ms"],
+        "timing": "HIP graph of the timed steps replayed on one stream, HIP events around the replay",
+        "eager_ms_per_step": t_eager,
         "roofline": perf.roofline(achieved, perf.PEAK_HBM_GBS, "GB/s", "hbm", traffic),
         "cpu_baseline": None,
     }
