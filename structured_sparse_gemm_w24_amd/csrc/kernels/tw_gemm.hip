@@ -8,211 +8,308 @@
 // transpose A so that the picked rows are contiguous; this kernel takes the
 // K-major At [K][M].
 //
-// One workgroup handles one work item (tile t, block of BM tokens):
-//   * the kept rows of At are gathered stage by stage (BK rows per stage);
-//     16 lanes read one picked row's 8*16 tokens as 256 contiguous bytes;
-//   * every thread owns an 8 (k) x 8 (token) block, transposes it in
-//     registers (byte permutes) and writes 8 K-contiguous 16-byte rows to LDS,
-//     which is the operand layout of the matrix instruction;
-//   * V_t's stage (rows padded with zeros to a multiple of 16) is copied to
-//     LDS the same way; K_t tails are zero on both operands;
-//   * v_mfma_f32_16x16x32_f16 accumulates D[token][j] in fp32;
-//   * the epilogue builds the tile's full G-wide output window in LDS: zeros,
-//     then the rounded (nearest-even) accumulators scattered to column
-//     offset_n[j]; the window is then stored with 16-byte coalesced writes, so
-//     pruned columns of C come out as +0 without a separate fill.
-// Index arrays are software-pipelined two stages ahead of the data, so the
-// gather never waits on its own index load.  Work items are ordered
-// token-block-major with tiles heaviest first (the packer's tile_order), and
-// block ids are remapped so that each XCD owns a contiguous range of items:
-// the tiles that share a token block share its At rows in one L2.
+// One workgroup (8 waves) handles one work item: a block of BM = 128 tokens
+// of one tile.
+//   * The tile's offset_k list is copied to LDS (KCAP entries at a time);
+//     every stage of BK picked rows is then gathered global -> LDS with
+//     direct-to-LDS loads: a picked row of At is 256 contiguous bytes for the
+//     block's tokens, so 16 lanes fetch one row.  V_t's rows for the stage
+//     are copied the same way.  Padding rows (N_t rounded up to 16) and the
+//     K_t tail read a zero page, so both operands are zero there.  Stages
+//     live in a ring of NB buffers handed over with one counter wait and one
+//     barrier per stage.
+//   * The At stage stays K-major in LDS ([k][token], 16-byte chunks XOR
+//     swizzled by row).  The matrix instruction wants 8 consecutive k of one
+//     token per lane; gfx950's transposing LDS read gives exactly that:
+//     within a 16-lane group, lane i receives element i%4 of the 8-byte run
+//     read by lane 4e + i/4 (e = 0..3), so lanes aimed at rows k0 + j/4,
+//     tokens 4(j%4).. return 4 consecutive k per token; two reads give 8.
+//   * v_mfma_f32_16x16x32_f16 accumulates D[j][token] = sum_k V_t[j][k] At[k][token];
+//     each wave owns 16 tokens and all NJ = ceil(N_t/16) column blocks of the
+//     tile (NJ is a template parameter: one instantiation per value).
+//   * Epilogue: the tile's G-wide output window for the 128 tokens is built in
+//     LDS (zeros, then accumulators rounded to nearest even and scattered to
+//     column offset_n[j]) and stored with 16-byte coalesced writes, so pruned
+//     columns of C come out as +0 without a separate fill.
+//   * The production shape (32-row stages, three buffers, 512-entry index
+//     chunks) needs 52 KiB of LDS and under 85 VGPRs, so three workgroups
+//     share a CU: one workgroup's epilogue stores and index loads overlap the
+//     others' main loops.
+// Work items are ordered token-block-major with tiles heaviest first (the
+// packer's tile_order), and block ids are remapped so each XCD owns a
+// contiguous range of items: the tiles that share a token block share its At
+// rows in one L2.
 #include "common.h"
 #include "launch.h"
 
 namespace ssg {
 
-namespace tw {
-constexpr int NT = 256;  // 4 waves
-constexpr int BM = 128;  // tokens per work item
-constexpr int BK = 128;  // gathered k per stage
-constexpr int ROWB = BK * 2;  // bytes per LDS row (16 chunks)
+// A zero page: the source of padding rows and K tails.
+__device__ __attribute__((aligned(256))) uint16_t g_tw_zero[128];
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 15); }
-}  // namespace tw
+namespace {
 
-template <int GMAX>
-__global__ void __launch_bounds__(tw::NT)
+typedef __attribute__((address_space(3))) void *tw_lds_ptr;
+
+__device__ __forceinline__ void tw_dma16(const void *g, uint8_t *wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (tw_lds_ptr)wave_base, 16, 0, 0);
+}
+
+// Wait until at most n of this wave's direct-to-LDS loads are outstanding and
+// its LDS reads have completed, then synchronise the workgroup.
+__device__ __forceinline__ void tw_wait_barrier(int n) {
+    switch (n) {
+#define TW_WAIT(N) \
+    case N: asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+        TW_WAIT(1) TW_WAIT(2) TW_WAIT(3) TW_WAIT(4) TW_WAIT(5) TW_WAIT(6) TW_WAIT(7)
+        TW_WAIT(8) TW_WAIT(9) TW_WAIT(10) TW_WAIT(11) TW_WAIT(12)
+#undef TW_WAIT
+        default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    }
+}
+
+// Column operand of two k32 steps: four transposing reads at byte offsets
+// 0, 1024 (k + 4), 8192 (k + 32) and 9216 (k + 36) from addr, waited for in
+// the same statement so no result register is live while its load is in
+// flight.
+__device__ __forceinline__ void tw_read_b(uint32_t addr, u32x2 &b0, u32x2 &b1, u32x2 &b2, u32x2 &b3) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:8192\n\t"
+        "ds_read_b64_tr_b16 %3, %4 offset:9216\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
+        : "v"(addr)
+        : "memory");
+}
+
+// Column operand of one k32 step: two transposing reads (k and k + 4).
+__device__ __forceinline__ void tw_read_b2(uint32_t addr, u32x2 &b0, u32x2 &b1) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2\n\t"
+        "ds_read_b64_tr_b16 %1, %2 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(b0), "=&v"(b1)
+        : "v"(addr)
+        : "memory");
+}
+
+}  // namespace
+
+// BK picked rows per stage (32 or 64), NB stage buffers, KCAP offset_k
+// entries held in LDS at a time, WPE waves per SIMD the register allocation
+// must allow (two workgroups per CU need 4).
+template <int BK_, int NB_, int KCAP_, int WPE_>
+struct TwCfg {
+    static constexpr int NW = 8, NT = NW * 64;
+    static constexpr int BM = 128;   // tokens per work item (8 blocks of 16)
+    static constexpr int BK = BK_;
+    static constexpr int KS = BK / 32;  // k32 steps per stage
+    static constexpr int NB = NB_;
+    static constexpr int KCAP = KCAP_;
+    static constexpr int WPE = WPE_;
+    static constexpr int GMAX = 128;  // widest supported tile
+    static constexpr int A_STAGE = BK * BM * 2;    // [BK][BM] halves
+    static constexpr int W_STAGE = GMAX * BK * 2;  // [GMAX][BK] halves
+    static constexpr int STAGE = A_STAGE + W_STAGE;
+    static constexpr int LA = A_STAGE / 1024 / NW;  // A loads per wave per stage
+    static constexpr int WROWS = 1024 / (BK * 2);   // V_t rows per direct-to-LDS load
+    static constexpr int WIN_ROW = GMAX * 2 + 16;   // output window row stride (bytes)
+    static constexpr int IDX_OFF = NB * STAGE;       // offset_k chunk, KCAP ints
+    static constexpr int OFFN_OFF = IDX_OFF + KCAP * 4;  // offset_n of the tile, GMAX ints
+    static constexpr int SMEM = OFFN_OFF + GMAX * 4;
+    static_assert(BK == 32 || BK == 64, "stage depth");
+    static_assert(LA >= 1 && LA * NW * 1024 == A_STAGE, "A stage must split over the waves");
+    static_assert(KCAP % NT == 0, "index chunk must split over the threads");
+    static_assert(BM * WIN_ROW <= NB * STAGE, "output window must fit in the stage ring");
+    static_assert(NB >= 2 && NB <= 4, "ring depth");
+};
+
+// At stage: row r (picked k), 16-byte chunk c (8 tokens) -> stored chunk.  The
+// four rows one transposing read touches land in distinct 32-byte bank groups.
+__device__ __forceinline__ int tw_swz_a(int r, int c) { return c ^ (2 * (r & 3)); }
+// V_t stage: row j (channel), 16-byte chunk c (8 k) of a BK-wide row -> stored
+// chunk; the 8 rows read by 8 consecutive lanes cover all banks.
+template <int BK>
+__device__ __forceinline__ int tw_swz_w(int j, int c) {
+    if constexpr (BK == 64) return c ^ ((j ^ (j >> 3)) & 7);
+    else return c ^ ((j >> 1) & 3);
+}
+
+template <class CF, int NJ>
+__device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restrict__ At,
+                                        const uint16_t *__restrict__ vt, const int32_t *__restrict__ offk,
+                                        const int32_t *__restrict__ offn, int kt, int nt, int G, int m0,
+                                        uint16_t *__restrict__ Cw, int M, int N) {
+    constexpr int NW = CF::NW, NT = CF::NT, BM = CF::BM, BK = CF::BK, NB = CF::NB, KCAP = CF::KCAP;
+    constexpr int A_STAGE = CF::A_STAGE, STAGE = CF::STAGE, LA = CF::LA, KS = CF::KS, WROWS = CF::WROWS;
+    constexpr int WIN_ROW = CF::WIN_ROW;
+    int32_t *s_idx = reinterpret_cast<int32_t *>(smem + CF::IDX_OFF);
+    int32_t *s_offn = reinterpret_cast<int32_t *>(smem + CF::OFFN_OFF);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int ld = (kt + 7) & ~7;
+    // V_t loads per stage: NJ*16 rows of 2*BK bytes = NJ*KS KiB, round-robin over waves
+    const int lw = (NJ * KS - wave + NW - 1) / NW;
+    const int per_stage = LA + lw;
+
+    // A loads: instruction j of the wave covers stage rows 4q .. 4q+3 (q = j*NW + wave);
+    // lane -> row 4q + lane/16, stored chunk lane%16.
+    const int a_sub = lane >> 4, a_pos = lane & 15;
+    // W loads: rows WROWS*q ..; lane -> row WROWS*q + lane/(8*KS), stored chunk lane%(4*KS).
+    const int w_sub = lane / (4 * KS), w_pos = lane % (4 * KS);
+
+    floatx4 acc[NJ > 0 ? NJ : 1];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int tok_mb = wave * 16;  // this wave's 16 tokens inside the block
+    const int g16 = lane >> 4, j16 = lane & 15;
+    // transposing-read address inside a stage: row 8*g16 + j16/4, tokens tok_mb + 4*(j16%4)
+    const int rb = 8 * g16 + (j16 >> 2);
+    const int tokl = tok_mb + 4 * (j16 & 3);
+    const uint32_t b_off = rb * (BM * 2) + tw_swz_a(rb, tokl >> 3) * 16 + (tokl & 7) * 2;
+    const uint32_t smem_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+
+    if (tid < nt && tid < CF::GMAX) s_offn[tid] = offn[tid];  // read back after the barriers below
+    if constexpr (NJ > 0) {
+        for (int cb = 0; cb < kt; cb += KCAP) {
+            const int ck = min(KCAP, kt - cb);  // picked rows in this chunk
+            if (cb > 0) __syncthreads();        // every wave is done with the previous list
+            {
+                // all loads first (clamped to the last entry), then the guarded LDS writes
+                constexpr int PER = KCAP / NT;
+                int32_t v[PER];
+#pragma unroll
+                for (int p = 0; p < PER; ++p) v[p] = offk[cb + min(tid + p * NT, ck - 1)];
+#pragma unroll
+                for (int p = 0; p < PER; ++p)
+                    if (tid + p * NT < ck) s_idx[tid + p * NT] = v[p];
+            }
+            __syncthreads();
+            const int S = (ck + BK - 1) / BK;
+
+            auto issue = [&](int s) {
+                uint8_t *base = smem + (s % NB) * STAGE;
+#pragma unroll
+                for (int j = 0; j < LA; ++j) {
+                    const int q = j * NW + wave;
+                    const int r = 4 * q + a_sub;  // stage row
+                    const int kk = s * BK + r;    // picked row inside the chunk
+                    const int tok = m0 + tw_swz_a(r, a_pos) * 8;
+                    const void *src = g_tw_zero;
+                    if (kk < ck && tok < M) src = At + int64_t(s_idx[kk]) * M + tok;
+                    tw_dma16(src, base + q * 1024);
+                }
+                for (int j = 0; j < lw; ++j) {
+                    const int q = j * NW + wave;
+                    const int row = WROWS * q + w_sub;
+                    const int k = cb + s * BK + tw_swz_w<BK>(row, w_pos) * 8;
+                    const void *src = g_tw_zero;
+                    if (row < nt && k < ld) src = vt + int64_t(row) * ld + k;
+                    tw_dma16(src, base + A_STAGE + q * 1024);
+                }
+            };
+
+            for (int s = 0; s < NB - 1 && s < S; ++s) issue(s);
+            for (int s = 0; s < S; ++s) {
+                // stage s complete; the younger stages already issued may stay in flight
+                tw_wait_barrier(min(NB - 2, S - 1 - s) * per_stage);
+                // the buffer of stage s-1 is free: refill it with stage s+NB-1
+                if (s + NB - 1 < S) issue(s + NB - 1);
+                const uint32_t stage_off = (s % NB) * STAGE;
+                const uint8_t *bW = smem + stage_off + A_STAGE;
+                u32x2 b[2 * KS];
+                if constexpr (KS == 2) tw_read_b(smem_addr + stage_off + b_off, b[0], b[1], b[2], b[3]);
+                else tw_read_b2(smem_addr + stage_off + b_off, b[0], b[1]);
+#pragma unroll
+                for (int k32 = 0; k32 < KS; ++k32) {
+                    const half8 bf = __builtin_bit_cast(
+                        half8, __builtin_shufflevector(b[2 * k32], b[2 * k32 + 1], 0, 1, 2, 3));
+                    u32x4 wf[NJ];
+#pragma unroll
+                    for (int jb = 0; jb < NJ; ++jb) {
+                        const int row = jb * 16 + j16;
+                        wf[jb] = *reinterpret_cast<const u32x4 *>(bW + row * (BK * 2) +
+                                                                  tw_swz_w<BK>(row, k32 * 4 + g16) * 16);
+                    }
+#pragma unroll
+                    for (int jb = 0; jb < NJ; ++jb)
+                        acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, wf[jb]), bf,
+                                                                         acc[jb], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue: G-wide output window in LDS (aliases the stage ring); rows
+    // padded by 16 bytes so the 16 tokens one scatter instruction writes fall in
+    // distinct banks
+    __syncthreads();
+    uint8_t *win = smem;
+    const int wrow_chunks = G / 8;  // 16-byte chunks per window row
+    for (int c = tid; c < BM * wrow_chunks; c += NT)
+        *reinterpret_cast<u32x4 *>(win + (c / wrow_chunks) * WIN_ROW + (c % wrow_chunks) * 16) = u32x4{0, 0, 0, 0};
+    __syncthreads();
+    // acc[jb] lane (g16, j16) holds D[j = 16jb + 4*g16 + i][token = tok_mb + j16]
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = jb * 16 + 4 * g16 + i;
+            if (j < nt)
+                *reinterpret_cast<uint16_t *>(win + (tok_mb + j16) * WIN_ROW + s_offn[j] * 2) =
+                    __builtin_bit_cast(uint16_t, (_Float16)acc[jb][i]);
+        }
+    }
+    __syncthreads();
+    for (int c = tid; c < BM * wrow_chunks; c += NT) {
+        const int row = c / wrow_chunks, ch = c % wrow_chunks;
+        const int m = m0 + row;
+        if (m < M) st16(Cw + int64_t(m) * N + ch * 8, *reinterpret_cast<const u32x4 *>(win + row * WIN_ROW + ch * 16));
+    }
+}
+
+template <class CF>
+__global__ void __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(CF::WPE)))
 tw_gemm_kernel(const uint16_t *__restrict__ At, const uint16_t *__restrict__ vals, const int32_t *__restrict__ offset_k,
                const int32_t *__restrict__ offset_n, const int32_t *__restrict__ v_ptr,
                const int32_t *__restrict__ k_ptr, const int32_t *__restrict__ n_ptr,
                const int32_t *__restrict__ tile_order, int T, int G, uint16_t *__restrict__ C, int M, int N) {
-    using namespace tw;
-    constexpr int NBJ = GMAX / 16;  // max 16-column blocks
-    static_assert(BM * GMAX * 2 <= 2 * BM * ROWB, "output window must fit in the A buffers");
-
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * ROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t sW[2][GMAX * ROWB];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-
-    const int n_mb = (M + BM - 1) / BM;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[CF::SMEM];
+    const int n_mb = (M + CF::BM - 1) / CF::BM;
     const int item = xcd_remap(blockIdx.x, n_mb * T);
     const int mb = item / T;
     const int t = tile_order[item % T];
-    const int m0 = mb * BM;
-
     const int kp0 = k_ptr[t], kt = k_ptr[t + 1] - kp0;
     const int np0 = n_ptr[t], nt = n_ptr[t + 1] - np0;
-    const int vp0 = v_ptr[t];
-    const int ld = (kt + 7) & ~7;
-    const int nbj = (nt + 15) >> 4;
-    const int S = (kt + BK - 1) / BK;
-    const int32_t *okt = offset_k + kp0;
-    const uint16_t *vt = vals + vp0;
-
-    // gather role: token chunk tc (8 tokens), k group kg (8 picked rows)
-    const int tc = tid & 15, kg = tid >> 4;
-    const bool tok_ok = (m0 + tc * 8) < M;
-    const uint16_t *at_base = At + m0 + tc * 8;
-
-    int ridx[8], rnext[8];
-    u32x4 ra[8], rw[NBJ];
-
-    auto load_idx = [&](int s, int *dst) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int kk = s * BK + kg * 8 + j;
-            dst[j] = (s < S && kk < kt) ? okt[kk] : -1;
-        }
-    };
-    auto load_data = [&](int s) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            ra[j] = u32x4{0, 0, 0, 0};
-            if (tok_ok && ridx[j] >= 0) ra[j] = ld16(at_base + int64_t(ridx[j]) * M);
-        }
-        const int kb = s * BK;
-#pragma unroll
-        for (int i = 0; i < NBJ; ++i) {
-            rw[i] = u32x4{0, 0, 0, 0};
-            const int row = (tid >> 4) + 16 * i, col = tid & 15;
-            const int k = kb + col * 8;
-            if (i < nbj && row < nt && k < ld) rw[i] = ld16(vt + int64_t(row) * ld + k);
-        }
-    };
-    auto store_data = [&](int buf) {
-        // 8x8 transpose: out[i] holds k = kg*8 .. +7 of token tc*8 + i
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-            u32x4 o;
-            o.x = __builtin_amdgcn_perm(ra[1][i >> 1], ra[0][i >> 1], sel);
-            o.y = __builtin_amdgcn_perm(ra[3][i >> 1], ra[2][i >> 1], sel);
-            o.z = __builtin_amdgcn_perm(ra[5][i >> 1], ra[4][i >> 1], sel);
-            o.w = __builtin_amdgcn_perm(ra[7][i >> 1], ra[6][i >> 1], sel);
-            const int row = tc * 8 + i;
-            *reinterpret_cast<u32x4 *>(&sA[buf][row * ROWB + swz(row, kg) * 16]) = o;
-        }
-#pragma unroll
-        for (int i = 0; i < NBJ; ++i) {
-            if (i < nbj) {
-                const int row = (tid >> 4) + 16 * i, col = tid & 15;
-                *reinterpret_cast<u32x4 *>(&sW[buf][row * ROWB + swz(row, col) * 16]) = rw[i];
-            }
-        }
-    };
-
-    floatx4 acc[2][NBJ];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int j = 0; j < NBJ; ++j) acc[a][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    if (S > 0) {
-        load_idx(0, ridx);
-        load_idx(1, rnext);
-        load_data(0);
-        store_data(0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ridx[j] = rnext[j];
-        load_idx(2, rnext);
-    }
-    __syncthreads();
-
-    const int r16 = lane & 15, q = lane >> 4;
-    for (int s = 0; s < S; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < S) load_data(s + 1);
-        const uint8_t *bA = sA[buf];
-        const uint8_t *bW = sW[buf];
-#pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-            const int chunk = kk * 4 + q;
-            half8 af[2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const int row = wave * 32 + a * 16 + r16;
-                af[a] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4 *>(bA + row * ROWB + swz(row, chunk) * 16));
-            }
-#pragma unroll
-            for (int j = 0; j < NBJ; ++j) {
-                if (j < nbj) {
-                    const int row = j * 16 + r16;
-                    const half8 bf =
-                        __builtin_bit_cast(half8, *reinterpret_cast<const u32x4 *>(bW + row * ROWB + swz(row, chunk) * 16));
-#pragma unroll
-                    for (int a = 0; a < 2; ++a)
-                        acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf, acc[a][j], 0, 0, 0);
-                }
-            }
-        }
-        if (s + 1 < S) {
-            store_data(buf ^ 1);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) ridx[j] = rnext[j];
-            load_idx(s + 3, rnext);
-        }
-        __syncthreads();
-    }
-
-    // ---- epilogue: G-wide output window in LDS (aliases the A buffers)
-    uint16_t *win = reinterpret_cast<uint16_t *>(&sA[0][0]);
-    const int wrow_chunks = G / 8;  // 16-byte chunks per window row
-    for (int c = tid; c < BM * wrow_chunks; c += NT)
-        *reinterpret_cast<u32x4 *>(win + c * 8) = u32x4{0, 0, 0, 0};
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NBJ; ++j) {
-        const int jj = j * 16 + r16;
-        if (j < nbj && jj < nt) {
-            const int col = offset_n[np0 + jj];
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = wave * 32 + a * 16 + q * 4 + i;
-                    win[row * G + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[a][j][i]);
-                }
-        }
-    }
-    __syncthreads();
-    const int64_t c0 = int64_t(t) * G;
-    for (int c = tid; c < BM * wrow_chunks; c += NT) {
-        const int row = c / wrow_chunks, ch = c % wrow_chunks;
-        const int m = m0 + row;
-        if (m < M) st16(C + int64_t(m) * N + c0 + ch * 8, *reinterpret_cast<const u32x4 *>(win + row * G + ch * 8));
+    const uint16_t *vt = vals + v_ptr[t];
+    const int32_t *offk = offset_k + kp0;
+    const int32_t *offn = offset_n + np0;
+    uint16_t *Cw = C + int64_t(t) * G;
+    const int m0 = mb * CF::BM;
+    switch ((nt + 15) >> 4) {
+#define TW_CASE(J) \
+    case J: tw_item<CF, J>(smem, At, vt, offk, offn, kt, nt, G, m0, Cw, M, N); break;
+        TW_CASE(0) TW_CASE(1) TW_CASE(2) TW_CASE(3) TW_CASE(4) TW_CASE(5) TW_CASE(6) TW_CASE(7) TW_CASE(8)
+#undef TW_CASE
+        default: break;
     }
 }
+
+// 32-row stages, three buffers, 512 picked rows per index chunk: 51.7 KiB of
+// LDS and at most 85 VGPRs (6 waves per SIMD), so three workgroups share a CU.
+using TwProd = TwCfg<32, 3, 512, 6>;
 
 hipError_t launch_tw_f16(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
                          const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
                          const int32_t *tile_order, int T, int G, void *C, int M, int N, hipStream_t st) {
-    const int n_mb = (M + tw::BM - 1) / tw::BM;
-    const dim3 grid(n_mb * T), block(tw::NT);
-    hipLaunchKernelGGL((tw_gemm_kernel<128>), grid, block, 0, st, static_cast<const uint16_t *>(At),
-                       static_cast<const uint16_t *>(vals), offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G,
-                       static_cast<uint16_t *>(C), M, N);
+    const int n_mb = (M + TwProd::BM - 1) / TwProd::BM;
+    hipLaunchKernelGGL(tw_gemm_kernel<TwProd>, dim3(n_mb * T), dim3(TwProd::NT), 0, st,
+                       static_cast<const uint16_t *>(At), static_cast<const uint16_t *>(vals), offset_k, offset_n,
+                       v_ptr, k_ptr, n_ptr, tile_order, T, G, static_cast<uint16_t *>(C), M, N);
     return hipGetLastError();
 }
 
