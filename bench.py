@@ -73,18 +73,25 @@ class Timer:
     times its replay: the GPU then runs the launches back to back without
     host launch gaps, so the per-step time is the kernel's own duration plus
     the hardware's dispatch gap.  graph=False times eager launches from
-    Python."""
+    Python.  `reps` replays are timed one by one; the call returns the median
+    per-step time and `stats` also gives p10 / p90 over the replays."""
 
-    def __init__(self, torch, graph=True):
+    def __init__(self, torch, graph=True, reps=1):
         self.torch = torch
         self.graph = graph
+        self.reps = reps
 
     def __call__(self, fn, steps, warmup):
+        return self.stats(fn, steps, warmup)["ms"]
+
+    def stats(self, fn, steps, warmup, reps=None):
         torch = self.torch
+        reps = reps or self.reps
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
         if self.graph:
             stream = torch.cuda.Stream()
             stream.wait_stream(torch.cuda.current_stream())
@@ -96,16 +103,24 @@ class Timer:
             torch.cuda.current_stream().wait_stream(stream)
             g.replay()  # warm replay
             torch.cuda.synchronize()
-            s.record()
-            g.replay()
-            e.record()
+            for _ in range(reps):
+                s.record()
+                g.replay()
+                e.record()
+                torch.cuda.synchronize()
+                times.append(s.elapsed_time(e) / steps)
+            del g
         else:
-            s.record()
-            for i in range(steps):
-                fn(i)
-            e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) / steps  # ms per call
+            for _ in range(reps):
+                s.record()
+                for i in range(steps):
+                    fn(i)
+                e.record()
+                torch.cuda.synchronize()
+                times.append(s.elapsed_time(e) / steps)
+        t = np.array(times)
+        return dict(ms=float(np.median(t)), p10=float(np.percentile(t, 10)), p90=float(np.percentile(t, 90)),
+                    replays=reps)  # ms per call
 
 
 def rotation(bytes_per_set):
@@ -113,7 +128,7 @@ def rotation(bytes_per_set):
 
 
 # ---------------------------------------------------------------- workloads
-def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
+def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, with_f16_dense=False):
     dev = torch.device("cuda")
     M, K, N = c["M"], c["K"], c["N"]
     vals, meta = ssg.w24_pack_i8(c["Wp"])
@@ -131,9 +146,21 @@ def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
                                    sets[i % R]["scale"], out=sets[i % R]["C"])
     de = lambda i: ssg.dense_gemm_i8(sets[i % R]["A"], sets[i % R]["Wt"], sets[i % R]["scale"],
                                      out=sets[i % R]["C"])
-    t_sp = timer(sp, steps, warmup)
+    st = timer.stats(sp, steps, warmup)
     t_de = timer(de, steps, warmup)
-    return dict(t_sparse_ms=t_sp, t_dense_ms=t_de, rotate_sets=R, sets=sets)
+    out = dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"], t_dense_ms=t_de,
+               rotate_sets=R, sets=sets)
+    if with_f16_dense:
+        # the same shape through the fp16 dense kernel (int8 values are exact in fp16)
+        for d in sets:
+            d["A16"] = d["A"].to(torch.float16)
+            d["Wt16"] = d["Wt"].to(torch.float16)
+            d["C16"] = torch.empty((M, N), dtype=torch.float16, device=dev)
+        d16 = lambda i: ssg.dense_gemm_f16(sets[i % R]["A16"], sets[i % R]["Wt16"], out=sets[i % R]["C16"])
+        out["t_dense_f16_ms"] = timer(d16, steps, warmup)
+        for d in sets:
+            del d["A16"], d["Wt16"], d["C16"]
+    return out
 
 
 def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
@@ -148,8 +175,9 @@ def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
     sp = lambda i: ssg.w24_gemm_f16(sets[i % R]["A"], sets[i % R]["vals"], sets[i % R]["meta"], out=sets[i % R]["C"])
     de = lambda i: ssg.dense_gemm_f16(sets[i % R]["A"], sets[i % R]["Wt"], out=sets[i % R]["C"])
     tm = lambda i: torch.matmul(sets[i % R]["A"], sets[i % R]["Wt"].T)
-    return dict(t_sparse_ms=timer(sp, steps, warmup), t_dense_ms=timer(de, steps, warmup),
-                t_torch_ms=timer(tm, steps, warmup), rotate_sets=R)
+    st = timer.stats(sp, steps, warmup)
+    return dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
+                t_dense_ms=timer(de, steps, warmup), t_torch_ms=timer(tm, steps, warmup), rotate_sets=R)
 
 
 def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
@@ -167,19 +195,24 @@ def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
     tr = lambda i: ssg.ssg_transpose_f16(sets[i % R]["A"], out=sets[i % R]["At"])
     de = lambda i: ssg.dense_gemm_f16(sets[i % R]["A"], sets[i % R]["Wt"], out=sets[i % R]["C"])
     nnz = int((np.diff(host.k_ptr) * np.diff(host.n_ptr)).sum())
-    return dict(t_sparse_ms=timer(sp, steps, warmup), t_transpose_ms=timer(tr, steps, warmup),
+    st = timer.stats(sp, steps, warmup)
+    return dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
+                t_transpose_ms=timer(tr, steps, warmup),
                 t_dense_ms=timer(de, steps, warmup), rotate_sets=R, bytes=bytes_,
                 ops=perf.tw_ops(M, nnz), union_rows=union)
 
 
 # ---------------------------------------------------------------- cpu baseline
-def cpu_baseline(c, perf, budget_s=12.0):
-    """The oracle as it stands, on the host cores, over a bounded number of full repetitions."""
+def cpu_baseline(c, perf, budget_s=12.0, one_core_rows=1024):
+    """The oracle as it stands, on the host cores, over a bounded number of full
+    repetitions; then on one core over the first `one_core_rows` token rows
+    (median of 3), the same GEMM restricted to a slice of A."""
     import oracle
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -189,9 +222,22 @@ def cpu_baseline(c, perf, budget_s=12.0):
         if el >= budget_s or reps >= 200:
             break
     nz, _ = perf.w24_ops(c["M"], c["N"], c["K"])
-    return {"value": nz * reps / el / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"full {c['M']}x{c['K']}x{c['N']} int8 GEMM + epilogue (numpy float64 BLAS), "
-                      f"{reps} repetition(s), {el:.1f} s; host {platform.processor() or platform.machine()}"}
+    out = {"value": nz * reps / el / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+           "sample": f"full {c['M']}x{c['K']}x{c['N']} int8 GEMM + epilogue (numpy float64 BLAS), "
+                     f"{reps} repetition(s), {el:.1f} s; host {platform.processor() or platform.machine()}"}
+    if threadpool_limits is not None:
+        rows = min(one_core_rows, c["M"])
+        A = np.ascontiguousarray(c["A"][:rows])
+        ts = []
+        with threadpool_limits(limits=1):
+            for _ in range(3):
+                t1 = time.perf_counter()
+                oracle.ref_gemm_i8(A, c["Wp"], c["scale"])
+                ts.append(time.perf_counter() - t1)
+        nz1, _ = perf.w24_ops(rows, c["N"], c["K"])
+        out["one_core"] = {"value": nz1 / float(np.median(ts)) / 1e12, "unit": "TOPS", "cores": 1,
+                           "sample": f"first {rows} token rows of the same GEMM, median of 3"}
+    return out
 
 
 # ---------------------------------------------------------------- main
@@ -201,6 +247,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true", help="table mode: every workload and kernel")
+    ap.add_argument("--workloads", default="",
+                    help="table mode: comma list from " + ",".join(WORKLOADS) + " (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--warm", action="store_true", help="one input set (cache-resident) instead of rotating")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a replayed HIP graph")
@@ -354,44 +402,131 @@ def summarize_profile(a):
     return 0
 
 
+def cfg5_stack(torch, ssg, perf, wl, dtype, timer, steps_gemm=20, passes=3, layers=24):
+    """The ViT-Large stack: `layers` x (qkv, proj, fc1, fc2), each GEMM with its own
+    2:4 weight and its own A, all resident in HBM.  Two views of "sum of GEMM time":
+    the sum over the GEMMs of each one's own graph-timed time (a GEMM repeated on
+    its own data, so its inputs are cache-warm), and one back-to-back replay of all
+    launches in layer order (the stack's working set is far larger than the
+    Infinity Cache, so this one streams weights and activations from HBM)."""
+    dev = torch.device("cuda")
+    odt = torch.float16 if dtype == "f16" else torch.float32
+    gemms, outs = [], {}
+    t0 = time.perf_counter()
+    for g in wl.cfg5_layers(dtype, layers=layers):
+        vals, meta = (ssg.w24_pack_f16 if dtype == "f16" else ssg.w24_pack_i8)(g["Wp"])
+        d = dict(shape=g["name"].rsplit("_", 1)[1], M=g["M"], K=g["K"], N=g["N"],
+                 A=torch.from_numpy(g["A"]).to(dev), vals=torch.from_numpy(vals).to(dev),
+                 meta=torch.from_numpy(meta.view(np.int32)).to(dev),
+                 Wt=torch.from_numpy(np.ascontiguousarray(g["W"].T)).to(dev),
+                 scale=torch.from_numpy(g["scale"]).to(dev) if dtype == "i8" else None)
+        key = (g["M"], g["N"])
+        if key not in outs:
+            outs[key] = torch.empty(key, dtype=odt, device=dev)
+        d["C"] = outs[key]
+        gemms.append(d)
+        if len(gemms) % 16 == 0:
+            log(f"cfg5 {dtype} stack: {len(gemms)} GEMMs generated and uploaded ({time.perf_counter() - t0:.0f} s)")
+
+    def sparse(d):
+        if dtype == "f16":
+            return ssg.w24_gemm_f16(d["A"], d["vals"], d["meta"], out=d["C"])
+        return ssg.w24_gemm_i8(d["A"], d["vals"], d["meta"], d["scale"], out=d["C"])
+
+    def dense(d):
+        if dtype == "f16":
+            return ssg.dense_gemm_f16(d["A"], d["Wt"], out=d["C"])
+        return ssg.dense_gemm_i8(d["A"], d["Wt"], d["scale"], out=d["C"])
+
+    n = len(gemms)
+    b2b_sp = timer.stats(lambda i: sparse(gemms[i % n]), n * passes, n)
+    b2b_de = timer.stats(lambda i: dense(gemms[i % n]), n * passes, n)
+    by_shape = {}
+    for j, d in enumerate(gemms):
+        ts = timer(lambda i, d=d: sparse(d), steps_gemm, 3)
+        td = timer(lambda i, d=d: dense(d), steps_gemm, 3)
+        e = by_shape.setdefault(d["shape"], dict(sparse_ms=0.0, dense_ms=0.0, count=0))
+        e["sparse_ms"] += ts
+        e["dense_ms"] += td
+        e["count"] += 1
+        if (j + 1) % 32 == 0:
+            log(f"cfg5 {dtype} stack: {j + 1} GEMMs timed one by one")
+    flops = sum(2.0 * d["M"] * d["N"] * d["K"] for d in gemms)
+    t_b2b, t_b2b_de = b2b_sp["ms"] * n, b2b_de["ms"] * n
+    t_sum = sum(e["sparse_ms"] for e in by_shape.values())
+    t_sum_de = sum(e["dense_ms"] for e in by_shape.values())
+    unit = "tflops" if dtype == "f16" else "tops"
+    del gemms, outs
+    torch.cuda.empty_cache()
+    return dict(workload=f"cfg5_vit_large_stack_w24_{dtype}", gemms=n, layers=layers,
+                t_back_to_back_ms=t_b2b, t_back_to_back_p10_ms=b2b_sp["p10"] * n,
+                t_back_to_back_p90_ms=b2b_sp["p90"] * n, t_dense_back_to_back_ms=t_b2b_de,
+                speedup_vs_dense_back_to_back=t_b2b_de / t_b2b,
+                t_sum_per_gemm_ms=t_sum, t_dense_sum_per_gemm_ms=t_sum_de, speedup_vs_dense_sum=t_sum_de / t_sum,
+                **{f"{unit}_dense_eq_back_to_back": flops / t_b2b / 1e9,
+                   f"{unit}_nonzero_back_to_back": flops / 2 / t_b2b / 1e9},
+                by_shape=by_shape)
+
+
+WORKLOADS = ("cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg5stack")
+
+
 def table(a, torch, ssg, perf, wl, timer):
     rotate = not a.warm
     steps, warmup = a.steps, a.warmup
+    want = set(a.workloads.split(",")) if a.workloads else set(WORKLOADS)
+    timer.reps = 5
 
     def emit(d):
         print(json.dumps(d), flush=True)
 
-    c = wl.make_cfg1()
-    r = w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate)
-    nz, de = perf.w24_ops(c["M"], c["N"], c["K"])
-    emit(dict(workload="cfg1_w24_f16", shape=[c["M"], c["K"], c["N"]], **r,
-              tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
-              speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
-    c = wl.make_cfg2()
-    r = w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate)
-    r.pop("sets")
-    nz, de = perf.w24_ops(c["M"], c["N"], c["K"])
-    b = perf.w24_bytes(c["M"], c["N"], c["K"], 1, 1, 4, True)
-    emit(dict(workload="cfg2_w24_i8", shape=[c["M"], c["K"], c["N"]], **r,
-              tops_nonzero=nz / r["t_sparse_ms"] / 1e9, tops_dense_eq=de / r["t_sparse_ms"] / 1e9,
-              gbs=b / r["t_sparse_ms"] / 1e6, speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
-    torch.cuda.empty_cache()
-    c3 = wl.make_cfg3()
-    c4 = wl.make_cfg4()
-    for c in (c3, c4["fc1"], c4["fc2"]):
+    if "cfg1" in want:
+        c = wl.make_cfg1()
+        r = w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate)
+        nz, de = perf.w24_ops(c["M"], c["N"], c["K"])
+        emit(dict(workload="cfg1_w24_f16", shape=[c["M"], c["K"], c["N"]], **r,
+                  tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
+                  speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
+    if "cfg2" in want:
+        c = wl.make_cfg2()
+        r = w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate, with_f16_dense=True)
+        r.pop("sets")
+        nz, de = perf.w24_ops(c["M"], c["N"], c["K"])
+        b = perf.w24_bytes(c["M"], c["N"], c["K"], 1, 1, 4, True)
+        emit(dict(workload="cfg2_w24_i8", shape=[c["M"], c["K"], c["N"]], **r,
+                  tops_nonzero=nz / r["t_sparse_ms"] / 1e9, tops_dense_eq=de / r["t_sparse_ms"] / 1e9,
+                  gbs=b / r["t_sparse_ms"] / 1e6, speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
+                  speedup_vs_dense_f16=r["t_dense_f16_ms"] / r["t_sparse_ms"]))
+        torch.cuda.empty_cache()
+    tw_cases = []
+    if "cfg3" in want:
+        tw_cases.append(wl.make_cfg3())
+    if "cfg4" in want:
+        c4 = wl.make_cfg4()
+        tw_cases += [c4["fc1"], c4["fc2"]]
+    for c in tw_cases:
         r = tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate)
         emit(dict(workload=c["name"] + "_tw_f16", shape=[c["M"], c["K"], c["N"]], **r,
                   tflops_nonzero=r["ops"] / r["t_sparse_ms"] / 1e9, gbs=r["bytes"] / r["t_sparse_ms"] / 1e6,
                   speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
                   speedup_vs_dense_incl_transpose=r["t_dense_ms"] / (r["t_sparse_ms"] + r["t_transpose_ms"])))
         torch.cuda.empty_cache()
-    for g in wl.cfg5_layers("f16", layers=1):
-        r = w24_f16_case(torch, ssg, perf, g, steps, warmup, timer, rotate)
-        nz, de = perf.w24_ops(g["M"], g["N"], g["K"])
-        emit(dict(workload=g["name"] + "_w24_f16", shape=[g["M"], g["K"], g["N"]], **r,
-                  tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
-                  speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
-        torch.cuda.empty_cache()
+    if "cfg5" in want:
+        for g in wl.cfg5_layers("f16", layers=1):
+            r = w24_f16_case(torch, ssg, perf, g, steps, warmup, timer, rotate)
+            nz, de = perf.w24_ops(g["M"], g["N"], g["K"])
+            emit(dict(workload=g["name"] + "_w24_f16", shape=[g["M"], g["K"], g["N"]], **r,
+                      tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
+                      speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
+            torch.cuda.empty_cache()
+    if "cfg5stack" in want:
+        f16 = cfg5_stack(torch, ssg, perf, wl, "f16", timer)
+        emit(f16)
+        i8 = cfg5_stack(torch, ssg, perf, wl, "i8", timer)
+        # int8 against the fp16 dense stack of the same shapes as well
+        i8["t_dense_f16_back_to_back_ms"] = f16["t_dense_back_to_back_ms"]
+        i8["speedup_vs_dense_f16_back_to_back"] = f16["t_dense_back_to_back_ms"] / i8["t_back_to_back_ms"]
+        emit(i8)
     return 0
 
 
