@@ -163,6 +163,28 @@ def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, with_f16
     return out
 
 
+def w24_i8_out_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate=True):
+    """2:4 and dense int8 GEMMs with the lower-traffic epilogue (fp16 or int8 output)."""
+    dev = torch.device("cuda")
+    M, K, N = c["M"], c["K"], c["N"]
+    ob = {"f16": 2, "i8": 1}[out_type]
+    odt = {"f16": torch.float16, "i8": torch.int8}[out_type]
+    vals, meta = ssg.w24_pack_i8(c["Wp"])
+    R = rotation(perf.w24_bytes(M, N, K, 1, 1, ob, scale=True)) if rotate else 1
+    A0 = torch.from_numpy(c["A"]).to(dev)
+    sets = [dict(A=A0.clone() if r else A0, vals=torch.from_numpy(vals).to(dev),
+                 meta=torch.from_numpy(meta.view(np.int32)).to(dev), scale=torch.from_numpy(c["scale"]).to(dev),
+                 C=torch.empty((M, N), dtype=odt, device=dev),
+                 Wt=torch.from_numpy(np.ascontiguousarray(c["W"].T)).to(dev)) for r in range(R)]
+    sp = lambda i: ssg.w24_gemm_i8_out(sets[i % R]["A"], sets[i % R]["vals"], sets[i % R]["meta"],
+                                       sets[i % R]["scale"], out_type=out_type, out=sets[i % R]["C"])
+    de = lambda i: ssg.dense_gemm_i8_out(sets[i % R]["A"], sets[i % R]["Wt"], sets[i % R]["scale"],
+                                         out_type=out_type, out=sets[i % R]["C"])
+    st = timer.stats(sp, steps, warmup)
+    return dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
+                t_dense_ms=timer(de, steps, warmup), rotate_sets=R, out_bytes=ob)
+
+
 def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
     dev = torch.device("cuda")
     M, K, N = c["M"], c["K"], c["N"]
@@ -498,6 +520,13 @@ def table(a, torch, ssg, perf, wl, timer):
                   gbs=b / r["t_sparse_ms"] / 1e6, speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
                   speedup_vs_dense_f16=r["t_dense_f16_ms"] / r["t_sparse_ms"]))
         torch.cuda.empty_cache()
+        for out_type in ("f16", "i8"):
+            r = w24_i8_out_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate)
+            b = perf.w24_bytes(c["M"], c["N"], c["K"], 1, 1, r["out_bytes"], True)
+            emit(dict(workload=f"cfg2_w24_i8_{out_type}_out", shape=[c["M"], c["K"], c["N"]], **r,
+                      tops_nonzero=nz / r["t_sparse_ms"] / 1e9, tops_dense_eq=de / r["t_sparse_ms"] / 1e9,
+                      gbs=b / r["t_sparse_ms"] / 1e6, speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
+            torch.cuda.empty_cache()
     tw_cases = []
     if "cfg3" in want:
         tw_cases.append(wl.make_cfg3())

@@ -165,6 +165,36 @@ int w24_gemm_f16(const void *A, const void *vals, const uint32_t *meta, void *C,
 int w24_gemm_i8(const int8_t *A, const int8_t *vals, const uint32_t *meta, const float *scale,
                 void *C, int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Output kinds of the int8 GEMMs' selectable epilogue. */
+enum {
+    SSG_OUT_I32 = 0, /* raw int32 accumulators; scale and bias must be NULL      */
+    SSG_OUT_F32 = 1, /* fp32 y                                                    */
+    SSG_OUT_F16 = 2, /* fp16 y, rounded to nearest even (overflow gives +-inf)   */
+    SSG_OUT_I8 = 3   /* int8: y rounded to nearest even, saturated to [-128,127] */
+};
+
+/* int8 GEMMs (dense baseline and 2:4) with a lower-traffic epilogue.  The
+ * integer path of GPUSQ-ViT ("Boost Vision Transformer with GPU-Friendly
+ * Sparsity and Quantization", abstract) deploys the 2:4 model with integer
+ * kernels; an output of 2 or 1 bytes per element, which the next quantised
+ * layer consumes, moves a half or a quarter of the fp32 output's bytes.
+ *
+ *   y[m][n] = float(acc[m][n]) * scale[n]  (+ bias[n] when bias != NULL)
+ *
+ * computed in fp32, each step rounded to nearest even (the int32 -> fp32
+ * conversion, the product, the sum; no fused multiply-add), then stored as
+ * out_type says.  scale: fp32 [N], required except for SSG_OUT_I32; bias:
+ * fp32 [N] or NULL (must be NULL for SSG_OUT_I32); both 16-byte aligned.
+ * C: [M][N] elements of the out_type.  Shape rules as dense_gemm_i8 /
+ * w24_gemm_i8; an unknown out_type is SSG_EINVAL.  dense_gemm_i8 and
+ * w24_gemm_i8 are these calls with bias = NULL and out_type SSG_OUT_F32
+ * (scale given) or SSG_OUT_I32 (scale NULL). */
+int dense_gemm_i8_out(const int8_t *A, const int8_t *Wt, const float *scale, const float *bias,
+                      void *C, int32_t out_type, int64_t M, int64_t N, int64_t K, void *stream);
+int w24_gemm_i8_out(const int8_t *A, const int8_t *vals, const uint32_t *meta, const float *scale,
+                    const float *bias, void *C, int32_t out_type, int64_t M, int64_t N, int64_t K,
+                    void *stream);
+
 /* Tile-wise GEMM, fp16 in, fp32 accumulate, fp16 out.  At is A stored
  * K-major ([K][M], M contiguous) so that the rows picked by offset_k are
  * contiguous reads (the tile-wise slides transpose A to avoid uncoalesced

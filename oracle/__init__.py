@@ -9,7 +9,8 @@ code.  It depends on numpy alone.
 What it computes (each function cites the passage it follows):
 
 * ``gemm``      -- the masked dense product C = A . W_p on the densified pruned
-  weights, in float64 (exact for int8 data), plus the int8 epilogue and the
+  weights, in float64 (exact for int8 data), plus the int8 epilogues (fp32,
+  fp16 or saturated int8 output of float32(acc) * scale (+ bias)) and the
   fp16 output rounding; the tile-wise indexed GEMM written with the slide's
   offset arrays.
 * ``pack``      -- the 2:4 compressed format (kept values + 2-bit positions)
@@ -26,6 +27,9 @@ from .gemm import (  # noqa: F401
     ref_gemm_f64,
     ref_gemm_f16,
     ref_gemm_i8,
+    ref_acc_i8,
+    ref_i8_epilogue,
+    ref_gemm_i8_out,
     ref_abs_gemm,
     ref_tw_gemm_indexed,
     ref_transpose,

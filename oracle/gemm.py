@@ -60,6 +60,14 @@ def ref_gemm_i8(A, Wp, scale=None):
     round-to-nearest-even, then one float32 multiply with round-to-nearest-even
     (no fused multiply-add, no bias, no clamp).
     """
+    acc = ref_acc_i8(A, Wp)
+    if scale is None:
+        return acc
+    return ref_i8_epilogue(acc, scale, None, "f32")
+
+
+def ref_acc_i8(A, Wp):
+    """Exact int32 accumulator of the int8 GEMM, sum_k A[m, k] * W_p[k, n]."""
     A = np.asarray(A)
     Wp = np.asarray(Wp)
     if A.dtype != np.int8 or Wp.dtype != np.int8:
@@ -70,10 +78,47 @@ def ref_gemm_i8(A, Wp, scale=None):
         raise AssertionError("float64 integer sum was not exact")
     if acc_i.size and (acc_i.max() > 2**31 - 1 or acc_i.min() < -(2**31)):
         raise OverflowError("accumulator exceeds int32")
+    return acc_i.astype(np.int32)
+
+
+def ref_i8_epilogue(acc, scale, bias=None, out="f32"):
+    """Epilogue of the integer path on the exact accumulator (the deployment
+    outputs of the GPUSQ-ViT abstract's integer model: fp32, fp16 for the next
+    fp16 layer, or requantised int8 for the next int8 layer).
+
+        y[m, n] = float32(acc[m, n]) * scale[n]  (+ bias[n])
+
+    each operation in float32 with round-to-nearest-even (conversion, product,
+    sum; no fused multiply-add).  out: "f32" -> y; "f16" -> y rounded to the
+    nearest fp16, ties to even, overflow to +-inf; "i8" -> y rounded to the
+    nearest integer, ties to even, then saturated to [-128, 127]; "i32" -> the
+    accumulator itself (no scale, no bias).
+    """
+    acc = np.asarray(acc)
+    if acc.dtype != np.int32:
+        raise TypeError("int32 accumulator expected")
+    if out == "i32":
+        if scale is not None or bias is not None:
+            raise ValueError("the raw accumulator output takes no scale or bias")
+        return acc.copy()
     if scale is None:
-        return acc_i.astype(np.int32)
-    s = np.asarray(scale, dtype=np.float32)
-    return acc_i.astype(np.float32) * s[None, :]
+        raise ValueError("scale is required")
+    y = acc.astype(np.float32) * np.asarray(scale, dtype=np.float32)[None, :]
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float32)[None, :]
+    if out == "f32":
+        return y
+    if out == "f16":
+        with np.errstate(over="ignore"):
+            return y.astype(np.float16)
+    if out == "i8":
+        return np.clip(np.rint(y), -128, 127).astype(np.int8)
+    raise ValueError(f"unknown output kind {out!r}")
+
+
+def ref_gemm_i8_out(A, Wp, scale, bias=None, out="f16"):
+    """int8 GEMM with the selectable epilogue: ref_i8_epilogue(ref_acc_i8(A, W_p), ...)."""
+    return ref_i8_epilogue(ref_acc_i8(A, Wp), scale, bias, out)
 
 
 def ref_tw_gemm_indexed(A, packed, N, G):

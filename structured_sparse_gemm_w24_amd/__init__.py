@@ -28,8 +28,14 @@ from ._lib import (  # noqa: F401
     tw_unpack_f16,
     dense_gemm_f16,
     dense_gemm_i8,
+    dense_gemm_i8_out,
     w24_gemm_f16,
     w24_gemm_i8,
+    w24_gemm_i8_out,
+    SSG_OUT_I32,
+    SSG_OUT_F32,
+    SSG_OUT_F16,
+    SSG_OUT_I8,
     tw_gemm_f16,
     ssg_transpose_f16,
     ssg_device_arch,

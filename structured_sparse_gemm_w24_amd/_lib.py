@@ -53,6 +53,8 @@ SIGNATURES = {
     "dense_gemm_i8": [_P, _P, _P, _P, _I64, _I64, _I64, _P],
     "w24_gemm_f16": [_P, _P, _P, _P, _I64, _I64, _I64, _P],
     "w24_gemm_i8": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P],
+    "dense_gemm_i8_out": [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P],
+    "w24_gemm_i8_out": [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P],
     "tw_gemm_f16": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _I64, _I64, _I64, _P],
     "ssg_transpose_f16": [_P, _P, _I64, _I64, _P],
     "ssg_device_arch": [ct.c_char_p, _I64],
@@ -270,6 +272,58 @@ def dense_gemm_i8(A, Wt, scale=None, out=None):
         _dev(scale, torch.float32, (N,), "scale")
     C = _out(out, (M, N), torch.int32 if scale is None else torch.float32, A)
     _check(load().dense_gemm_i8(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(C), M, N, K, _stream(A)))
+    return C
+
+
+# Output kinds of the int8 GEMMs' selectable epilogue (SSG_OUT_* in ssg.h).
+SSG_OUT_I32, SSG_OUT_F32, SSG_OUT_F16, SSG_OUT_I8 = 0, 1, 2, 3
+_OUT_KINDS = {"i32": SSG_OUT_I32, "f32": SSG_OUT_F32, "f16": SSG_OUT_F16, "i8": SSG_OUT_I8}
+
+
+def _out_kind(out_type):
+    torch = _torch()
+    if out_type not in _OUT_KINDS:
+        raise ValueError(f"out_type must be one of {sorted(_OUT_KINDS)}, got {out_type!r}")
+    dt = {"i32": torch.int32, "f32": torch.float32, "f16": torch.float16, "i8": torch.int8}[out_type]
+    return _OUT_KINDS[out_type], dt
+
+
+def _epilogue_args(N, scale, bias):
+    torch = _torch()
+    if scale is not None:
+        _dev(scale, torch.float32, (N,), "scale")
+    if bias is not None:
+        _dev(bias, torch.float32, (N,), "bias")
+
+
+def dense_gemm_i8_out(A, Wt, scale, bias=None, out_type="f16", out=None):
+    """int8 dense GEMM with the selectable epilogue: y = float(acc) * scale[n] (+ bias[n]),
+    stored as out_type ("f32", "f16", "i8"; "i32" = raw accumulators, no scale or bias)."""
+    torch = _torch()
+    M, K = A.shape
+    N = Wt.shape[0]
+    _dev(A, torch.int8, (M, K), "A")
+    _dev(Wt, torch.int8, (N, K), "Wt")
+    code, dt = _out_kind(out_type)
+    _epilogue_args(N, scale, bias)
+    C = _out(out, (M, N), dt, A)
+    _check(load().dense_gemm_i8_out(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(bias), _ptr(C), code, M, N, K, _stream(A)))
+    return C
+
+
+def w24_gemm_i8_out(A, vals, meta, scale, bias=None, out_type="f16", out=None):
+    """2:4 int8 GEMM with the selectable epilogue (see dense_gemm_i8_out)."""
+    torch = _torch()
+    M, K = A.shape
+    N = vals.shape[0]
+    _dev(A, torch.int8, (M, K), "A")
+    _dev(vals, torch.int8, (N, K // 2), "vals")
+    _dev(meta, torch.int32, (N, -(-K // 32)), "meta")
+    code, dt = _out_kind(out_type)
+    _epilogue_args(N, scale, bias)
+    C = _out(out, (M, N), dt, A)
+    _check(load().w24_gemm_i8_out(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), _ptr(bias), _ptr(C), code,
+                                  M, N, K, _stream(A)))
     return C
 
 

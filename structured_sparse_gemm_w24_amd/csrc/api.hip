@@ -89,14 +89,49 @@ SSG_API int dense_gemm_f16(const void *A, const void *Wt, void *C, int64_t M, in
     return launched(ssg::launch_dense_f16(A, Wt, C, int(M), int(N), int(K), hipStream_t(stream)), "dense_gemm_f16");
 }
 
+namespace {
+
+// Checks shared by the int8 GEMMs' epilogue arguments.
+int check_i8_epilogue(const char *fn, const float *scale, const float *bias, int out) {
+    if (out < ssg::OUT_I32 || out > ssg::OUT_I8) return ssg::fail(SSG_EINVAL, "%s: unknown out_type %d", fn, out);
+    if (out == ssg::OUT_I32 && (scale || bias))
+        return ssg::fail(SSG_EINVAL, "%s: SSG_OUT_I32 takes no scale or bias", fn);
+    if (out != ssg::OUT_I32 && !scale) return ssg::fail(SSG_EINVAL, "%s: this out_type needs scale", fn);
+    if ((scale && !ssg::aligned16(scale)) || (bias && !ssg::aligned16(bias)))
+        return ssg::fail(SSG_EINVAL, "%s: scale and bias must be 16-byte aligned", fn);
+    return SSG_OK;
+}
+
+int dense_i8(const char *fn, const int8_t *A, const int8_t *Wt, const float *scale, const float *bias, void *C,
+             int out, int64_t M, int64_t N, int64_t K, void *stream) {
+    int rc = check_gemm(fn, A, Wt, C, M, N, K, 128, 64);
+    if (rc || M == 0) return rc ? rc : (ssg::clear_error(), SSG_OK);
+    if ((rc = check_i8_epilogue(fn, scale, bias, out))) return rc;
+    if ((rc = check_device())) return rc;
+    return launched(ssg::launch_dense_i8(A, Wt, scale, bias, C, out, int(M), int(N), int(K), hipStream_t(stream)), fn);
+}
+
+int w24_i8(const char *fn, const int8_t *A, const int8_t *vals, const uint32_t *meta, const float *scale,
+           const float *bias, void *C, int out, int64_t M, int64_t N, int64_t K, void *stream) {
+    int rc = check_gemm(fn, A, vals, C, M, N, K, 128, 64);
+    if (rc || M == 0) return rc ? rc : (ssg::clear_error(), SSG_OK);
+    if (!meta || !ssg::aligned16(meta)) return ssg::fail(SSG_EINVAL, "%s: meta null or misaligned", fn);
+    if ((rc = check_i8_epilogue(fn, scale, bias, out))) return rc;
+    if ((rc = check_device())) return rc;
+    return launched(ssg::launch_w24_i8(A, vals, meta, scale, bias, C, out, int(M), int(N), int(K), hipStream_t(stream)),
+                    fn);
+}
+
+}  // namespace
+
 SSG_API int dense_gemm_i8(const int8_t *A, const int8_t *Wt, const float *scale, void *C, int64_t M, int64_t N,
                           int64_t K, void *stream) {
-    int rc = check_gemm("dense_gemm_i8", A, Wt, C, M, N, K, 128, 64);
-    if (rc || M == 0) return rc ? rc : (ssg::clear_error(), SSG_OK);
-    if (scale && !ssg::aligned16(scale)) return ssg::fail(SSG_EINVAL, "dense_gemm_i8: scale must be 16-byte aligned");
-    if ((rc = check_device())) return rc;
-    return launched(ssg::launch_dense_i8(A, Wt, scale, C, int(M), int(N), int(K), hipStream_t(stream)),
-                    "dense_gemm_i8");
+    return dense_i8("dense_gemm_i8", A, Wt, scale, nullptr, C, scale ? ssg::OUT_F32 : ssg::OUT_I32, M, N, K, stream);
+}
+
+SSG_API int dense_gemm_i8_out(const int8_t *A, const int8_t *Wt, const float *scale, const float *bias, void *C,
+                              int32_t out_type, int64_t M, int64_t N, int64_t K, void *stream) {
+    return dense_i8("dense_gemm_i8_out", A, Wt, scale, bias, C, out_type, M, N, K, stream);
 }
 
 SSG_API int w24_gemm_f16(const void *A, const void *vals, const uint32_t *meta, void *C, int64_t M, int64_t N,
@@ -111,13 +146,14 @@ SSG_API int w24_gemm_f16(const void *A, const void *vals, const uint32_t *meta, 
 
 SSG_API int w24_gemm_i8(const int8_t *A, const int8_t *vals, const uint32_t *meta, const float *scale, void *C,
                         int64_t M, int64_t N, int64_t K, void *stream) {
-    int rc = check_gemm("w24_gemm_i8", A, vals, C, M, N, K, 128, 64);
-    if (rc || M == 0) return rc ? rc : (ssg::clear_error(), SSG_OK);
-    if (!meta || !ssg::aligned16(meta)) return ssg::fail(SSG_EINVAL, "w24_gemm_i8: meta null or misaligned");
-    if (scale && !ssg::aligned16(scale)) return ssg::fail(SSG_EINVAL, "w24_gemm_i8: scale must be 16-byte aligned");
-    if ((rc = check_device())) return rc;
-    return launched(ssg::launch_w24_i8(A, vals, meta, scale, C, int(M), int(N), int(K), hipStream_t(stream)),
-                    "w24_gemm_i8");
+    return w24_i8("w24_gemm_i8", A, vals, meta, scale, nullptr, C, scale ? ssg::OUT_F32 : ssg::OUT_I32, M, N, K,
+                  stream);
+}
+
+SSG_API int w24_gemm_i8_out(const int8_t *A, const int8_t *vals, const uint32_t *meta, const float *scale,
+                            const float *bias, void *C, int32_t out_type, int64_t M, int64_t N, int64_t K,
+                            void *stream) {
+    return w24_i8("w24_gemm_i8_out", A, vals, meta, scale, bias, C, out_type, M, N, K, stream);
 }
 
 SSG_API int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,

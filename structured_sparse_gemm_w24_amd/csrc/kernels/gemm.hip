@@ -37,8 +37,10 @@
 //     columns in that XCD's L2;
 //   * epilogue: the accumulators go through LDS as row-major [token][channel]
 //     slabs, so C is written as whole contiguous row segments, 16 bytes per
-//     lane (fp16 rounded to nearest even; int8 path: int32 or
-//     float(acc) * scale[n]).
+//     lane (fp16 kinds: fp16 rounded to nearest even; int8 kinds: raw int32,
+//     or y = float(acc) * scale[n] (+ bias[n]) written as fp32, as fp16
+//     rounded to nearest even, or as int8 rounded to nearest even and
+//     saturated to [-128, 127]).
 //
 // Instruction operand layouts (64-lane wave, h = lane / 32, r = lane % 32):
 //   dense f16 32x32x16 : row-op lane holds k = 8h .. 8h+7 of its row r
@@ -63,7 +65,10 @@
 namespace ssg {
 
 enum Kind { DENSE_F16 = 0, W24_F16 = 1, DENSE_I8 = 2, W24_I8 = 3 };
-enum Epi { EPI_F16 = 0, EPI_I32 = 1, EPI_F32_SCALE = 2 };
+// EPI_F16: fp16 kinds.  int8 kinds: EPI_I32 raw accumulators; the others
+// compute y = float(acc) * scale[n] (+ bias[n]), each step rounded to nearest
+// even, then store y as fp32, fp16 or saturated int8.
+enum Epi { EPI_F16 = 0, EPI_I32 = 1, EPI_F32_SCALE = 2, EPI_F16_SCALE = 3, EPI_I8_SCALE = 4 };
 
 template <int KIND>
 struct KindTraits;
@@ -202,7 +207,8 @@ struct Layout {
 template <int KIND, int EPI, class CF>
 __global__ void __launch_bounds__(CF::WM *CF::WN * 64)
 gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const uint32_t *__restrict__ meta,
-            const float *__restrict__ scale, void *__restrict__ C, int M, int N, int K) {
+            const float *__restrict__ scale, const float *__restrict__ bias, void *__restrict__ C, int M, int N,
+            int K) {
     using KT = KindTraits<KIND>;
     using LY = Layout<KIND, CF>;
     using Acc = typename AccOf<KIND>::T;
@@ -212,7 +218,7 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     constexpr int A_STAGE = LY::A_STAGE, W_STAGE = LY::W_STAGE, STAGE = LY::STAGE;
     constexpr int SA = KT::kI8 ? 1 : 2;  // bytes per element
     // LDS-staged epilogue: each wave owns 32 token rows x TN*32 channels per pass
-    constexpr int OB = (EPI == EPI_F16) ? 2 : 4;  // output bytes per element
+    constexpr int OB = (EPI == EPI_F16 || EPI == EPI_F16_SCALE) ? 2 : (EPI == EPI_I8_SCALE ? 1 : 4);  // output bytes
     constexpr int EROW = TN * 32 * OB + 16;       // padded LDS row (odd multiple of 16 B)
     constexpr int EWAVE = 32 * EROW;
     constexpr int EPASS = (TM * EWAVE * LY::NW <= CF::STAGES * STAGE) ? TM : 1;
@@ -393,25 +399,43 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     // ---- epilogue.  Lane (h, r) holds, for 32x32 block (tn, tm) and q = 0..3,
     // channels n = tn*32 + 8q + 4h .. +3 of token m = tm*32 + r.
     auto convert = [&](const Acc &v, int q, int n) -> u32x4 {
-        u32x4 o;
+        u32x4 o = u32x4{0, 0, 0, 0};
         if constexpr (EPI == EPI_F16) {
             o.x = pack_half2_rne(v[4 * q + 0], v[4 * q + 1]);
             o.y = pack_half2_rne(v[4 * q + 2], v[4 * q + 3]);
-            o.z = 0;
-            o.w = 0;
         } else if constexpr (EPI == EPI_I32) {
             o.x = uint32_t(v[4 * q + 0]);
             o.y = uint32_t(v[4 * q + 1]);
             o.z = uint32_t(v[4 * q + 2]);
             o.w = uint32_t(v[4 * q + 3]);
         } else {
-            const floatx4 sc = *reinterpret_cast<const floatx4 *>(scale + min(n, N - 4));
+            const int nc = min(n, N - 4);
+            const floatx4 sc = *reinterpret_cast<const floatx4 *>(scale + nc);
             floatx4 f;
             f.x = __fmul_rn(float(v[4 * q + 0]), sc.x);
             f.y = __fmul_rn(float(v[4 * q + 1]), sc.y);
             f.z = __fmul_rn(float(v[4 * q + 2]), sc.z);
             f.w = __fmul_rn(float(v[4 * q + 3]), sc.w);
-            o = __builtin_bit_cast(u32x4, f);
+            if (bias) {
+                const floatx4 bi = *reinterpret_cast<const floatx4 *>(bias + nc);
+                f.x = __fadd_rn(f.x, bi.x);
+                f.y = __fadd_rn(f.y, bi.y);
+                f.z = __fadd_rn(f.z, bi.z);
+                f.w = __fadd_rn(f.w, bi.w);
+            }
+            if constexpr (EPI == EPI_F32_SCALE) {
+                o = __builtin_bit_cast(u32x4, f);
+            } else if constexpr (EPI == EPI_F16_SCALE) {
+                o.x = pack_half2_rne(f.x, f.y);
+                o.y = pack_half2_rne(f.z, f.w);
+            } else {
+                // round to nearest even, saturate, pack four int8 into one word
+                auto q8 = [](float y) -> uint32_t {
+                    const float r = fminf(fmaxf(__builtin_rintf(y), -128.0f), 127.0f);
+                    return uint32_t(int32_t(r)) & 0xffu;
+                };
+                o.x = q8(f.x) | (q8(f.y) << 8) | (q8(f.z) << 16) | (q8(f.w) << 24);
+            }
         }
         return o;
     };
@@ -436,7 +460,8 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
                 for (int q = 0; q < 4; ++q) {
                     const int c = tn * 32 + q * 8 + h * 4;
                     const u32x4 o = convert(acc[tn][tp + e], q, nw + c);
-                    if constexpr (OB == 2) *reinterpret_cast<u32x2 *>(slab + c * 2) = u32x2{o.x, o.y};
+                    if constexpr (OB == 1) *reinterpret_cast<uint32_t *>(slab + c) = o.x;
+                    else if constexpr (OB == 2) *reinterpret_cast<u32x2 *>(slab + c * 2) = u32x2{o.x, o.y};
                     else *reinterpret_cast<u32x4 *>(slab + c * 4) = o;
                 }
         }
@@ -457,12 +482,13 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
 }
 
 template <int KIND, int EPI, class CF>
-static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, const float *scale, void *C,
-                         int M, int N, int K, hipStream_t st) {
+static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, const float *scale,
+                         const float *bias, void *C, int M, int N, int K, hipStream_t st) {
     using LY = Layout<KIND, CF>;
     const int nb = ((M + LY::BM - 1) / LY::BM) * ((N + LY::BN - 1) / LY::BN);
     hipLaunchKernelGGL((gemm_kernel<KIND, EPI, CF>), dim3(nb), dim3(LY::NT), 0, st,
-                       static_cast<const uint8_t *>(A), static_cast<const uint8_t *>(Wv), meta, scale, C, M, N, K);
+                       static_cast<const uint8_t *>(A), static_cast<const uint8_t *>(Wv), meta, scale, bias, C, M, N,
+                       K);
     return hipGetLastError();
 }
 
@@ -501,36 +527,55 @@ static Shape pick_i8(int M, int N, int K) {
 
 template <int KIND, int EPI, bool NTS, bool DENSE>
 static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const uint32_t *meta, const float *scale,
-                               void *C, int M, int N, int K, hipStream_t st) {
+                               const float *bias, void *C, int M, int N, int K, hipStream_t st) {
     if (sh == SHAPE_BIG) {
-        if constexpr (DENSE) return launch<KIND, EPI, CfgBigDense<NTS>>(A, Wv, meta, scale, C, M, N, K, st);
-        else return launch<KIND, EPI, CfgBig<NTS>>(A, Wv, meta, scale, C, M, N, K, st);
+        if constexpr (DENSE) return launch<KIND, EPI, CfgBigDense<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
+        else return launch<KIND, EPI, CfgBig<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
     }
-    if (sh == SHAPE_MID) return launch<KIND, EPI, CfgMid<NTS>>(A, Wv, meta, scale, C, M, N, K, st);
-    return launch<KIND, EPI, CfgSmall<NTS>>(A, Wv, meta, scale, C, M, N, K, st);
+    if (sh == SHAPE_MID) return launch<KIND, EPI, CfgMid<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
+    return launch<KIND, EPI, CfgSmall<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
 }
 
 hipError_t launch_dense_f16(const void *A, const void *Wt, void *C, int M, int N, int K, hipStream_t st) {
-    return launch_shape<DENSE_F16, EPI_F16, false, true>(pick_f16(M, N), A, Wt, nullptr, nullptr, C, M, N, K, st);
+    return launch_shape<DENSE_F16, EPI_F16, false, true>(pick_f16(M, N), A, Wt, nullptr, nullptr, nullptr, C, M, N, K,
+                                                          st);
 }
 
 hipError_t launch_w24_f16(const void *A, const void *vals, const uint32_t *meta, void *C, int M, int N, int K,
                           hipStream_t st) {
-    return launch_shape<W24_F16, EPI_F16, false, false>(pick_f16(M, N), A, vals, meta, nullptr, C, M, N, K, st);
+    return launch_shape<W24_F16, EPI_F16, false, false>(pick_f16(M, N), A, vals, meta, nullptr, nullptr, C, M, N, K,
+                                                         st);
 }
 
-hipError_t launch_dense_i8(const void *A, const void *Wt, const float *scale, void *C, int M, int N, int K,
-                           hipStream_t st) {
+// int8 kinds: out selects the epilogue (OUT_I32 raw accumulators; OUT_F32,
+// OUT_F16 and OUT_I8 apply scale and the optional bias).  Every output kind
+// keeps the int8 tile choice: with short K the main loop's operand traffic,
+// not the output stream, sets most of the time (measured on the ViT-Base
+// fc1 shape: fp32 / fp16 / int8 outputs 46.5 / 43.2 / 41.6 us).
+template <int KIND, bool DENSE>
+static hipError_t launch_i8(const void *A, const void *Wv, const uint32_t *meta, const float *scale,
+                            const float *bias, void *C, int out, int M, int N, int K, hipStream_t st) {
     const Shape sh = pick_i8(M, N, K);
-    if (scale) return launch_shape<DENSE_I8, EPI_F32_SCALE, true, true>(sh, A, Wt, nullptr, scale, C, M, N, K, st);
-    return launch_shape<DENSE_I8, EPI_I32, true, true>(sh, A, Wt, nullptr, nullptr, C, M, N, K, st);
+    switch (out) {
+        case OUT_I32:
+            return launch_shape<KIND, EPI_I32, true, DENSE>(sh, A, Wv, meta, nullptr, nullptr, C, M, N, K, st);
+        case OUT_F32:
+            return launch_shape<KIND, EPI_F32_SCALE, true, DENSE>(sh, A, Wv, meta, scale, bias, C, M, N, K, st);
+        case OUT_F16:
+            return launch_shape<KIND, EPI_F16_SCALE, true, DENSE>(sh, A, Wv, meta, scale, bias, C, M, N, K, st);
+        default:
+            return launch_shape<KIND, EPI_I8_SCALE, true, DENSE>(sh, A, Wv, meta, scale, bias, C, M, N, K, st);
+    }
 }
 
-hipError_t launch_w24_i8(const void *A, const void *vals, const uint32_t *meta, const float *scale, void *C,
-                         int M, int N, int K, hipStream_t st) {
-    const Shape sh = pick_i8(M, N, K);
-    if (scale) return launch_shape<W24_I8, EPI_F32_SCALE, true, false>(sh, A, vals, meta, scale, C, M, N, K, st);
-    return launch_shape<W24_I8, EPI_I32, true, false>(sh, A, vals, meta, nullptr, C, M, N, K, st);
+hipError_t launch_dense_i8(const void *A, const void *Wt, const float *scale, const float *bias, void *C, int out,
+                           int M, int N, int K, hipStream_t st) {
+    return launch_i8<DENSE_I8, true>(A, Wt, nullptr, scale, bias, C, out, M, N, K, st);
+}
+
+hipError_t launch_w24_i8(const void *A, const void *vals, const uint32_t *meta, const float *scale, const float *bias,
+                         void *C, int out, int M, int N, int K, hipStream_t st) {
+    return launch_i8<W24_I8, false>(A, vals, meta, scale, bias, C, out, M, N, K, st);
 }
 
 }  // namespace ssg

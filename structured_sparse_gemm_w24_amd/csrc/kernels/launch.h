@@ -7,13 +7,16 @@
 
 namespace ssg {
 
+// int8 GEMM output kinds (the values of the C-ABI's SSG_OUT_* constants)
+enum OutKind { OUT_I32 = 0, OUT_F32 = 1, OUT_F16 = 2, OUT_I8 = 3 };
+
 hipError_t launch_dense_f16(const void *A, const void *Wt, void *C, int M, int N, int K, hipStream_t st);
-hipError_t launch_dense_i8(const void *A, const void *Wt, const float *scale, void *C, int M, int N,
-                           int K, hipStream_t st);
+hipError_t launch_dense_i8(const void *A, const void *Wt, const float *scale, const float *bias, void *C,
+                           int out, int M, int N, int K, hipStream_t st);
 hipError_t launch_w24_f16(const void *A, const void *vals, const uint32_t *meta, void *C, int M, int N,
                           int K, hipStream_t st);
 hipError_t launch_w24_i8(const void *A, const void *vals, const uint32_t *meta, const float *scale,
-                         void *C, int M, int N, int K, hipStream_t st);
+                         const float *bias, void *C, int out, int M, int N, int K, hipStream_t st);
 hipError_t launch_tw_f16(const void *At, const void *vals, const int32_t *offset_k,
                          const int32_t *offset_n, const int32_t *v_ptr, const int32_t *k_ptr,
                          const int32_t *n_ptr, const int32_t *tile_order, int T, int G, void *C,

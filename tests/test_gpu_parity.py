@@ -199,6 +199,80 @@ def test_dense_equals_sparse_on_pruned_weight(lib, gpu):
     assert np.array_equal(Cs.view(np.uint32), Cd.view(np.uint32))
 
 
+# ---------------------------------------------------------------- int8 epilogues
+def _bits(x):
+    return x.view({4: np.uint32, 2: np.uint16, 1: np.uint8}[x.dtype.itemsize])
+
+
+def _i8_out_case(rng, M, K, N, out):
+    case = wl.random_24_i8(rng, M, K, N)
+    # y in each output kind's working range: fp16 up to a few thousand, int8 around +-100
+    scale = {"f32": case["scale"], "f16": case["scale"] * np.float32(20.0),
+             "i8": rng.uniform(2e-4, 2e-3, size=N).astype(np.float32)}[out]
+    bias = rng.normal(0, 4.0, size=N).astype(np.float32)
+    return case, scale, bias
+
+
+I8_OUT_SHAPES = [(1, 128, 64), (130, 768, 192), (257, 256, 320), (1000, 1024, 576)]
+
+
+@pytest.mark.parametrize("out", ["f32", "f16", "i8"])
+@pytest.mark.parametrize("with_bias", [False, True])
+@pytest.mark.parametrize("M,K,N", I8_OUT_SHAPES)
+def test_w24_i8_out_bit_exact(lib, gpu, M, K, N, out, with_bias):
+    rng = np.random.default_rng(M * 7 + K + N)
+    case, scale, bias = _i8_out_case(rng, M, K, N, out)
+    b = bias if with_bias else None
+    vals, meta = lib.w24_pack_i8(case["Wp"])
+    C = H(lib.w24_gemm_i8_out(T(case["A"]), T(vals), meta_t(meta), T(scale), None if b is None else T(b),
+                              out_type=out))
+    ref = oracle.ref_gemm_i8_out(case["A"], case["Wp"], scale, b, out)
+    assert C.dtype == ref.dtype
+    bad = np.flatnonzero(_bits(C) != _bits(ref))
+    assert bad.size == 0, f"{bad.size} mismatches, first at {np.unravel_index(bad[0], C.shape)}"
+
+
+@pytest.mark.parametrize("out", ["i32", "f32", "f16", "i8"])
+def test_dense_i8_out_bit_exact(lib, gpu, out):
+    rng = np.random.default_rng(21)
+    case, scale, bias = _i8_out_case(rng, 200, 512, 320, out if out != "i32" else "f32")
+    s, b = (None, None) if out == "i32" else (scale, bias)
+    C = H(lib.dense_gemm_i8_out(T(case["A"]), T(case["W"].T), None if s is None else T(s),
+                                None if b is None else T(b), out_type=out))
+    ref = oracle.ref_gemm_i8_out(case["A"], case["W"], s, b, out)
+    assert np.array_equal(_bits(C), _bits(ref))
+
+
+def test_i8_out_saturation_and_ties(lib, gpu):
+    # small activations and weights with scale 0.5: odd accumulators are exact
+    # ties (x.5, rounded to even), and two rows of +-127 drive outputs into saturation
+    rng = np.random.default_rng(22)
+    A = rng.integers(-2, 3, size=(64, 256)).astype(np.int8)
+    A[0] = 127
+    A[1] = -127
+    Wp = wl.prune24_magnitude(rng.integers(-1, 2, size=(256, 64)).astype(np.int8))
+    scale = np.full(64, 0.5, np.float32)
+    acc = oracle.ref_acc_i8(A, Wp)
+    assert (acc % 2 != 0).sum() > 500 and (np.abs(acc * 0.5) > 128).sum() > 20
+    vals, meta = lib.w24_pack_i8(Wp)
+    for out in ("i8", "f16"):
+        C = H(lib.w24_gemm_i8_out(T(A), T(vals), meta_t(meta), T(scale), out_type=out))
+        ref = oracle.ref_gemm_i8_out(A, Wp, scale, None, out)
+        assert np.array_equal(_bits(C), _bits(ref)), out
+
+
+@pytest.mark.parametrize("out", ["f16", "i8"])
+def test_w24_i8_out_cfg2(lib, gpu, out):
+    c = wl.make_cfg2()
+    rng = np.random.default_rng(5)
+    scale = (c["scale"] * np.float32(0.02)) if out == "i8" else c["scale"]
+    bias = rng.normal(0, 2.0, size=c["N"]).astype(np.float32)
+    vals, meta = lib.w24_pack_i8(c["Wp"])
+    C = H(lib.w24_gemm_i8_out(T(c["A"]), T(vals), meta_t(meta), T(scale), T(bias), out_type=out))
+    ref = oracle.ref_gemm_i8_out(c["A"], c["Wp"], scale, bias, out)
+    assert np.array_equal(_bits(C), _bits(ref))
+
+
 # ---------------------------------------------------------------- tile-wise
 def run_tw(lib, A, Wp, G, prefill_nan=True):
     import torch

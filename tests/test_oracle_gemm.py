@@ -222,3 +222,144 @@ def _mut_f32_accumulate(A, W):
                                     _mut_f32_accumulate])
 def test_bruteforce_catches_planted_mistakes(mutant):
     assert not check_gemm_bruteforce(mutant)
+
+
+# ---------------------------------------------------------------- int8 epilogues
+def round_to_f16(x: Fraction):
+    """Nearest fp16 to the rational x, ties to even, |x| beyond the largest
+    finite value rounds to +-inf (IEEE binary16 by enumeration of the finite set)."""
+    finite = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)  # +0 .. 65504
+    mags = [Fraction(float(v)) for v in finite]
+    ax = abs(x)
+    # overflow threshold: halfway between 65504 and the next step 65536
+    if ax >= Fraction(65520):
+        r = np.float16(np.inf)
+    else:
+        lo, hi = 0, len(mags) - 1
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if mags[mid] <= ax:
+                lo = mid
+            else:
+                hi = mid
+        cands = [lo] if mags[lo] == ax else [lo, hi]
+        best = min(cands, key=lambda i: (abs(mags[i] - ax), i & 1))
+        r = finite[best]
+    return -r if x < 0 else r
+
+
+def round_to_i8(x: Fraction):
+    """Nearest integer, ties to even, saturated to [-128, 127]."""
+    fl = x.numerator // x.denominator
+    frac = x - fl
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return max(-128, min(127, fl))
+
+
+def expected_epilogue(acc, scale, bias, out):
+    """Exact rationals with one round-to-float32 per step, then the output rounding."""
+    M, N = acc.shape
+    res = []
+    for m in range(M):
+        row = []
+        for n in range(N):
+            a32 = round_to_f32(Fraction(int(acc[m, n])))
+            y = round_to_f32(Fraction(float(a32)) * Fraction(float(scale[n])))
+            if bias is not None:
+                y = round_to_f32(Fraction(float(y)) + Fraction(float(bias[n])))
+            if out == "f32":
+                row.append(y)
+            elif out == "f16":
+                row.append(round_to_f16(Fraction(float(y))))
+            else:
+                row.append(round_to_i8(Fraction(float(y))))
+        res.append(row)
+    return res
+
+
+@pytest.mark.parametrize("out", ["f32", "f16", "i8"])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_i8_epilogue_matches_exact_rationals(out, with_bias):
+    rng = np.random.default_rng(11)
+    case = wl.random_24_i8(rng, 4, 64, 5)
+    acc = oracle.ref_acc_i8(case["A"], case["Wp"])
+    # scales that put y in the interesting range of each output kind
+    scale = {"f32": case["scale"], "f16": case["scale"] * np.float32(40.0),
+             "i8": rng.uniform(1e-4, 3e-3, size=5).astype(np.float32)}[out]
+    bias = rng.normal(0, 3.0, size=5).astype(np.float32) if with_bias else None
+    got = oracle.ref_i8_epilogue(acc, scale, bias, out)
+    want = expected_epilogue(acc, scale, bias, out)
+    assert got.dtype == {"f32": np.float32, "f16": np.float16, "i8": np.int8}[out]
+    for m in range(4):
+        for n in range(5):
+            if out == "i8":
+                assert int(got[m, n]) == want[m][n]
+            else:
+                bits = np.uint32 if out == "f32" else np.uint16
+                assert got[m, n].view(bits) == np.asarray(want[m][n]).view(bits)
+
+
+def test_i8_epilogue_hand_computed_cases():
+    # fp16 spacing is 2 on [2048, 4096): 2049 and 2051 are ties, to the even mantissa
+    acc = np.array([[2049, 2051, -2049, 65519, 65520, 70000]], dtype=np.int32)
+    one = np.ones(6, np.float32)
+    f16 = oracle.ref_i8_epilogue(acc, one, None, "f16")
+    assert f16.tolist() == [[2048.0, 2052.0, -2048.0, 65504.0, np.inf, np.inf]]
+    # int8: ties to even, then saturation (127.5 rounds to 128 and saturates)
+    acc = np.array([[5, 7, -5, 255, 256, -257, 600, -600]], dtype=np.int32)
+    half = np.full(8, 0.5, np.float32)
+    i8 = oracle.ref_i8_epilogue(acc, half, None, "i8")
+    assert i8.tolist() == [[2, 4, -2, 127, 127, -128, 127, -128]]
+    # the bias is added to the rounded product (no fused multiply-add):
+    # 3 * (1 + 2^-23) = 3 + 1.5 * 2^-22 is a tie and rounds to even, 3 + 2^-21;
+    # adding 2^-22 then gives 3 + 3 * 2^-22 exactly.  One fused rounding of
+    # 3 + 2.5 * 2^-22 would give 3 + 2^-21 instead.
+    acc = np.array([[3]], dtype=np.int32)
+    s = np.array([1 + 2.0 ** -23], np.float32)
+    b = np.array([2.0 ** -22], np.float32)
+    y = oracle.ref_i8_epilogue(acc, s, b, "f32")[0, 0]
+    assert Fraction(float(y)) == 3 + 3 * Fraction(1, 2 ** 22)
+    assert Fraction(float(y)) != 3 + Fraction(1, 2 ** 21)
+
+
+def test_i8_raw_output_is_the_accumulator():
+    rng = np.random.default_rng(12)
+    case = wl.random_24_i8(rng, 3, 32, 4)
+    acc = oracle.ref_acc_i8(case["A"], case["Wp"])
+    assert np.array_equal(oracle.ref_gemm_i8_out(case["A"], case["Wp"], None, None, "i32"), acc)
+    with pytest.raises(ValueError):
+        oracle.ref_i8_epilogue(acc, case["scale"], None, "i32")
+
+
+def _mut_fused(acc, scale, bias, out):
+    y = (acc.astype(np.float64) * scale.astype(np.float64)[None, :] + bias.astype(np.float64)[None, :])
+    return y.astype(np.float32)
+
+
+def _mut_trunc_i8(acc, scale, bias, out):
+    y = acc.astype(np.float32) * scale[None, :] + bias[None, :]
+    return np.clip(np.trunc(y), -128, 127).astype(np.int8)
+
+
+def _mut_sym_i8(acc, scale, bias, out):
+    y = acc.astype(np.float32) * scale[None, :] + bias[None, :]
+    return np.clip(np.rint(y), -127, 127).astype(np.int8)
+
+
+@pytest.mark.parametrize("mutant,out", [(_mut_fused, "f32"), (_mut_trunc_i8, "i8"), (_mut_sym_i8, "i8")])
+def test_epilogue_pins_catch_planted_mistakes(mutant, out):
+    rng = np.random.default_rng(13)
+    acc = rng.integers(-40000, 40000, size=(16, 8)).astype(np.int32)
+    acc[0, :] = -400  # drives int8 outputs to the negative limit
+    if out == "f32":
+        scale = rng.uniform(1e-3, 1e-2, 8).astype(np.float32)
+    else:
+        scale = np.full(8, 0.01, np.float32)
+    bias = rng.normal(0, 1.0, 8).astype(np.float32)
+    want = expected_epilogue(acc, scale, bias, out)
+    got = mutant(acc, scale, bias, out)
+    same = all((int(got[m, n]) == want[m][n]) if out == "i8" else
+               (got[m, n].view(np.uint32) == np.asarray(want[m][n]).view(np.uint32))
+               for m in range(16) for n in range(8))
+    assert not same
