@@ -33,18 +33,18 @@ if ROOT not in sys.path:
 METRIC = "effective TFLOPS/TOPS of sparse GEMM + speedup vs dense MFMA GEMM, same shape"
 CACHE_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w24_gemm_i8_vit_base_fc1.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "structured_sparse_gemm_w24_amd", "csrc", "kernels", f)
-                  for f in ("gemm.hip", "common.h")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash():
+def kernel_hash(main="gemm.hip"):
+    """Hash of a kernel source and the shared header (traffic counters are only
+    reused while this matches)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
+    for f in (main, "common.h"):
+        h.update(open(os.path.join(ROOT, "structured_sparse_gemm_w24_amd", "csrc", "kernels", f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -270,7 +270,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true", help="table mode: every workload and kernel")
     ap.add_argument("--workloads", default="",
-                    help="table mode: comma list from " + ",".join(WORKLOADS) + " (default: all)")
+                    help="table mode: comma list from " + ",".join(WORKLOADS) +
+                         " or cfg5:<qkv|proj|fc1|fc2> for one layer-0 GEMM (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--warm", action="store_true", help="one input set (cache-resident) instead of rotating")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a replayed HIP graph")
@@ -279,6 +280,8 @@ def main(argv=None):
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="summarise rocprofv3 CSV output under DIR into --out (no GPU needed)")
     ap.add_argument("--kernel", default="gemm_kernel<3", help="kernel-name substring for --summarize-profile")
+    ap.add_argument("--kernel-source", default="gemm.hip",
+                    help="kernel source file whose hash the --summarize-profile summary records")
     ap.add_argument("--out", help="summary file for --summarize-profile")
     ap.add_argument("--command", default="", help="the profiled command line, recorded in the summary")
     a = ap.parse_args(argv)
@@ -381,7 +384,8 @@ def summarize_profile(a):
     """Writes a short text summary of rocprofv3 CSV output found under DIR:
     DIR/trace (--kernel-trace --stats), DIR/fetch and DIR/write (--pmc FETCH_SIZE,
     --pmc WRITE_SIZE on the same command), DIR/copy_fetch and DIR/copy_write (the
-    same counters on --copy-calibration).  The counters are KiB per dispatch; the
+    same counters on --copy-calibration), optionally DIR/mfma (--pmc
+    SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE).  The counters are KiB per dispatch; the
     copy of COPY_BYTES gives the scale from counted to true bytes."""
     root = a.summarize_profile
     out = []
@@ -408,11 +412,21 @@ def summarize_profile(a):
     cf, ncf = counter("copy_fetch", "FETCH_SIZE", is_copy)
     cw, ncw = counter("copy_write", "WRITE_SIZE", is_copy)
     out.append(f"target '{a.kernel}': FETCH_SIZE {tf} KiB ({ntf} dispatches), WRITE_SIZE {tw} KiB ({ntw})")
+    busy, nb = counter("mfma", "SQ_VALU_MFMA_BUSY_CYCLES", is_target)
+    gui, ng = counter("mfma", "GRBM_GUI_ACTIVE", is_target)
+    if busy is not None and gui:
+        # MFMA busy cycles are summed over every SIMD (a 32x32 sparse or
+        # 32x32x16 dense instruction counts 32 cycles, its issue interval at
+        # peak); GRBM_GUI_ACTIVE is summed over the 8 XCDs, each with 32 CUs x
+        # 4 SIMDs, so the fraction of the matrix-core peak at the running clock
+        # is busy / (GUI_ACTIVE x 128)
+        out.append(f"target '{a.kernel}': SQ_VALU_MFMA_BUSY_CYCLES {busy:.0f}, GRBM_GUI_ACTIVE {gui:.0f} "
+                   f"({nb} dispatches); MFMA busy fraction = busy / (GUI_ACTIVE x 128) = {busy / (gui * 128):.3f}")
     out.append(f"copy of {COPY_BYTES} B: FETCH_SIZE {cf} KiB ({ncf}), WRITE_SIZE {cw} KiB ({ncw})")
     if None not in (cf, cw, tf, tw) and cf > 0 and cw > 0:
         kf, kw = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
         out.append(f"scale (true bytes per counted byte): fetch {kf:.4f} write {kw:.4f}")
-        out.append(f"kernel_sha: {kernel_hash()}")
+        out.append(f"kernel_sha: {kernel_hash(a.kernel_source)}")
         out.append(f"hbm_read_bytes_per_launch: {tf * 1024 * kf:.0f}")
         out.append(f"hbm_write_bytes_per_launch: {tw * 1024 * kw:.0f}")
         out.append(f"hbm_bytes_per_launch: {tf * 1024 * kf + tw * 1024 * kw:.0f}")
@@ -540,8 +554,11 @@ def table(a, torch, ssg, perf, wl, timer):
                   speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
                   speedup_vs_dense_incl_transpose=r["t_dense_ms"] / (r["t_sparse_ms"] + r["t_transpose_ms"])))
         torch.cuda.empty_cache()
-    if "cfg5" in want:
+    only5 = {w.split(":", 1)[1] for w in want if w.startswith("cfg5:")}
+    if "cfg5" in want or only5:
         for g in wl.cfg5_layers("f16", layers=1):
+            if only5 and g["name"].rsplit("_", 1)[1] not in only5:
+                continue
             r = w24_f16_case(torch, ssg, perf, g, steps, warmup, timer, rotate)
             nz, de = perf.w24_ops(g["M"], g["N"], g["K"])
             emit(dict(workload=g["name"] + "_w24_f16", shape=[g["M"], g["K"], g["N"]], **r,
