@@ -207,6 +207,30 @@ int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_k,
                 const int32_t *n_ptr, const int32_t *tile_order, int32_t T, int32_t G,
                 void *C, int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Flags of tw_gemm_f16_ex. */
+enum {
+    SSG_TW_OUT_T = 1 /* write C transposed: Ct [N][M], M contiguous */
+};
+
+/* Tile-wise GEMM over a range of tiles, optionally with transposed output.
+ * Runs the tiles tile_order[t_first .. t_first + t_count) (0 <= t_first,
+ * t_count >= 1, t_first + t_count <= T) and writes only their G-column
+ * windows of C; every other argument is as in tw_gemm_f16.
+ *   - flags & SSG_TW_OUT_T: C is Ct [N][M] (row n = output channel, tokens
+ *     contiguous), i.e. the K-major input At of a following tile-wise layer.
+ *     The tile-wise slides fuse A's transpose into the producing kernel (the
+ *     BERT layer); here the producing tile-wise GEMM writes its output in
+ *     that layout, so chained tile-wise layers need no separate transpose.
+ *   - a tile range lets the caller run condensed tiles as separate launches
+ *     (for example one per stream, as the slides' multi-stream scheduling
+ *     does); tw_gemm_f16 is one launch over all tiles in LPT order.
+ * Unknown flag bits or an empty or out-of-range tile range give SSG_EINVAL. */
+int tw_gemm_f16_ex(const void *At, const void *vals, const int32_t *offset_k,
+                   const int32_t *offset_n, const int32_t *v_ptr, const int32_t *k_ptr,
+                   const int32_t *n_ptr, const int32_t *tile_order, int32_t T, int32_t G,
+                   int32_t t_first, int32_t t_count, int32_t flags, void *C,
+                   int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Explicit transpose At[k][m] = A[m][k] (fp16), the "explicit transpose"
  * variant of the tile-wise slides.  M % 8 == 0, K % 8 == 0. */
 int ssg_transpose_f16(const void *A, void *At, int64_t M, int64_t K, void *stream);

@@ -37,6 +37,9 @@ from ._lib import (  # noqa: F401
     SSG_OUT_F16,
     SSG_OUT_I8,
     tw_gemm_f16,
+    tw_gemm_f16_ex,
+    tw_gemm_f16_streams,
+    SSG_TW_OUT_T,
     ssg_transpose_f16,
     ssg_device_arch,
     TwPacked,

@@ -56,6 +56,7 @@ SIGNATURES = {
     "dense_gemm_i8_out": [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P],
     "w24_gemm_i8_out": [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P],
     "tw_gemm_f16": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _I64, _I64, _I64, _P],
+    "tw_gemm_f16_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I64, _I64, _I64, _P],
     "ssg_transpose_f16": [_P, _P, _I64, _I64, _P],
     "ssg_device_arch": [ct.c_char_p, _I64],
 }
@@ -369,6 +370,50 @@ def tw_gemm_f16(At, packed: TwPacked, out=None):
     _check(load().tw_gemm_f16(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
                               _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]),
                               _ptr(arrs["tile_order"]), packed.T, packed.G, _ptr(C), M, packed.N, K, _stream(At)))
+    return C
+
+
+SSG_TW_OUT_T = 1
+
+
+def tw_gemm_f16_ex(At, packed: TwPacked, t_first=0, t_count=None, out_t=False, out=None):
+    """Tile-wise GEMM over tiles tile_order[t_first : t_first + t_count]; with out_t the
+    result is written transposed, Ct [N, M] (the K-major input of a next tile-wise layer).
+    Only the selected tiles' column windows of the output are written."""
+    torch = _torch()
+    K, M = At.shape
+    if K != packed.K:
+        raise ValueError(f"At has K={K}, packed weight has K={packed.K}")
+    if t_count is None:
+        t_count = packed.T - t_first
+    _dev(At, torch.float16, (K, M), "At")
+    arrs = packed.arrays()
+    _dev(arrs["vals"], torch.float16, None, "vals")
+    for key in ("offset_k", "offset_n", "v_ptr", "k_ptr", "n_ptr", "tile_order"):
+        _dev(arrs[key], torch.int32, None, key)
+    C = _out(out, (packed.N, M) if out_t else (M, packed.N), torch.float16, At)
+    _check(load().tw_gemm_f16_ex(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
+                                 _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]),
+                                 _ptr(arrs["tile_order"]), packed.T, packed.G, int(t_first), int(t_count),
+                                 SSG_TW_OUT_T if out_t else 0, _ptr(C), M, packed.N, K, _stream(At)))
+    return C
+
+
+def tw_gemm_f16_streams(At, packed: TwPacked, streams, out=None):
+    """The slides' multi-stream schedule: one launch per condensed tile, tiles taken
+    in tile_order and dealt round-robin over `streams` (default-priority torch
+    streams); the current stream waits for all of them before returning."""
+    torch = _torch()
+    K, M = At.shape
+    C = _out(out, (M, packed.N), torch.float16, At)
+    cur = torch.cuda.current_stream()
+    for st in streams:
+        st.wait_stream(cur)
+    for i in range(packed.T):
+        with torch.cuda.stream(streams[i % len(streams)]):
+            tw_gemm_f16_ex(At, packed, t_first=i, t_count=1, out=C)
+    for st in streams:
+        cur.wait_stream(st)
     return C
 
 

@@ -156,10 +156,12 @@ SSG_API int w24_gemm_i8_out(const int8_t *A, const int8_t *vals, const uint32_t 
     return w24_i8("w24_gemm_i8_out", A, vals, meta, scale, bias, C, out_type, M, N, K, stream);
 }
 
-SSG_API int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
-                        const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr, const int32_t *tile_order,
-                        int32_t T, int32_t G, void *C, int64_t M, int64_t N, int64_t K, void *stream) {
-    const char *fn = "tw_gemm_f16";
+namespace {
+
+int tw_run(const char *fn, const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
+           const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr, const int32_t *tile_order, int32_t T,
+           int32_t G, int32_t t_first, int32_t t_count, int32_t flags, void *C, int64_t M, int64_t N, int64_t K,
+           void *stream) {
     if (M < 0 || N <= 0 || K <= 0 || !fits_int(M) || !fits_int(N) || !fits_int(K))
         return ssg::fail(SSG_EINVAL, "%s: bad shape M=%lld N=%lld K=%lld", fn, (long long)M, (long long)N,
                          (long long)K);
@@ -168,7 +170,10 @@ SSG_API int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_
     if (N % G) return ssg::fail(SSG_EINVAL, "%s: N=%lld must be a multiple of G=%d", fn, (long long)N, G);
     if (T != N / G) return ssg::fail(SSG_EINVAL, "%s: T=%d must equal N/G=%lld", fn, T, (long long)(N / G));
     if (M % 8) return ssg::fail(SSG_EINVAL, "%s: M=%lld must be a multiple of 8", fn, (long long)M);
-    if (!fits_int((M + 127) / 128 * int64_t(T))) return ssg::fail(SSG_EINVAL, "%s: too many work items", fn);
+    if (t_first < 0 || t_count < 1 || int64_t(t_first) + t_count > T)
+        return ssg::fail(SSG_EINVAL, "%s: tile range [%d, %d + %d) outside [0, %d)", fn, t_first, t_first, t_count, T);
+    if (flags & ~SSG_TW_OUT_T) return ssg::fail(SSG_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+    if (!fits_int((M + 127) / 128 * int64_t(t_count))) return ssg::fail(SSG_EINVAL, "%s: too many work items", fn);
     if (M == 0) {
         ssg::clear_error();
         return SSG_OK;
@@ -179,9 +184,27 @@ SSG_API int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_
         return ssg::fail(SSG_EINVAL, "%s: At, vals and C must be 16-byte aligned", fn);
     int rc = check_device();
     if (rc) return rc;
-    return launched(ssg::launch_tw_f16(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G, C, int(M),
-                                       int(N), hipStream_t(stream)),
+    return launched(ssg::launch_tw_f16(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, t_first,
+                                       t_count, G, (flags & SSG_TW_OUT_T) != 0, C, int(M), int(N),
+                                       hipStream_t(stream)),
                     fn);
+}
+
+}  // namespace
+
+SSG_API int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
+                        const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr, const int32_t *tile_order,
+                        int32_t T, int32_t G, void *C, int64_t M, int64_t N, int64_t K, void *stream) {
+    return tw_run("tw_gemm_f16", At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G, 0, T, 0, C, M,
+                  N, K, stream);
+}
+
+SSG_API int tw_gemm_f16_ex(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
+                           const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
+                           const int32_t *tile_order, int32_t T, int32_t G, int32_t t_first, int32_t t_count,
+                           int32_t flags, void *C, int64_t M, int64_t N, int64_t K, void *stream) {
+    return tw_run("tw_gemm_f16_ex", At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G, t_first,
+                  t_count, flags, C, M, N, K, stream);
 }
 
 SSG_API int ssg_transpose_f16(const void *A, void *At, int64_t M, int64_t K, void *stream) {

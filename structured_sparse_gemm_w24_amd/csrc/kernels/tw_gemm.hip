@@ -137,7 +137,11 @@ __device__ __forceinline__ int tw_swz_w(int j, int c) {
     else return c ^ ((j >> 1) & 3);
 }
 
-template <class CF, int NJ>
+// OUTT: write C transposed, Ct [N][M] (token-contiguous rows), which is the
+// K-major input of a following tile-wise layer (the transpose fused into the
+// producing GEMM); otherwise C [M][N].  Cw points at the tile's first output
+// column (row, for OUTT).
+template <class CF, int NJ, bool OUTT>
 __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restrict__ At,
                                         const uint16_t *__restrict__ vt, const int32_t *__restrict__ offk,
                                         const int32_t *__restrict__ offn, int kt, int nt, int G, int m0,
@@ -245,54 +249,85 @@ __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restric
     }
 
     // ---- epilogue: G-wide output window in LDS (aliases the stage ring); rows
-    // padded by 16 bytes so the 16 tokens one scatter instruction writes fall in
-    // distinct banks
+    // padded by 16 bytes so the 16 tokens (or channels) one scatter instruction
+    // writes fall in distinct banks
     __syncthreads();
     uint8_t *win = smem;
-    const int wrow_chunks = G / 8;  // 16-byte chunks per window row
-    for (int c = tid; c < BM * wrow_chunks; c += NT)
-        *reinterpret_cast<u32x4 *>(win + (c / wrow_chunks) * WIN_ROW + (c % wrow_chunks) * 16) = u32x4{0, 0, 0, 0};
-    __syncthreads();
-    // acc[jb] lane (g16, j16) holds D[j = 16jb + 4*g16 + i][token = tok_mb + j16]
+    if constexpr (!OUTT) {
+        const int wrow_chunks = G / 8;  // 16-byte chunks per window row
+        for (int c = tid; c < BM * wrow_chunks; c += NT)
+            *reinterpret_cast<u32x4 *>(win + (c / wrow_chunks) * WIN_ROW + (c % wrow_chunks) * 16) =
+                u32x4{0, 0, 0, 0};
+        __syncthreads();
+        // acc[jb] lane (g16, j16) holds D[j = 16jb + 4*g16 + i][token = tok_mb + j16]
 #pragma unroll
-    for (int jb = 0; jb < NJ; ++jb) {
+        for (int jb = 0; jb < NJ; ++jb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = jb * 16 + 4 * g16 + i;
-            if (j < nt)
-                *reinterpret_cast<uint16_t *>(win + (tok_mb + j16) * WIN_ROW + s_offn[j] * 2) =
-                    __builtin_bit_cast(uint16_t, (_Float16)acc[jb][i]);
+            for (int i = 0; i < 4; ++i) {
+                const int j = jb * 16 + 4 * g16 + i;
+                if (j < nt)
+                    *reinterpret_cast<uint16_t *>(win + (tok_mb + j16) * WIN_ROW + s_offn[j] * 2) =
+                        __builtin_bit_cast(uint16_t, (_Float16)acc[jb][i]);
+            }
         }
-    }
-    __syncthreads();
-    for (int c = tid; c < BM * wrow_chunks; c += NT) {
-        const int row = c / wrow_chunks, ch = c % wrow_chunks;
-        const int m = m0 + row;
-        if (m < M) st16(Cw + int64_t(m) * N + ch * 8, *reinterpret_cast<const u32x4 *>(win + row * WIN_ROW + ch * 16));
+        __syncthreads();
+        for (int c = tid; c < BM * wrow_chunks; c += NT) {
+            const int row = c / wrow_chunks, ch = c % wrow_chunks;
+            const int m = m0 + row;
+            if (m < M)
+                st16(Cw + int64_t(m) * N + ch * 8, *reinterpret_cast<const u32x4 *>(win + row * WIN_ROW + ch * 16));
+        }
+    } else {
+        // transposed window [G][BM]: row = tile-local channel, tokens contiguous
+        constexpr int TROW = BM * 2 + 16;
+        static_assert(CF::GMAX * TROW <= CF::NB * CF::STAGE, "transposed window must fit in the stage ring");
+        constexpr int TCH = BM / 8;  // 16-byte chunks per row
+        for (int c = tid; c < G * TCH; c += NT)
+            *reinterpret_cast<u32x4 *>(win + (c / TCH) * TROW + (c % TCH) * 16) = u32x4{0, 0, 0, 0};
+        __syncthreads();
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = jb * 16 + 4 * g16 + i;
+                if (j < nt)
+                    *reinterpret_cast<uint16_t *>(win + s_offn[j] * TROW + (tok_mb + j16) * 2) =
+                        __builtin_bit_cast(uint16_t, (_Float16)acc[jb][i]);
+            }
+        }
+        __syncthreads();
+        for (int c = tid; c < G * TCH; c += NT) {
+            const int row = c / TCH, ch = c % TCH;
+            const int m = m0 + ch * 8;  // M % 8 == 0: a chunk is all in or all out
+            if (m < M)
+                st16(Cw + int64_t(row) * M + m, *reinterpret_cast<const u32x4 *>(win + row * TROW + ch * 16));
+        }
     }
 }
 
-template <class CF>
+// Work items: token block mb x tiles tile_order[t_first .. t_first + t_count).
+template <class CF, bool OUTT>
 __global__ void __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(CF::WPE)))
 tw_gemm_kernel(const uint16_t *__restrict__ At, const uint16_t *__restrict__ vals, const int32_t *__restrict__ offset_k,
                const int32_t *__restrict__ offset_n, const int32_t *__restrict__ v_ptr,
                const int32_t *__restrict__ k_ptr, const int32_t *__restrict__ n_ptr,
-               const int32_t *__restrict__ tile_order, int T, int G, uint16_t *__restrict__ C, int M, int N) {
+               const int32_t *__restrict__ tile_order, int t_first, int t_count, int G, uint16_t *__restrict__ C,
+               int M, int N) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[CF::SMEM];
     const int n_mb = (M + CF::BM - 1) / CF::BM;
-    const int item = xcd_remap(blockIdx.x, n_mb * T);
-    const int mb = item / T;
-    const int t = tile_order[item % T];
+    const int item = xcd_remap(blockIdx.x, n_mb * t_count);
+    const int mb = item / t_count;
+    const int t = tile_order[t_first + item % t_count];
     const int kp0 = k_ptr[t], kt = k_ptr[t + 1] - kp0;
     const int np0 = n_ptr[t], nt = n_ptr[t + 1] - np0;
     const uint16_t *vt = vals + v_ptr[t];
     const int32_t *offk = offset_k + kp0;
     const int32_t *offn = offset_n + np0;
-    uint16_t *Cw = C + int64_t(t) * G;
+    uint16_t *Cw = OUTT ? C + int64_t(t) * G * M : C + int64_t(t) * G;
     const int m0 = mb * CF::BM;
     switch ((nt + 15) >> 4) {
 #define TW_CASE(J) \
-    case J: tw_item<CF, J>(smem, At, vt, offk, offn, kt, nt, G, m0, Cw, M, N); break;
+    case J: tw_item<CF, J, OUTT>(smem, At, vt, offk, offn, kt, nt, G, m0, Cw, M, N); break;
         TW_CASE(0) TW_CASE(1) TW_CASE(2) TW_CASE(3) TW_CASE(4) TW_CASE(5) TW_CASE(6) TW_CASE(7) TW_CASE(8)
 #undef TW_CASE
         default: break;
@@ -305,11 +340,13 @@ using TwProd = TwCfg<32, 3, 512, 6>;
 
 hipError_t launch_tw_f16(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
                          const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
-                         const int32_t *tile_order, int T, int G, void *C, int M, int N, hipStream_t st) {
+                         const int32_t *tile_order, int t_first, int t_count, int G, bool out_t, void *C, int M,
+                         int N, hipStream_t st) {
     const int n_mb = (M + TwProd::BM - 1) / TwProd::BM;
-    hipLaunchKernelGGL(tw_gemm_kernel<TwProd>, dim3(n_mb * T), dim3(TwProd::NT), 0, st,
-                       static_cast<const uint16_t *>(At), static_cast<const uint16_t *>(vals), offset_k, offset_n,
-                       v_ptr, k_ptr, n_ptr, tile_order, T, G, static_cast<uint16_t *>(C), M, N);
+    auto kern = out_t ? tw_gemm_kernel<TwProd, true> : tw_gemm_kernel<TwProd, false>;
+    hipLaunchKernelGGL(kern, dim3(n_mb * t_count), dim3(TwProd::NT), 0, st, static_cast<const uint16_t *>(At),
+                       static_cast<const uint16_t *>(vals), offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order,
+                       t_first, t_count, G, static_cast<uint16_t *>(C), M, N);
     return hipGetLastError();
 }
 

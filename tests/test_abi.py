@@ -26,7 +26,7 @@ def test_header_declares_the_path():
     assert {"w24_pack_f16", "w24_pack_i8", "w24_unpack_f16", "w24_unpack_i8", "tw_pack_query",
             "tw_pack_f16", "tw_unpack_f16", "dense_gemm_f16", "dense_gemm_i8", "w24_gemm_f16",
             "w24_gemm_i8", "tw_gemm_f16", "ssg_transpose_f16", "ssg_last_error",
-            "dense_gemm_i8_out", "w24_gemm_i8_out"} <= names
+            "dense_gemm_i8_out", "w24_gemm_i8_out", "tw_gemm_f16_ex"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -72,6 +72,9 @@ def has_device(lib):
     (lambda r: r.w24_gemm_i8_out(*[_p(16)] * 3, None, None, _p(16), 2, 8, 64, 128, None), "needs scale"),
     (lambda r: r.dense_gemm_i8_out(*[_p(16)] * 3, _p(36), _p(16), 3, 8, 64, 128, None), "16-byte aligned"),
     (lambda r: r.dense_gemm_i8_out(*[_p(16)] * 4, _p(16), 1, 8, 64, 100, None), "multiple of 128"),
+    (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 1, 2, 0, _p(16), 8, 32, 64, None), "tile range"),
+    (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 0, 0, _p(16), 8, 32, 64, None), "tile range"),
+    (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 2, 6, _p(16), 8, 32, 64, None), "unknown flags"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 24, _p(16), 8, 48, 64, None), "G=24"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 256, _p(16), 8, 512, 64, None), "at most 128"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 3, 16, _p(16), 8, 32, 64, None), "T=3"),

@@ -344,6 +344,72 @@ def test_tw_indexed_oracle_agrees(lib, gpu):
     assert oracle.loose_err(C, ref) <= 1e-2
 
 
+# ---------------------------------------------------------------- tile-wise: fused transpose, tile ranges, streams
+def _tw_setup(lib, A, Wp, G):
+    packed = lib.tw_pack_f16(Wp, G).to("cuda")
+    At = lib.ssg_transpose_f16(T(A))
+    return packed, At
+
+
+@pytest.mark.parametrize("M,K,N,G,d", TW_SMALL)
+def test_tw_transposed_output(lib, gpu, M, K, N, G, d):
+    import torch
+    case = wl.random_tw_f16(np.random.default_rng(M + 2 * K + G), M, K, N, G, d)
+    packed, At = _tw_setup(lib, case["A"], case["Wp"], G)
+    C = H(lib.tw_gemm_f16(At, packed))
+    Ct = H(lib.tw_gemm_f16_ex(At, packed, out_t=True,
+                              out=torch.full((N, M), float("nan"), dtype=torch.float16, device="cuda")))
+    assert Ct.shape == (N, M)
+    # the same products in the same order: bit-identical, only the layout differs
+    assert np.array_equal(Ct.T.view(np.uint16), C.view(np.uint16))
+
+
+def test_tw_chain_without_transpose(lib, gpu):
+    # two tile-wise layers: layer 1 writes Ct1 [N1][M], which is layer 2's At directly
+    rng = np.random.default_rng(30)
+    M, K, N1, N2, G = 256, 384, 512, 256, 128
+    l1 = wl.random_tw_f16(rng, M, K, N1, G, [0.3, 0.5, 0.2, 0.4])
+    W2 = wl.prune_tilewise(wl.f16_normal(rng, (N1, N2), 0.05), G, np.array([0.4, 0.25]))
+    p1 = lib.tw_pack_f16(l1["Wp"], G).to("cuda")
+    p2 = lib.tw_pack_f16(W2, G).to("cuda")
+    Ct1 = lib.tw_gemm_f16_ex(lib.ssg_transpose_f16(T(l1["A"])), p1, out_t=True)
+    C2 = H(lib.tw_gemm_f16(Ct1, p2))
+    A2 = H(Ct1).T.copy()  # layer 1's fp16 output, as the oracle's input of layer 2
+    check_f16(A2, l1["A"], l1["Wp"], K, "chain layer 1")
+    check_f16(C2, A2, W2, N1, "chain layer 2")
+
+
+def test_tw_tile_ranges(lib, gpu):
+    import torch
+    case = wl.random_tw_f16(np.random.default_rng(31), 200, 512, 640, 128, [0.2, 0.5, 0.0, 0.8, 0.3])
+    packed, At = _tw_setup(lib, case["A"], case["Wp"], 128)
+    full = H(lib.tw_gemm_f16(At, packed))
+    C = torch.full((200, 640), float("nan"), dtype=torch.float16, device="cuda")
+    lib.tw_gemm_f16_ex(At, packed, t_first=1, t_count=2, out=C)
+    part = H(C)
+    order = H(packed.tile_order)
+    done = set(int(t) for t in order[1:3])
+    for t in range(5):
+        win = part[:, t * 128:(t + 1) * 128]
+        if t in done:
+            assert np.array_equal(win.view(np.uint16), full[:, t * 128:(t + 1) * 128].view(np.uint16))
+        else:
+            assert np.isnan(win).all()  # tiles outside the range are not written
+    lib.tw_gemm_f16_ex(At, packed, t_first=0, t_count=1, out=C)
+    lib.tw_gemm_f16_ex(At, packed, t_first=3, t_count=2, out=C)
+    assert np.array_equal(H(C).view(np.uint16), full.view(np.uint16))
+
+
+def test_tw_multi_stream_schedule(lib, gpu):
+    import torch
+    c = wl.make_cfg3()
+    packed, At = _tw_setup(lib, c["A"], c["Wp"], c["G"])
+    full = H(lib.tw_gemm_f16(At, packed))
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    C = H(lib.tw_gemm_f16_streams(At, packed, streams))
+    assert np.array_equal(C.view(np.uint16), full.view(np.uint16))
+
+
 # ---------------------------------------------------------------- transpose, determinism, errors
 @pytest.mark.parametrize("M,K", [(8, 8), (136, 200), (4096, 768), (1000, 1024)])
 def test_transpose_bit_exact(lib, gpu, M, K):
