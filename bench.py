@@ -223,6 +223,9 @@ def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
         d["Ct"] = torch.empty((N, M), dtype=torch.float16, device=dev)
     fu = lambda i: ssg.tw_gemm_f16_ex(sets[i % R]["At"], sets[i % R]["packed"], out_t=True, out=sets[i % R]["Ct"])
     t_fused = timer(fu, steps, warmup)
+    # the slides' "without transpose" case: row-major A gathered as scattered elements
+    nt_ = lambda i: ssg.tw_gemm_f16_ex(sets[i % R]["A"], sets[i % R]["packed"], a_rowmajor=True, out=sets[i % R]["C"])
+    t_no_transpose = timer(nt_, steps, warmup)
     # the slides' multi-stream schedule: one launch per tile over 4 streams
     streams = [torch.cuda.Stream() for _ in range(4)]
     ms = lambda i: ssg.tw_gemm_f16_streams(sets[i % R]["At"], sets[i % R]["packed"], streams, out=sets[i % R]["C"])
@@ -231,7 +234,8 @@ def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
     except RuntimeError:
         t_ms, ms_timing = Timer(torch, graph=False)(ms, steps, warmup), "eager"
     return dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
-                t_fused_transposed_out_ms=t_fused, t_multistream4_ms=t_ms, multistream_timing=ms_timing,
+                t_fused_transposed_out_ms=t_fused, t_no_transpose_ms=t_no_transpose,
+                t_multistream4_ms=t_ms, multistream_timing=ms_timing,
                 t_transpose_ms=timer(tr, steps, warmup),
                 t_dense_ms=timer(de, steps, warmup), rotate_sets=R, bytes=bytes_,
                 ops=perf.tw_ops(M, nnz), union_rows=union)

@@ -209,7 +209,8 @@ int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_k,
 
 /* Flags of tw_gemm_f16_ex. */
 enum {
-    SSG_TW_OUT_T = 1 /* write C transposed: Ct [N][M], M contiguous */
+    SSG_TW_OUT_T = 1,     /* write C transposed: Ct [N][M], M contiguous            */
+    SSG_TW_A_ROWMAJOR = 2 /* the A argument is row-major A [M][K], not At [K][M]    */
 };
 
 /* Tile-wise GEMM over a range of tiles, optionally with transposed output.
@@ -224,6 +225,10 @@ enum {
  *   - a tile range lets the caller run condensed tiles as separate launches
  *     (for example one per stream, as the slides' multi-stream scheduling
  *     does); tw_gemm_f16 is one launch over all tiles in LPT order.
+ *   - flags & SSG_TW_A_ROWMAJOR: the first argument is A [M][K] row-major
+ *     (16-byte aligned), read without a transpose: the slides' "without
+ *     transpose" case, whose gathered activations are scattered 2-byte
+ *     accesses (it exists to measure that cost; K-major At is the fast path).
  * Unknown flag bits or an empty or out-of-range tile range give SSG_EINVAL. */
 int tw_gemm_f16_ex(const void *At, const void *vals, const int32_t *offset_k,
                    const int32_t *offset_n, const int32_t *v_ptr, const int32_t *k_ptr,

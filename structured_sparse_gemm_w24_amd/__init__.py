@@ -40,6 +40,7 @@ from ._lib import (  # noqa: F401
     tw_gemm_f16_ex,
     tw_gemm_f16_streams,
     SSG_TW_OUT_T,
+    SSG_TW_A_ROWMAJOR,
     ssg_transpose_f16,
     ssg_device_arch,
     TwPacked,

@@ -376,26 +376,34 @@ def tw_gemm_f16(At, packed: TwPacked, out=None):
 SSG_TW_OUT_T = 1
 
 
-def tw_gemm_f16_ex(At, packed: TwPacked, t_first=0, t_count=None, out_t=False, out=None):
+SSG_TW_A_ROWMAJOR = 2
+
+
+def tw_gemm_f16_ex(At, packed: TwPacked, t_first=0, t_count=None, out_t=False, a_rowmajor=False, out=None):
     """Tile-wise GEMM over tiles tile_order[t_first : t_first + t_count]; with out_t the
     result is written transposed, Ct [N, M] (the K-major input of a next tile-wise layer).
-    Only the selected tiles' column windows of the output are written."""
+    With a_rowmajor the first argument is row-major A [M, K] (the slides' "without
+    transpose" case).  Only the selected tiles' column windows of the output are written."""
     torch = _torch()
-    K, M = At.shape
+    if a_rowmajor:
+        M, K = At.shape
+    else:
+        K, M = At.shape
     if K != packed.K:
         raise ValueError(f"At has K={K}, packed weight has K={packed.K}")
     if t_count is None:
         t_count = packed.T - t_first
-    _dev(At, torch.float16, (K, M), "At")
+    _dev(At, torch.float16, (M, K) if a_rowmajor else (K, M), "A" if a_rowmajor else "At")
     arrs = packed.arrays()
     _dev(arrs["vals"], torch.float16, None, "vals")
     for key in ("offset_k", "offset_n", "v_ptr", "k_ptr", "n_ptr", "tile_order"):
         _dev(arrs[key], torch.int32, None, key)
     C = _out(out, (packed.N, M) if out_t else (M, packed.N), torch.float16, At)
+    flags = (SSG_TW_OUT_T if out_t else 0) | (SSG_TW_A_ROWMAJOR if a_rowmajor else 0)
     _check(load().tw_gemm_f16_ex(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
                                  _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]),
                                  _ptr(arrs["tile_order"]), packed.T, packed.G, int(t_first), int(t_count),
-                                 SSG_TW_OUT_T if out_t else 0, _ptr(C), M, packed.N, K, _stream(At)))
+                                 flags, _ptr(C), M, packed.N, K, _stream(At)))
     return C
 
 

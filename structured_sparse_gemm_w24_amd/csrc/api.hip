@@ -172,7 +172,7 @@ int tw_run(const char *fn, const void *At, const void *vals, const int32_t *offs
     if (M % 8) return ssg::fail(SSG_EINVAL, "%s: M=%lld must be a multiple of 8", fn, (long long)M);
     if (t_first < 0 || t_count < 1 || int64_t(t_first) + t_count > T)
         return ssg::fail(SSG_EINVAL, "%s: tile range [%d, %d + %d) outside [0, %d)", fn, t_first, t_first, t_count, T);
-    if (flags & ~SSG_TW_OUT_T) return ssg::fail(SSG_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+    if (flags & ~(SSG_TW_OUT_T | SSG_TW_A_ROWMAJOR)) return ssg::fail(SSG_EINVAL, "%s: unknown flags 0x%x", fn, flags);
     if (!fits_int((M + 127) / 128 * int64_t(t_count))) return ssg::fail(SSG_EINVAL, "%s: too many work items", fn);
     if (M == 0) {
         ssg::clear_error();
@@ -185,8 +185,8 @@ int tw_run(const char *fn, const void *At, const void *vals, const int32_t *offs
     int rc = check_device();
     if (rc) return rc;
     return launched(ssg::launch_tw_f16(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, t_first,
-                                       t_count, G, (flags & SSG_TW_OUT_T) != 0, C, int(M), int(N),
-                                       hipStream_t(stream)),
+                                       t_count, G, (flags & SSG_TW_OUT_T) != 0, (flags & SSG_TW_A_ROWMAJOR) != 0, C,
+                                       int(M), int(N), int(K), hipStream_t(stream)),
                     fn);
 }
 

@@ -18,11 +18,13 @@ hipError_t launch_w24_f16(const void *A, const void *vals, const uint32_t *meta,
 hipError_t launch_w24_i8(const void *A, const void *vals, const uint32_t *meta, const float *scale,
                          const float *bias, void *C, int out, int M, int N, int K, hipStream_t st);
 // Tiles tile_order[t_first .. t_first + t_count); out_t: C is written
-// transposed, Ct [N][M].
+// transposed, Ct [N][M]; a_rowmajor: the A operand is row-major [M][K]
+// instead of K-major At [K][M].
 hipError_t launch_tw_f16(const void *At, const void *vals, const int32_t *offset_k,
                          const int32_t *offset_n, const int32_t *v_ptr, const int32_t *k_ptr,
                          const int32_t *n_ptr, const int32_t *tile_order, int t_first, int t_count,
-                         int G, bool out_t, void *C, int M, int N, hipStream_t st);
+                         int G, bool out_t, bool a_rowmajor, void *C, int M, int N, int K,
+                         hipStream_t st);
 hipError_t launch_transpose_f16(const void *A, void *At, int M, int K, hipStream_t st);
 
 }  // namespace ssg

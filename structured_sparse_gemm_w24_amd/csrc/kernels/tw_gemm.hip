@@ -141,11 +141,15 @@ __device__ __forceinline__ int tw_swz_w(int j, int c) {
 // K-major input of a following tile-wise layer (the transpose fused into the
 // producing GEMM); otherwise C [M][N].  Cw points at the tile's first output
 // column (row, for OUTT).
-template <class CF, int NJ, bool OUTT>
+// AROW: A is row-major [M][K] (the slides' "without transpose" case): the
+// picked k of a token are scattered 2-byte elements of its row, so each stage
+// is gathered through registers, 8 elements per thread, into the same
+// K-major LDS layout; every element is its own memory request.
+template <class CF, int NJ, bool OUTT, bool AROW>
 __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restrict__ At,
                                         const uint16_t *__restrict__ vt, const int32_t *__restrict__ offk,
                                         const int32_t *__restrict__ offn, int kt, int nt, int G, int m0,
-                                        uint16_t *__restrict__ Cw, int M, int N) {
+                                        uint16_t *__restrict__ Cw, int M, int N, int K) {
     constexpr int NW = CF::NW, NT = CF::NT, BM = CF::BM, BK = CF::BK, NB = CF::NB, KCAP = CF::KCAP;
     constexpr int A_STAGE = CF::A_STAGE, STAGE = CF::STAGE, LA = CF::LA, KS = CF::KS, WROWS = CF::WROWS;
     constexpr int WIN_ROW = CF::WIN_ROW;
@@ -157,7 +161,7 @@ __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restric
     const int ld = (kt + 7) & ~7;
     // V_t loads per stage: NJ*16 rows of 2*BK bytes = NJ*KS KiB, round-robin over waves
     const int lw = (NJ * KS - wave + NW - 1) / NW;
-    const int per_stage = LA + lw;
+    const int per_stage = (AROW ? 0 : LA) + lw;  // direct-to-LDS loads per stage
 
     // A loads: instruction j of the wave covers stage rows 4q .. 4q+3 (q = j*NW + wave);
     // lane -> row 4q + lane/16, stored chunk lane%16.
@@ -197,8 +201,25 @@ __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restric
 
             auto issue = [&](int s) {
                 uint8_t *base = smem + (s % NB) * STAGE;
+                if constexpr (AROW) {
+                    static_assert(BK == 32 && NT == 4 * BM, "gather mapping: 4 threads x 8 picked rows per token");
+                    const int tok = tid >> 2, kg = (tid & 3) * 8;
+                    const int m = m0 + tok;
+                    uint16_t v[8];
 #pragma unroll
-                for (int j = 0; j < LA; ++j) {
+                    for (int e = 0; e < 8; ++e) {
+                        const int kk = s * BK + kg + e;
+                        v[e] = (kk < ck && m < M) ? At[int64_t(m) * K + s_idx[kk]] : uint16_t(0);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int r = kg + e;
+                        *reinterpret_cast<uint16_t *>(base + r * (BM * 2) + tw_swz_a(r, tok >> 3) * 16 + (tok & 7) * 2) =
+                            v[e];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < (AROW ? 0 : LA); ++j) {
                     const int q = j * NW + wave;
                     const int r = 4 * q + a_sub;  // stage row
                     const int kk = s * BK + r;    // picked row inside the chunk
@@ -306,13 +327,13 @@ __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restric
 }
 
 // Work items: token block mb x tiles tile_order[t_first .. t_first + t_count).
-template <class CF, bool OUTT>
+template <class CF, bool OUTT, bool AROW>
 __global__ void __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(CF::WPE)))
 tw_gemm_kernel(const uint16_t *__restrict__ At, const uint16_t *__restrict__ vals, const int32_t *__restrict__ offset_k,
                const int32_t *__restrict__ offset_n, const int32_t *__restrict__ v_ptr,
                const int32_t *__restrict__ k_ptr, const int32_t *__restrict__ n_ptr,
                const int32_t *__restrict__ tile_order, int t_first, int t_count, int G, uint16_t *__restrict__ C,
-               int M, int N) {
+               int M, int N, int K) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[CF::SMEM];
     const int n_mb = (M + CF::BM - 1) / CF::BM;
     const int item = xcd_remap(blockIdx.x, n_mb * t_count);
@@ -327,7 +348,7 @@ tw_gemm_kernel(const uint16_t *__restrict__ At, const uint16_t *__restrict__ val
     const int m0 = mb * CF::BM;
     switch ((nt + 15) >> 4) {
 #define TW_CASE(J) \
-    case J: tw_item<CF, J, OUTT>(smem, At, vt, offk, offn, kt, nt, G, m0, Cw, M, N); break;
+    case J: tw_item<CF, J, OUTT, AROW>(smem, At, vt, offk, offn, kt, nt, G, m0, Cw, M, N, K); break;
         TW_CASE(0) TW_CASE(1) TW_CASE(2) TW_CASE(3) TW_CASE(4) TW_CASE(5) TW_CASE(6) TW_CASE(7) TW_CASE(8)
 #undef TW_CASE
         default: break;
@@ -340,13 +361,14 @@ using TwProd = TwCfg<32, 3, 512, 6>;
 
 hipError_t launch_tw_f16(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
                          const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
-                         const int32_t *tile_order, int t_first, int t_count, int G, bool out_t, void *C, int M,
-                         int N, hipStream_t st) {
+                         const int32_t *tile_order, int t_first, int t_count, int G, bool out_t, bool a_rowmajor,
+                         void *C, int M, int N, int K, hipStream_t st) {
     const int n_mb = (M + TwProd::BM - 1) / TwProd::BM;
-    auto kern = out_t ? tw_gemm_kernel<TwProd, true> : tw_gemm_kernel<TwProd, false>;
+    auto kern = a_rowmajor ? (out_t ? tw_gemm_kernel<TwProd, true, true> : tw_gemm_kernel<TwProd, false, true>)
+                           : (out_t ? tw_gemm_kernel<TwProd, true, false> : tw_gemm_kernel<TwProd, false, false>);
     hipLaunchKernelGGL(kern, dim3(n_mb * t_count), dim3(TwProd::NT), 0, st, static_cast<const uint16_t *>(At),
                        static_cast<const uint16_t *>(vals), offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order,
-                       t_first, t_count, G, static_cast<uint16_t *>(C), M, N);
+                       t_first, t_count, G, static_cast<uint16_t *>(C), M, N, K);
     return hipGetLastError();
 }
 

@@ -74,7 +74,7 @@ def has_device(lib):
     (lambda r: r.dense_gemm_i8_out(*[_p(16)] * 4, _p(16), 1, 8, 64, 100, None), "multiple of 128"),
     (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 1, 2, 0, _p(16), 8, 32, 64, None), "tile range"),
     (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 0, 0, _p(16), 8, 32, 64, None), "tile range"),
-    (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 2, 6, _p(16), 8, 32, 64, None), "unknown flags"),
+    (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 2, 4, _p(16), 8, 32, 64, None), "unknown flags"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 24, _p(16), 8, 48, 64, None), "G=24"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 256, _p(16), 8, 512, 64, None), "at most 128"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 3, 16, _p(16), 8, 32, 64, None), "T=3"),

@@ -364,6 +364,19 @@ def test_tw_transposed_output(lib, gpu, M, K, N, G, d):
     assert np.array_equal(Ct.T.view(np.uint16), C.view(np.uint16))
 
 
+@pytest.mark.parametrize("M,K,N,G,d", TW_SMALL)
+def test_tw_row_major_a(lib, gpu, M, K, N, G, d):
+    # the "without transpose" case reads A [M][K] directly; the LDS stage holds the
+    # same values in the same places, so the result is bit-identical
+    case = wl.random_tw_f16(np.random.default_rng(M + 3 * K + G), M, K, N, G, d)
+    packed, At = _tw_setup(lib, case["A"], case["Wp"], G)
+    C = H(lib.tw_gemm_f16(At, packed))
+    Cr = H(lib.tw_gemm_f16_ex(T(case["A"]), packed, a_rowmajor=True))
+    assert np.array_equal(Cr.view(np.uint16), C.view(np.uint16))
+    Crt = H(lib.tw_gemm_f16_ex(T(case["A"]), packed, a_rowmajor=True, out_t=True))
+    assert np.array_equal(Crt.T.view(np.uint16), C.view(np.uint16))
+
+
 def test_tw_chain_without_transpose(lib, gpu):
     # two tile-wise layers: layer 1 writes Ct1 [N1][M], which is layer 2's At directly
     rng = np.random.default_rng(30)
