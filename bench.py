@@ -202,7 +202,7 @@ def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
                 t_dense_ms=timer(de, steps, warmup), t_torch_ms=timer(tm, steps, warmup), rotate_sets=R)
 
 
-def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
+def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, extras=True):
     dev = torch.device("cuda")
     M, K, N, G = c["M"], c["K"], c["N"], c["G"]
     host = ssg.tw_pack_f16(c["Wp"], G)
@@ -218,6 +218,11 @@ def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
     de = lambda i: ssg.dense_gemm_f16(sets[i % R]["A"], sets[i % R]["Wt"], out=sets[i % R]["C"])
     nnz = int((np.diff(host.k_ptr) * np.diff(host.n_ptr)).sum())
     st = timer.stats(sp, steps, warmup)
+    out = dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
+               t_transpose_ms=timer(tr, steps, warmup), t_dense_ms=timer(de, steps, warmup), rotate_sets=R,
+               bytes=bytes_, ops=perf.tw_ops(M, nnz), union_rows=union)
+    if not extras:
+        return out
     # fused transpose: the same GEMM writing Ct [N][M], the next tile-wise layer's At
     for d in sets:
         d["Ct"] = torch.empty((N, M), dtype=torch.float16, device=dev)
@@ -233,12 +238,9 @@ def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
         t_ms, ms_timing = timer(ms, steps, warmup), "graph"
     except RuntimeError:
         t_ms, ms_timing = Timer(torch, graph=False)(ms, steps, warmup), "eager"
-    return dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
-                t_fused_transposed_out_ms=t_fused, t_no_transpose_ms=t_no_transpose,
-                t_multistream4_ms=t_ms, multistream_timing=ms_timing,
-                t_transpose_ms=timer(tr, steps, warmup),
-                t_dense_ms=timer(de, steps, warmup), rotate_sets=R, bytes=bytes_,
-                ops=perf.tw_ops(M, nnz), union_rows=union)
+    out.update(t_fused_transposed_out_ms=t_fused, t_no_transpose_ms=t_no_transpose, t_multistream4_ms=t_ms,
+               multistream_timing=ms_timing)
+    return out
 
 
 # ---------------------------------------------------------------- cpu baseline
@@ -290,6 +292,9 @@ def main(argv=None):
                     help="table mode: comma list from " + ",".join(WORKLOADS) +
                          " or cfg5:<qkv|proj|fc1|fc2> for one layer-0 GEMM (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--no-tw-extras", action="store_true",
+                    help="table mode: time only the grouped tile-wise kernel (not the fused, row-major-A "
+                         "and multi-stream variants)")
     ap.add_argument("--warm", action="store_true", help="one input set (cache-resident) instead of rotating")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a replayed HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -565,7 +570,7 @@ def table(a, torch, ssg, perf, wl, timer):
         c4 = wl.make_cfg4()
         tw_cases += [c4["fc1"], c4["fc2"]]
     for c in tw_cases:
-        r = tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate)
+        r = tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate, extras=not a.no_tw_extras)
         emit(dict(workload=c["name"] + "_tw_f16", shape=[c["M"], c["K"], c["N"]], **r,
                   tflops_nonzero=r["ops"] / r["t_sparse_ms"] / 1e9, gbs=r["bytes"] / r["t_sparse_ms"] / 1e6,
                   speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],

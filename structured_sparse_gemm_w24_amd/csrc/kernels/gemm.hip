@@ -537,14 +537,14 @@ static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const ui
 }
 
 hipError_t launch_dense_f16(const void *A, const void *Wt, void *C, int M, int N, int K, hipStream_t st) {
-    return launch_shape<DENSE_F16, EPI_F16, false, true>(pick_f16(M, N), A, Wt, nullptr, nullptr, nullptr, C, M, N, K,
-                                                          st);
+    return launch_shape<DENSE_F16, EPI_F16, true, true>(pick_f16(M, N), A, Wt, nullptr, nullptr, nullptr, C, M, N, K,
+                                                         st);
 }
 
 hipError_t launch_w24_f16(const void *A, const void *vals, const uint32_t *meta, void *C, int M, int N, int K,
                           hipStream_t st) {
-    return launch_shape<W24_F16, EPI_F16, false, false>(pick_f16(M, N), A, vals, meta, nullptr, nullptr, C, M, N, K,
-                                                         st);
+    return launch_shape<W24_F16, EPI_F16, true, false>(pick_f16(M, N), A, vals, meta, nullptr, nullptr, C, M, N, K,
+                                                        st);
 }
 
 // int8 kinds: out selects the epilogue (OUT_I32 raw accumulators; OUT_F32,
