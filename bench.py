@@ -185,6 +185,28 @@ def w24_i8_out_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate=
                 t_dense_ms=timer(de, steps, warmup), rotate_sets=R, out_bytes=ob)
 
 
+def tw_i8_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate=True):
+    """int8 tile-wise GEMM (fp16 or int8 output) and the dense int8 GEMM with the same epilogue."""
+    dev = torch.device("cuda")
+    M, K, N, G = c["M"], c["K"], c["N"], c["G"]
+    odt = {"f16": torch.float16, "i8": torch.int8}[out_type]
+    ob = {"f16": 2, "i8": 1}[out_type]
+    host = ssg.tw_pack_i8(c["Wp"], G)
+    R = rotation(M * K + M * N * ob + host.vals.size) if rotate else 1
+    A = torch.from_numpy(c["A"]).to(dev)
+    sets = [dict(A=A, At=A.t().contiguous(), packed=host.to(dev), scale=torch.from_numpy(c["scale"]).to(dev),
+                 C=torch.empty((M, N), dtype=odt, device=dev),
+                 Wt=torch.from_numpy(np.ascontiguousarray(c["W"].T)).to(dev)) for _ in range(R)]
+    sp = lambda i: ssg.tw_gemm_i8(sets[i % R]["At"], sets[i % R]["packed"], sets[i % R]["scale"], out_type=out_type,
+                                  out=sets[i % R]["C"])
+    de = lambda i: ssg.dense_gemm_i8_out(sets[i % R]["A"], sets[i % R]["Wt"], sets[i % R]["scale"],
+                                         out_type=out_type, out=sets[i % R]["C"])
+    nnz = int((np.diff(host.k_ptr) * np.diff(host.n_ptr)).sum())
+    st = timer.stats(sp, steps, warmup)
+    return dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
+                t_dense_ms=timer(de, steps, warmup), rotate_sets=R, ops=perf.tw_ops(M, nnz))
+
+
 def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
     dev = torch.device("cuda")
     M, K, N = c["M"], c["K"], c["N"]
@@ -526,7 +548,7 @@ def cfg5_stack(torch, ssg, perf, wl, dtype, timer, steps_gemm=20, passes=3, laye
                 by_shape=by_shape)
 
 
-WORKLOADS = ("cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg5stack")
+WORKLOADS = ("cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg5stack", "cfg3_i8")
 
 
 def table(a, torch, ssg, perf, wl, timer):
@@ -576,6 +598,14 @@ def table(a, torch, ssg, perf, wl, timer):
                   speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
                   speedup_vs_dense_incl_transpose=r["t_dense_ms"] / (r["t_sparse_ms"] + r["t_transpose_ms"])))
         torch.cuda.empty_cache()
+    if "cfg3_i8" in want:
+        c = wl.make_cfg3_i8()
+        for out_type in ("f16", "i8"):
+            r = tw_i8_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate)
+            emit(dict(workload=f"cfg3_shape_tw_i8_{out_type}_out", shape=[c["M"], c["K"], c["N"]], **r,
+                      tops_nonzero=r["ops"] / r["t_sparse_ms"] / 1e9,
+                      speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
+            torch.cuda.empty_cache()
     only5 = {w.split(":", 1)[1] for w in want if w.startswith("cfg5:")}
     if "cfg5" in want or only5:
         for g in wl.cfg5_layers("f16", layers=1):

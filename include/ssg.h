@@ -108,14 +108,17 @@ int w24_unpack_i8(const int8_t *vals, const uint32_t *meta, int64_t K, int64_t N
  *   offset_k  kept rows of tile t, global k, ascending (rows with a nonzero
  *             among the tile's columns);
  *   vals      tile t's block V_t[j][kk] = W[offset_k[kk]][t*G + offset_n[j]],
- *             stored [N_t][ld_t] with ld_t = K_t rounded up to a multiple of
- *             8 (zero padded), tiles back to back;
+ *             stored [N_t][ld_t] with ld_t = K_t rounded up so that a row is
+ *             a multiple of 16 bytes (8 fp16 or 16 int8 elements; zero
+ *             padded), tiles back to back;
  *   v_ptr, k_ptr, n_ptr  [T+1] prefix sums (elements of vals, of offset_k,
  *             of offset_n);
  *   tile_order [T] tiles by K_t*N_t descending, ties to the lower t
  *             (longest-processing-time order for the grouped launch).
- * tw_pack_query fills the sizes; tw_pack_f16 returns SSG_ENOSPC when a
- * capacity in *cap is smaller than needed.  Requires G > 0, K > 0, N > 0,
+ * tw_pack_query (tw_pack_query_i8) fills the sizes; tw_pack_f16
+ * (tw_pack_i8) returns SSG_ENOSPC when a capacity in *cap is smaller than
+ * needed.  The int8 forms are the same format with int8 values (the
+ * quantised deployment of the integer path).  Requires G > 0, K > 0, N > 0,
  * K < 2^31, and sum of tile sizes < 2^31.
  * ------------------------------------------------------------------------ */
 typedef struct {
@@ -132,6 +135,13 @@ int tw_pack_f16(const uint16_t *W, int64_t K, int64_t N, int32_t G, const tw_siz
 int tw_unpack_f16(const uint16_t *vals, const int32_t *offset_k, const int32_t *offset_n,
                   const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
                   int64_t K, int64_t N, int32_t G, uint16_t *W);
+int tw_pack_query_i8(const int8_t *W, int64_t K, int64_t N, int32_t G, tw_sizes *out);
+int tw_pack_i8(const int8_t *W, int64_t K, int64_t N, int32_t G, const tw_sizes *cap,
+               int8_t *vals, int32_t *offset_k, int32_t *offset_n,
+               int32_t *v_ptr, int32_t *k_ptr, int32_t *n_ptr, int32_t *tile_order);
+int tw_unpack_i8(const int8_t *vals, const int32_t *offset_k, const int32_t *offset_n,
+                 const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
+                 int64_t K, int64_t N, int32_t G, int8_t *W);
 
 /* ------------------------------------------------------------------------
  * Device GEMMs (gfx950 only: SSG_EARCH elsewhere, SSG_ENODEV without a GPU).
@@ -235,6 +245,22 @@ int tw_gemm_f16_ex(const void *At, const void *vals, const int32_t *offset_k,
                    const int32_t *n_ptr, const int32_t *tile_order, int32_t T, int32_t G,
                    int32_t t_first, int32_t t_count, int32_t flags, void *C,
                    int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Tile-wise GEMM, int8 in, exact int32 accumulate: the tile-wise format
+ * (tw_pack_i8's arrays) on the integer path of GPUSQ-ViT ("Boost Vision
+ * Transformer with GPU-Friendly Sparsity and Quantization", abstract).  At
+ * is int8 A stored K-major ([K][M], M contiguous).  The epilogue is that of
+ * the int8 GEMMs: out_type SSG_OUT_I32 writes the raw accumulators (scale
+ * and bias NULL), otherwise y = float(acc) * scale[n] (+ bias[n]) stored as
+ * fp32, fp16 or saturated int8 (scale, bias: fp32 [N], 16-byte aligned).
+ * Every column of C is written: pruned columns get the epilogue of a zero
+ * accumulator (0 * scale[n] + bias[n]).  Requires G % 16 == 0, G <= 128,
+ * N % G == 0, M % 16 == 0, K >= 1. */
+int tw_gemm_i8(const int8_t *At, const int8_t *vals, const int32_t *offset_k,
+               const int32_t *offset_n, const int32_t *v_ptr, const int32_t *k_ptr,
+               const int32_t *n_ptr, const int32_t *tile_order, int32_t T, int32_t G,
+               const float *scale, const float *bias, void *C, int32_t out_type,
+               int64_t M, int64_t N, int64_t K, void *stream);
 
 /* Explicit transpose At[k][m] = A[m][k] (fp16), the "explicit transpose"
  * variant of the tile-wise slides.  M % 8 == 0, K % 8 == 0. */

@@ -42,7 +42,7 @@ from .pack import (  # noqa: F401
     ref_tw_structure,
     ref_tw_pack,
     ref_tw_unpack,
-    TW_ROW_ALIGN,
+    TW_ROW_ALIGN_BYTES,
 )
 from .bounds import (  # noqa: F401
     loose_ok,

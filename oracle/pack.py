@@ -24,8 +24,8 @@ The reading adopted here:
 * a tile's kept columns are those with a nonzero in the tile, its kept rows
   the rows with a nonzero among the tile's columns, both ascending;
 * the block V_t is stored [N_t x K_t] (K contiguous), each row padded with
-  zeros to a multiple of ``TW_ROW_ALIGN`` elements so rows start 16-byte
-  aligned; ``v_ptr`` counts padded elements;
+  zeros to a multiple of ``TW_ROW_ALIGN_BYTES`` bytes (8 fp16 or 16 int8
+  elements) so rows start 16-byte aligned; ``v_ptr`` counts padded elements;
 * ``v_ptr``, ``k_ptr``, ``n_ptr`` are [T+1] prefix sums;
 * ``tile_order`` lists tiles heaviest first (K_t * N_t descending, ties to the
   lower t): the longest-processing-time order used to schedule the grouped
@@ -36,7 +36,7 @@ from __future__ import annotations
 
 import numpy as np
 
-TW_ROW_ALIGN = 8
+TW_ROW_ALIGN_BYTES = 16
 
 
 def _is_nonzero(W):
@@ -156,7 +156,7 @@ def ref_tw_pack(Wp, G):
     blocks, oks, ons, work = [], [], [], []
     for t, (rows, cols) in enumerate(struct):
         kt, nt = len(rows), len(cols)
-        ld = _round_up(kt, TW_ROW_ALIGN)
+        ld = _round_up(kt, TW_ROW_ALIGN_BYTES // Wp.dtype.itemsize)
         blk = np.zeros((nt, ld), dtype=Wp.dtype)
         if kt and nt:
             blk[:, :kt] = Wp[np.ix_(rows, t * G + cols)].T

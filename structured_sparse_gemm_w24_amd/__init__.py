@@ -26,6 +26,8 @@ from ._lib import (  # noqa: F401
     tw_pack_query,
     tw_pack_f16,
     tw_unpack_f16,
+    tw_pack_i8,
+    tw_unpack_i8,
     dense_gemm_f16,
     dense_gemm_i8,
     dense_gemm_i8_out,
@@ -38,6 +40,7 @@ from ._lib import (  # noqa: F401
     SSG_OUT_I8,
     tw_gemm_f16,
     tw_gemm_f16_ex,
+    tw_gemm_i8,
     tw_gemm_f16_streams,
     SSG_TW_OUT_T,
     SSG_TW_A_ROWMAJOR,

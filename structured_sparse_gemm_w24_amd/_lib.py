@@ -49,6 +49,9 @@ SIGNATURES = {
     "tw_pack_query": [_P, _I64, _I64, _I32, ct.POINTER(TwSizes)],
     "tw_pack_f16": [_P, _I64, _I64, _I32, ct.POINTER(TwSizes), _P, _P, _P, _P, _P, _P, _P],
     "tw_unpack_f16": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _P],
+    "tw_pack_query_i8": [_P, _I64, _I64, _I32, ct.POINTER(TwSizes)],
+    "tw_pack_i8": [_P, _I64, _I64, _I32, ct.POINTER(TwSizes), _P, _P, _P, _P, _P, _P, _P],
+    "tw_unpack_i8": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _P],
     "dense_gemm_f16": [_P, _P, _P, _I64, _I64, _I64, _P],
     "dense_gemm_i8": [_P, _P, _P, _P, _I64, _I64, _I64, _P],
     "w24_gemm_f16": [_P, _P, _P, _P, _I64, _I64, _I64, _P],
@@ -56,6 +59,7 @@ SIGNATURES = {
     "dense_gemm_i8_out": [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P],
     "w24_gemm_i8_out": [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P],
     "tw_gemm_f16": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _I64, _I64, _I64, _P],
+    "tw_gemm_i8": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _I32, _I64, _I64, _I64, _P],
     "tw_gemm_f16_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I64, _I64, _I64, _P],
     "ssg_transpose_f16": [_P, _P, _I64, _I64, _P],
     "ssg_device_arch": [ct.c_char_p, _I64],
@@ -175,38 +179,65 @@ class TwPacked:
         return TwPacked(self.K, self.N, self.G, self.T, *[conv(a) for a in self.arrays().values()])
 
 
+def _tw_fns(dtype):
+    dt = np.dtype(dtype)
+    if dt == np.float16:
+        return np.float16, "tw_pack_query", "tw_pack_f16", "tw_unpack_f16"
+    if dt == np.int8:
+        return np.int8, "tw_pack_query_i8", "tw_pack_i8", "tw_unpack_i8"
+    raise TypeError(f"tile-wise packing takes float16 or int8, got {dt}")
+
+
 def tw_pack_query(W, G):
-    W = _host(W, np.float16, 2)
+    dt, q, _, _ = _tw_fns(np.asarray(W).dtype)
+    W = _host(W, dt, 2)
     K, N = W.shape
     sz = TwSizes()
-    _check(load().tw_pack_query(_np_ptr(W), K, N, G, ct.byref(sz)))
+    _check(getattr(load(), q)(_np_ptr(W), K, N, G, ct.byref(sz)))
     return dict(T=sz.T, sum_kt=sz.sum_kt, sum_nt=sz.sum_nt, vals_elems=sz.vals_elems)
 
 
-def tw_pack_f16(W, G):
-    """W [K, N] float16 -> TwPacked (host arrays)."""
-    W = _host(W, np.float16, 2)
+def _tw_pack(W, G, dt, q, pk):
+    W = _host(W, dt, 2)
     K, N = W.shape
     sz = TwSizes()
-    _check(load().tw_pack_query(_np_ptr(W), K, N, G, ct.byref(sz)))
-    vals = np.empty(sz.vals_elems, np.float16)
+    _check(getattr(load(), q)(_np_ptr(W), K, N, G, ct.byref(sz)))
+    vals = np.empty(sz.vals_elems, dt)
     ok = np.empty(sz.sum_kt, np.int32)
     on = np.empty(sz.sum_nt, np.int32)
     vp = np.empty(sz.T + 1, np.int32)
     kp = np.empty(sz.T + 1, np.int32)
     np_ = np.empty(sz.T + 1, np.int32)
     order = np.empty(sz.T, np.int32)
-    _check(load().tw_pack_f16(_np_ptr(W), K, N, G, ct.byref(sz), _np_ptr(vals), _np_ptr(ok), _np_ptr(on),
-                              _np_ptr(vp), _np_ptr(kp), _np_ptr(np_), _np_ptr(order)))
+    _check(getattr(load(), pk)(_np_ptr(W), K, N, G, ct.byref(sz), _np_ptr(vals), _np_ptr(ok), _np_ptr(on),
+                               _np_ptr(vp), _np_ptr(kp), _np_ptr(np_), _np_ptr(order)))
     return TwPacked(K, N, G, int(sz.T), vals, ok, on, vp, kp, np_, order)
 
 
-def tw_unpack_f16(p: TwPacked):
-    W = np.empty((p.K, p.N), np.float16)
-    arrs = [_host(p.vals, np.float16), _host(p.offset_k, np.int32), _host(p.offset_n, np.int32),
+def tw_pack_f16(W, G):
+    """W [K, N] float16 -> TwPacked (host arrays)."""
+    return _tw_pack(W, G, np.float16, "tw_pack_query", "tw_pack_f16")
+
+
+def tw_pack_i8(W, G):
+    """W [K, N] int8 -> TwPacked (host arrays, int8 values, rows padded to 16)."""
+    return _tw_pack(W, G, np.int8, "tw_pack_query_i8", "tw_pack_i8")
+
+
+def _tw_unpack(p: TwPacked, dt, fn):
+    W = np.empty((p.K, p.N), dt)
+    arrs = [_host(p.vals, dt), _host(p.offset_k, np.int32), _host(p.offset_n, np.int32),
             _host(p.v_ptr, np.int32), _host(p.k_ptr, np.int32), _host(p.n_ptr, np.int32)]
-    _check(load().tw_unpack_f16(*[_np_ptr(a) for a in arrs], p.K, p.N, p.G, _np_ptr(W)))
+    _check(getattr(load(), fn)(*[_np_ptr(a) for a in arrs], p.K, p.N, p.G, _np_ptr(W)))
     return W
+
+
+def tw_unpack_f16(p: TwPacked):
+    return _tw_unpack(p, np.float16, "tw_unpack_f16")
+
+
+def tw_unpack_i8(p: TwPacked):
+    return _tw_unpack(p, np.int8, "tw_unpack_i8")
 
 
 # ---------------------------------------------------------------- device side
@@ -370,6 +401,29 @@ def tw_gemm_f16(At, packed: TwPacked, out=None):
     _check(load().tw_gemm_f16(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
                               _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]),
                               _ptr(arrs["tile_order"]), packed.T, packed.G, _ptr(C), M, packed.N, K, _stream(At)))
+    return C
+
+
+def tw_gemm_i8(At, packed: TwPacked, scale, bias=None, out_type="f16", out=None):
+    """int8 tile-wise GEMM; At [K, M] int8 (K-major A), packed int8 tiles on the device;
+    y = float(acc) * scale[n] (+ bias[n]) stored as out_type ("f32", "f16", "i8"; "i32"
+    writes the raw accumulators and takes no scale or bias)."""
+    torch = _torch()
+    K, M = At.shape
+    if K != packed.K:
+        raise ValueError(f"At has K={K}, packed weight has K={packed.K}")
+    _dev(At, torch.int8, (K, M), "At")
+    arrs = packed.arrays()
+    _dev(arrs["vals"], torch.int8, None, "vals")
+    for key in ("offset_k", "offset_n", "v_ptr", "k_ptr", "n_ptr", "tile_order"):
+        _dev(arrs[key], torch.int32, None, key)
+    code, dt = _out_kind(out_type)
+    _epilogue_args(packed.N, scale, bias)
+    C = _out(out, (M, packed.N), dt, At)
+    _check(load().tw_gemm_i8(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
+                             _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]), _ptr(arrs["tile_order"]),
+                             packed.T, packed.G, _ptr(scale), _ptr(bias), _ptr(C), code, M, packed.N, K,
+                             _stream(At)))
     return C
 
 

@@ -207,6 +207,36 @@ SSG_API int tw_gemm_f16_ex(const void *At, const void *vals, const int32_t *offs
                   t_count, flags, C, M, N, K, stream);
 }
 
+SSG_API int tw_gemm_i8(const int8_t *At, const int8_t *vals, const int32_t *offset_k, const int32_t *offset_n,
+                       const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr, const int32_t *tile_order,
+                       int32_t T, int32_t G, const float *scale, const float *bias, void *C, int32_t out_type,
+                       int64_t M, int64_t N, int64_t K, void *stream) {
+    const char *fn = "tw_gemm_i8";
+    if (M < 0 || N <= 0 || K <= 0 || !fits_int(M) || !fits_int(N) || !fits_int(K))
+        return ssg::fail(SSG_EINVAL, "%s: bad shape M=%lld N=%lld K=%lld", fn, (long long)M, (long long)N,
+                         (long long)K);
+    if (G <= 0 || G % 16 || G > 128)
+        return ssg::fail(SSG_EINVAL, "%s: G=%d must be a positive multiple of 16, at most 128", fn, G);
+    if (N % G) return ssg::fail(SSG_EINVAL, "%s: N=%lld must be a multiple of G=%d", fn, (long long)N, G);
+    if (T != N / G) return ssg::fail(SSG_EINVAL, "%s: T=%d must equal N/G=%lld", fn, T, (long long)(N / G));
+    if (M % 16) return ssg::fail(SSG_EINVAL, "%s: M=%lld must be a multiple of 16", fn, (long long)M);
+    if (!fits_int((M + 127) / 128 * int64_t(T))) return ssg::fail(SSG_EINVAL, "%s: too many work items", fn);
+    int rc = check_i8_epilogue(fn, scale, bias, out_type);
+    if (rc) return rc;
+    if (M == 0) {
+        ssg::clear_error();
+        return SSG_OK;
+    }
+    if (!At || !C || !v_ptr || !k_ptr || !n_ptr || !tile_order || !offset_k || !offset_n || !vals)
+        return ssg::fail(SSG_EINVAL, "%s: null pointer", fn);
+    if (!ssg::aligned16(At) || !ssg::aligned16(C) || !ssg::aligned16(vals))
+        return ssg::fail(SSG_EINVAL, "%s: At, vals and C must be 16-byte aligned", fn);
+    if ((rc = check_device())) return rc;
+    return launched(ssg::launch_tw_i8(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G, scale,
+                                      bias, C, out_type, int(M), int(N), hipStream_t(stream)),
+                    fn);
+}
+
 SSG_API int ssg_transpose_f16(const void *A, void *At, int64_t M, int64_t K, void *stream) {
     const char *fn = "ssg_transpose_f16";
     if (M < 0 || K <= 0 || !fits_int(M) || !fits_int(K) || M % 8 || K % 8)

@@ -25,6 +25,12 @@ hipError_t launch_tw_f16(const void *At, const void *vals, const int32_t *offset
                          const int32_t *n_ptr, const int32_t *tile_order, int t_first, int t_count,
                          int G, bool out_t, bool a_rowmajor, void *C, int M, int N, int K,
                          hipStream_t st);
+// int8 tile-wise GEMM (K-major int8 At, condensed int8 tiles), epilogue as
+// the int8 GEMMs' OUT_* kinds.
+hipError_t launch_tw_i8(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
+                        const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
+                        const int32_t *tile_order, int T, int G, const float *scale, const float *bias,
+                        void *C, int out, int M, int N, hipStream_t st);
 hipError_t launch_transpose_f16(const void *A, void *At, int M, int K, hipStream_t st);
 
 }  // namespace ssg

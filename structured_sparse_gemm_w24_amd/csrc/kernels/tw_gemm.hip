@@ -41,6 +41,7 @@
 // rows in one L2.
 #include "common.h"
 #include "launch.h"
+#include "tw_common.h"
 
 namespace ssg {
 
@@ -49,31 +50,7 @@ __device__ __attribute__((aligned(256))) uint16_t g_tw_zero[128];
 
 namespace {
 
-typedef __attribute__((address_space(3))) void *tw_lds_ptr;
-
-__device__ __forceinline__ void tw_dma16(const void *g, uint8_t *wave_base) {
-    __builtin_amdgcn_global_load_lds(g, (tw_lds_ptr)wave_base, 16, 0, 0);
-}
-
-// Output stores are nontemporal: C is written once and not read back by this
-// kernel, and streaming it past L2 avoids write-backs at the kernel's end
-// (measured 12-17 % faster on the BERT FFN shapes).
-__device__ __forceinline__ void tw_store16(void *p, u32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-}
-
-// Wait until at most n of this wave's direct-to-LDS loads are outstanding and
-// its LDS reads have completed, then synchronise the workgroup.
-__device__ __forceinline__ void tw_wait_barrier(int n) {
-    switch (n) {
-#define TW_WAIT(N) \
-    case N: asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-        TW_WAIT(1) TW_WAIT(2) TW_WAIT(3) TW_WAIT(4) TW_WAIT(5) TW_WAIT(6) TW_WAIT(7)
-        TW_WAIT(8) TW_WAIT(9) TW_WAIT(10) TW_WAIT(11) TW_WAIT(12)
-#undef TW_WAIT
-        default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    }
-}
+using namespace tw_detail;
 
 // Column operand of two k32 steps: four transposing reads at byte offsets
 // 0, 1024 (k + 4), 8192 (k + 32) and 9216 (k + 36) from addr, waited for in

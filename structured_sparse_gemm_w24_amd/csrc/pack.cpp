@@ -117,7 +117,19 @@ struct TileStruct {
     std::vector<std::vector<int32_t>> rows, cols;
 };
 
-int tw_scan(const uint16_t *W, int64_t K, int64_t N, int32_t G, TileStruct &ts, tw_sizes &sz) {
+// Condensed rows are padded to 16 bytes (8 fp16 or 16 int8 elements) so that
+// every row of a tile starts 16-byte aligned.
+template <typename T>
+constexpr int64_t tw_row_align() {
+    return 16 / int64_t(sizeof(T));
+}
+template <typename T>
+int64_t tw_ld(int64_t kt) {
+    return (kt + tw_row_align<T>() - 1) / tw_row_align<T>() * tw_row_align<T>();
+}
+
+template <typename E>
+int tw_scan(const E *W, int64_t K, int64_t N, int32_t G, TileStruct &ts, tw_sizes &sz) {
     if (!W) return ssg::fail(SSG_EINVAL, "tw_pack: null W");
     if (K <= 0 || N <= 0 || G <= 0)
         return ssg::fail(SSG_EINVAL, "tw_pack: K=%lld N=%lld G=%d must be positive", (long long)K,
@@ -127,7 +139,7 @@ int tw_scan(const uint16_t *W, int64_t K, int64_t N, int32_t G, TileStruct &ts, 
     const int64_t T = (N + G - 1) / G;
     std::vector<uint8_t> rowmark(size_t(T) * size_t(K), 0), colmark(size_t(N), 0);
     for (int64_t k = 0; k < K; ++k) {
-        const uint16_t *r = W + k * N;
+        const E *r = W + k * N;
         for (int64_t c = 0; c < N; ++c) {
             if (nonzero(r[c])) {
                 colmark[c] = 1;
@@ -147,7 +159,7 @@ int tw_scan(const uint16_t *W, int64_t K, int64_t N, int32_t G, TileStruct &ts, 
         const int64_t kt = int64_t(ts.rows[t].size()), nt = int64_t(ts.cols[t].size());
         skt += kt;
         snt += nt;
-        sv += nt * ((kt + 7) / 8 * 8);
+        sv += nt * tw_ld<E>(kt);
     }
     if (sv >= (int64_t(1) << 31) || skt >= (int64_t(1) << 31))
         return ssg::fail(SSG_EINVAL, "tw_pack: packed sizes exceed int32 range");
@@ -155,6 +167,102 @@ int tw_scan(const uint16_t *W, int64_t K, int64_t N, int32_t G, TileStruct &ts, 
     sz.sum_kt = skt;
     sz.sum_nt = snt;
     sz.vals_elems = sv;
+    return SSG_OK;
+}
+
+
+template <typename T>
+int tw_pack(const char *fn, const T *W, int64_t K, int64_t N, int32_t G, const tw_sizes *cap, T *vals,
+            int32_t *offset_k, int32_t *offset_n, int32_t *v_ptr, int32_t *k_ptr, int32_t *n_ptr,
+            int32_t *tile_order) {
+    if (!cap || !v_ptr || !k_ptr || !n_ptr || !tile_order) return ssg::fail(SSG_EINVAL, "%s: null pointer", fn);
+    TileStruct ts;
+    tw_sizes sz{};
+    int rc = tw_scan(W, K, N, G, ts, sz);
+    if (rc) return rc;
+    if (cap->T < sz.T || cap->sum_kt < sz.sum_kt || cap->sum_nt < sz.sum_nt || cap->vals_elems < sz.vals_elems)
+        return ssg::fail(SSG_ENOSPC,
+                         "%s: capacity (T=%lld kt=%lld nt=%lld vals=%lld) < needed "
+                         "(T=%lld kt=%lld nt=%lld vals=%lld)",
+                         fn, (long long)cap->T, (long long)cap->sum_kt, (long long)cap->sum_nt,
+                         (long long)cap->vals_elems, (long long)sz.T, (long long)sz.sum_kt, (long long)sz.sum_nt,
+                         (long long)sz.vals_elems);
+    if ((sz.sum_kt && !offset_k) || (sz.sum_nt && !offset_n) || (sz.vals_elems && !vals))
+        return ssg::fail(SSG_EINVAL, "%s: null output array", fn);
+    const int64_t T_ = sz.T;
+    std::vector<int64_t> work(static_cast<size_t>(T_));
+    int64_t vp = 0, kp = 0, np = 0;
+    v_ptr[0] = k_ptr[0] = n_ptr[0] = 0;
+    for (int64_t t = 0; t < T_; ++t) {
+        const auto &rows = ts.rows[t];
+        const auto &cols = ts.cols[t];
+        const int64_t kt = int64_t(rows.size()), nt = int64_t(cols.size());
+        const int64_t ld = tw_ld<T>(kt);
+        for (int64_t j = 0; j < nt; ++j) {
+            T *dst = vals + vp + j * ld;
+            const int64_t c = t * int64_t(G) + cols[j];
+            for (int64_t kk = 0; kk < kt; ++kk) dst[kk] = canon(W[int64_t(rows[kk]) * N + c]);
+            for (int64_t kk = kt; kk < ld; ++kk) dst[kk] = T(0);
+        }
+        std::copy(rows.begin(), rows.end(), offset_k + kp);
+        std::copy(cols.begin(), cols.end(), offset_n + np);
+        vp += nt * ld;
+        kp += kt;
+        np += nt;
+        v_ptr[t + 1] = int32_t(vp);
+        k_ptr[t + 1] = int32_t(kp);
+        n_ptr[t + 1] = int32_t(np);
+        work[t] = kt * nt;
+    }
+    std::vector<int32_t> order(static_cast<size_t>(T_));
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return work[a] > work[b]; });
+    std::copy(order.begin(), order.end(), tile_order);
+    ssg::clear_error();
+    return SSG_OK;
+}
+
+template <typename T>
+int tw_unpack(const char *fn, const T *vals, const int32_t *offset_k, const int32_t *offset_n, const int32_t *v_ptr,
+              const int32_t *k_ptr, const int32_t *n_ptr, int64_t K, int64_t N, int32_t G, T *W) {
+    if (!W || !v_ptr || !k_ptr || !n_ptr) return ssg::fail(SSG_EINVAL, "%s: null pointer", fn);
+    if (K <= 0 || N <= 0 || G <= 0) return ssg::fail(SSG_EINVAL, "%s: bad shape", fn);
+    const int64_t T_ = (N + G - 1) / G;
+    for (int64_t t = 0; t < T_; ++t) {
+        const int64_t kt = k_ptr[t + 1] - k_ptr[t], nt = n_ptr[t + 1] - n_ptr[t];
+        const int64_t g = std::min<int64_t>(G, N - t * G);
+        if (kt < 0 || nt < 0 || v_ptr[t + 1] - v_ptr[t] != nt * tw_ld<T>(kt))
+            return ssg::fail(SSG_EINVAL, "%s: inconsistent pointers at tile %lld", fn, (long long)t);
+        for (int64_t kk = 0; kk < kt; ++kk)
+            if (offset_k[k_ptr[t] + kk] < 0 || offset_k[k_ptr[t] + kk] >= K)
+                return ssg::fail(SSG_EINVAL, "%s: offset_k out of range in tile %lld", fn, (long long)t);
+        for (int64_t j = 0; j < nt; ++j)
+            if (offset_n[n_ptr[t] + j] < 0 || offset_n[n_ptr[t] + j] >= g)
+                return ssg::fail(SSG_EINVAL, "%s: offset_n out of range in tile %lld", fn, (long long)t);
+    }
+    std::memset(W, 0, sizeof(T) * size_t(K) * size_t(N));
+    for (int64_t t = 0; t < T_; ++t) {
+        const int64_t kt = k_ptr[t + 1] - k_ptr[t], nt = n_ptr[t + 1] - n_ptr[t];
+        const int64_t ld = tw_ld<T>(kt);
+        for (int64_t j = 0; j < nt; ++j) {
+            const int64_t c = t * int64_t(G) + offset_n[n_ptr[t] + j];
+            const T *src = vals + v_ptr[t] + j * ld;
+            for (int64_t kk = 0; kk < kt; ++kk) W[int64_t(offset_k[k_ptr[t] + kk]) * N + c] = canon(src[kk]);
+        }
+    }
+    ssg::clear_error();
+    return SSG_OK;
+}
+
+template <typename T>
+int tw_query(const T *W, int64_t K, int64_t N, int32_t G, tw_sizes *out) {
+    if (!out) return ssg::fail(SSG_EINVAL, "tw_pack_query: null out");
+    TileStruct ts;
+    tw_sizes sz{};
+    int rc = tw_scan(W, K, N, G, ts, sz);
+    if (rc) return rc;
+    *out = sz;
+    ssg::clear_error();
     return SSG_OK;
 }
 
@@ -177,96 +285,32 @@ SSG_API int w24_unpack_i8(const int8_t *vals, const uint32_t *meta, int64_t K, i
 }
 
 SSG_API int tw_pack_query(const uint16_t *W, int64_t K, int64_t N, int32_t G, tw_sizes *out) {
-    if (!out) return ssg::fail(SSG_EINVAL, "tw_pack_query: null out");
-    TileStruct ts;
-    tw_sizes sz{};
-    int rc = tw_scan(W, K, N, G, ts, sz);
-    if (rc) return rc;
-    *out = sz;
-    ssg::clear_error();
-    return SSG_OK;
+    return tw_query(W, K, N, G, out);
+}
+
+SSG_API int tw_pack_query_i8(const int8_t *W, int64_t K, int64_t N, int32_t G, tw_sizes *out) {
+    return tw_query(W, K, N, G, out);
 }
 
 SSG_API int tw_pack_f16(const uint16_t *W, int64_t K, int64_t N, int32_t G, const tw_sizes *cap,
                         uint16_t *vals, int32_t *offset_k, int32_t *offset_n, int32_t *v_ptr,
                         int32_t *k_ptr, int32_t *n_ptr, int32_t *tile_order) {
-    if (!cap || !v_ptr || !k_ptr || !n_ptr || !tile_order)
-        return ssg::fail(SSG_EINVAL, "tw_pack_f16: null pointer");
-    TileStruct ts;
-    tw_sizes sz{};
-    int rc = tw_scan(W, K, N, G, ts, sz);
-    if (rc) return rc;
-    if (cap->T < sz.T || cap->sum_kt < sz.sum_kt || cap->sum_nt < sz.sum_nt ||
-        cap->vals_elems < sz.vals_elems)
-        return ssg::fail(SSG_ENOSPC,
-                         "tw_pack_f16: capacity (T=%lld kt=%lld nt=%lld vals=%lld) < needed "
-                         "(T=%lld kt=%lld nt=%lld vals=%lld)",
-                         (long long)cap->T, (long long)cap->sum_kt, (long long)cap->sum_nt,
-                         (long long)cap->vals_elems, (long long)sz.T, (long long)sz.sum_kt,
-                         (long long)sz.sum_nt, (long long)sz.vals_elems);
-    if ((sz.sum_kt && !offset_k) || (sz.sum_nt && !offset_n) || (sz.vals_elems && !vals))
-        return ssg::fail(SSG_EINVAL, "tw_pack_f16: null output array");
-    const int64_t T = sz.T;
-    std::vector<int64_t> work(static_cast<size_t>(T));
-    int64_t vp = 0, kp = 0, np = 0;
-    v_ptr[0] = k_ptr[0] = n_ptr[0] = 0;
-    for (int64_t t = 0; t < T; ++t) {
-        const auto &rows = ts.rows[t];
-        const auto &cols = ts.cols[t];
-        const int64_t kt = int64_t(rows.size()), nt = int64_t(cols.size());
-        const int64_t ld = (kt + 7) / 8 * 8;
-        for (int64_t j = 0; j < nt; ++j) {
-            uint16_t *dst = vals + vp + j * ld;
-            const int64_t c = t * int64_t(G) + cols[j];
-            for (int64_t kk = 0; kk < kt; ++kk) dst[kk] = canon(W[int64_t(rows[kk]) * N + c]);
-            for (int64_t kk = kt; kk < ld; ++kk) dst[kk] = 0;
-        }
-        std::copy(rows.begin(), rows.end(), offset_k + kp);
-        std::copy(cols.begin(), cols.end(), offset_n + np);
-        vp += nt * ld;
-        kp += kt;
-        np += nt;
-        v_ptr[t + 1] = int32_t(vp);
-        k_ptr[t + 1] = int32_t(kp);
-        n_ptr[t + 1] = int32_t(np);
-        work[t] = kt * nt;
-    }
-    std::vector<int32_t> order(static_cast<size_t>(T));
-    std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return work[a] > work[b]; });
-    std::copy(order.begin(), order.end(), tile_order);
-    ssg::clear_error();
-    return SSG_OK;
+    return tw_pack("tw_pack_f16", W, K, N, G, cap, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order);
+}
+
+SSG_API int tw_pack_i8(const int8_t *W, int64_t K, int64_t N, int32_t G, const tw_sizes *cap, int8_t *vals,
+                       int32_t *offset_k, int32_t *offset_n, int32_t *v_ptr, int32_t *k_ptr, int32_t *n_ptr,
+                       int32_t *tile_order) {
+    return tw_pack("tw_pack_i8", W, K, N, G, cap, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order);
 }
 
 SSG_API int tw_unpack_f16(const uint16_t *vals, const int32_t *offset_k, const int32_t *offset_n,
                           const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
                           int64_t K, int64_t N, int32_t G, uint16_t *W) {
-    if (!W || !v_ptr || !k_ptr || !n_ptr) return ssg::fail(SSG_EINVAL, "tw_unpack_f16: null pointer");
-    if (K <= 0 || N <= 0 || G <= 0) return ssg::fail(SSG_EINVAL, "tw_unpack_f16: bad shape");
-    const int64_t T = (N + G - 1) / G;
-    for (int64_t t = 0; t < T; ++t) {
-        const int64_t kt = k_ptr[t + 1] - k_ptr[t], nt = n_ptr[t + 1] - n_ptr[t];
-        const int64_t g = std::min<int64_t>(G, N - t * G);
-        if (kt < 0 || nt < 0 || v_ptr[t + 1] - v_ptr[t] != nt * ((kt + 7) / 8 * 8))
-            return ssg::fail(SSG_EINVAL, "tw_unpack_f16: inconsistent pointers at tile %lld", (long long)t);
-        for (int64_t kk = 0; kk < kt; ++kk)
-            if (offset_k[k_ptr[t] + kk] < 0 || offset_k[k_ptr[t] + kk] >= K)
-                return ssg::fail(SSG_EINVAL, "tw_unpack_f16: offset_k out of range in tile %lld", (long long)t);
-        for (int64_t j = 0; j < nt; ++j)
-            if (offset_n[n_ptr[t] + j] < 0 || offset_n[n_ptr[t] + j] >= g)
-                return ssg::fail(SSG_EINVAL, "tw_unpack_f16: offset_n out of range in tile %lld", (long long)t);
-    }
-    std::memset(W, 0, sizeof(uint16_t) * size_t(K) * size_t(N));
-    for (int64_t t = 0; t < T; ++t) {
-        const int64_t kt = k_ptr[t + 1] - k_ptr[t], nt = n_ptr[t + 1] - n_ptr[t];
-        const int64_t ld = (kt + 7) / 8 * 8;
-        for (int64_t j = 0; j < nt; ++j) {
-            const int64_t c = t * int64_t(G) + offset_n[n_ptr[t] + j];
-            const uint16_t *src = vals + v_ptr[t] + j * ld;
-            for (int64_t kk = 0; kk < kt; ++kk) W[int64_t(offset_k[k_ptr[t] + kk]) * N + c] = canon(src[kk]);
-        }
-    }
-    ssg::clear_error();
-    return SSG_OK;
+    return tw_unpack("tw_unpack_f16", vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, K, N, G, W);
+}
+
+SSG_API int tw_unpack_i8(const int8_t *vals, const int32_t *offset_k, const int32_t *offset_n, const int32_t *v_ptr,
+                         const int32_t *k_ptr, const int32_t *n_ptr, int64_t K, int64_t N, int32_t G, int8_t *W) {
+    return tw_unpack("tw_unpack_i8", vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, K, N, G, W);
 }

@@ -26,7 +26,8 @@ def test_header_declares_the_path():
     assert {"w24_pack_f16", "w24_pack_i8", "w24_unpack_f16", "w24_unpack_i8", "tw_pack_query",
             "tw_pack_f16", "tw_unpack_f16", "dense_gemm_f16", "dense_gemm_i8", "w24_gemm_f16",
             "w24_gemm_i8", "tw_gemm_f16", "ssg_transpose_f16", "ssg_last_error",
-            "dense_gemm_i8_out", "w24_gemm_i8_out", "tw_gemm_f16_ex"} <= names
+            "dense_gemm_i8_out", "w24_gemm_i8_out", "tw_gemm_f16_ex", "tw_pack_i8", "tw_unpack_i8",
+            "tw_pack_query_i8", "tw_gemm_i8"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -75,6 +76,8 @@ def has_device(lib):
     (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 1, 2, 0, _p(16), 8, 32, 64, None), "tile range"),
     (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 0, 0, _p(16), 8, 32, 64, None), "tile range"),
     (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 2, 4, _p(16), 8, 32, 64, None), "unknown flags"),
+    (lambda r: r.tw_gemm_i8(*[_p(16)] * 8, 2, 16, _p(16), None, _p(16), 2, 24, 32, 64, None), "multiple of 16"),
+    (lambda r: r.tw_gemm_i8(*[_p(16)] * 8, 2, 16, None, None, _p(16), 2, 32, 32, 64, None), "needs scale"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 24, _p(16), 8, 48, 64, None), "G=24"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 256, _p(16), 8, 512, 64, None), "at most 128"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 3, 16, _p(16), 8, 32, 64, None), "T=3"),

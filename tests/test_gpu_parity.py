@@ -344,6 +344,53 @@ def test_tw_indexed_oracle_agrees(lib, gpu):
     assert oracle.loose_err(C, ref) <= 1e-2
 
 
+# ---------------------------------------------------------------- int8 tile-wise
+TW8_SHAPES = [(16, 64, 32, 16, [0.5, 1.0]), (144, 200, 96, 32, [0.3, 0.0, 0.9]),
+              (256, 768, 384, 128, [0.1, 0.25, 0.4]), (48, 1000, 64, 64, 0.6), (208, 96, 128, 128, 1.0)]
+
+
+def run_tw_i8(lib, A, Wp, G, scale, bias, out):
+    packed = lib.tw_pack_i8(Wp, G).to("cuda")
+    At = T(np.ascontiguousarray(A.T))
+    return H(lib.tw_gemm_i8(At, packed, None if scale is None else T(scale), None if bias is None else T(bias),
+                            out_type=out))
+
+
+@pytest.mark.parametrize("out", ["i32", "f32", "f16", "i8"])
+@pytest.mark.parametrize("M,K,N,G,d", TW8_SHAPES)
+def test_tw_i8_bit_exact(lib, gpu, M, K, N, G, d, out):
+    rng = np.random.default_rng(M + 5 * K + G)
+    case = wl.random_tw_i8(rng, M, K, N, G, d)
+    scale = {"i32": None, "f32": case["scale"], "f16": case["scale"] * np.float32(20.0),
+             "i8": rng.uniform(2e-4, 2e-3, size=N).astype(np.float32)}[out]
+    bias = None if out == "i32" else rng.normal(0, 3.0, size=N).astype(np.float32)
+    C = run_tw_i8(lib, case["A"], case["Wp"], G, scale, bias, out)
+    ref = oracle.ref_gemm_i8_out(case["A"], case["Wp"], scale, bias, out)
+    bad = np.flatnonzero(_bits(C) != _bits(ref))
+    assert bad.size == 0, f"{bad.size} mismatches, first at {np.unravel_index(bad[0], C.shape)}"
+
+
+def test_tw_i8_no_bias_pruned_columns(lib, gpu):
+    # without bias a pruned column is the epilogue of a zero accumulator: +0 for
+    # positive scales
+    rng = np.random.default_rng(40)
+    case = wl.random_tw_i8(rng, 64, 256, 256, 128, [0.2, 0.5])
+    C = run_tw_i8(lib, case["A"], case["Wp"], 128, case["scale"], None, "f32")
+    ref = oracle.ref_gemm_i8_out(case["A"], case["Wp"], case["scale"], None, "f32")
+    assert np.array_equal(_bits(C), _bits(ref))
+
+
+@pytest.mark.parametrize("out", ["f16", "i8"])
+def test_tw_i8_workload(lib, gpu, out):
+    c = wl.make_cfg3_i8()
+    rng = np.random.default_rng(41)
+    scale = c["scale"] if out == "f16" else (c["scale"] * np.float32(0.05))
+    bias = rng.normal(0, 2.0, size=c["N"]).astype(np.float32)
+    C = run_tw_i8(lib, c["A"], c["Wp"], c["G"], scale, bias, out)
+    ref = oracle.ref_gemm_i8_out(c["A"], c["Wp"], scale, bias, out)
+    assert np.array_equal(_bits(C), _bits(ref))
+
+
 # ---------------------------------------------------------------- tile-wise: fused transpose, tile ranges, streams
 def _tw_setup(lib, A, Wp, G):
     packed = lib.tw_pack_f16(Wp, G).to("cuda")

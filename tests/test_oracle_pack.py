@@ -129,7 +129,8 @@ def _check_tw_invariants(Wp, G, packed):
             assert 0 <= ks[0] and ks[-1] < K
         if len(ns):
             assert 0 <= ns[0] and ns[-1] < min(G, N - t * G)
-        ld = oracle.TW_ROW_ALIGN * -(-len(ks) // oracle.TW_ROW_ALIGN)
+        align = 16 // packed["vals"].dtype.itemsize  # rows padded to 16 bytes
+        ld = align * -(-len(ks) // align)
         assert vp[t + 1] - vp[t] == len(ns) * ld
         # zero outside kept rows x kept columns
         win = Wp[:, t * G:(t + 1) * G].copy()

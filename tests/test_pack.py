@@ -101,6 +101,26 @@ def test_tw_pack_matches_oracle(lib, K, N, G, d):
     assert np.array_equal(lib.tw_unpack_f16(p).astype(np.float64), W.astype(np.float64))
 
 
+@pytest.mark.parametrize("K,N,G,d", [(64, 48, 16, [0.3, 1.0, 0.0]), (100, 40, 16, 0.5), (33, 10, 4, 0.4),
+                                     (768, 384, 128, [0.1, 0.4, 0.25])])
+def test_tw_pack_i8_matches_oracle(lib, K, N, G, d):
+    case = wl.random_tw_i8(np.random.default_rng(K + 2 * N), 1, K, N, G, d)
+    p = lib.tw_pack_i8(case["Wp"], G)
+    assert p.vals.dtype == np.int8
+    ref = oracle.ref_tw_pack(case["Wp"], G)
+    _tw_equal(p, ref)
+    # int8 rows are padded to 16 elements (16 bytes)
+    for t in range(p.T):
+        kt, nt = p.k_ptr[t + 1] - p.k_ptr[t], p.n_ptr[t + 1] - p.n_ptr[t]
+        assert p.v_ptr[t + 1] - p.v_ptr[t] == nt * (-(-kt // 16) * 16)
+    assert np.array_equal(lib.tw_unpack_i8(p), case["Wp"])
+
+
+def test_tw_pack_i8_workload(lib):
+    c = wl.make_cfg3_i8()
+    _tw_equal(lib.tw_pack_i8(c["Wp"], 128), oracle.ref_tw_pack(c["Wp"], 128))
+
+
 def test_tw_pack_full_configs(lib):
     c3 = wl.make_cfg3()
     _tw_equal(lib.tw_pack_f16(c3["Wp"], 128), oracle.ref_tw_pack(c3["Wp"], 128))

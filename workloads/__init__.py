@@ -20,6 +20,7 @@ from .gen import (  # noqa: F401
     make_cfg1,
     make_cfg2,
     make_cfg3,
+    make_cfg3_i8,
     make_cfg4,
     cfg5_layers,
     prune24_magnitude,
@@ -32,6 +33,7 @@ from .gen import (  # noqa: F401
     f32_scales,
     random_24_f16,
     random_24_i8,
+    random_tw_i8,
     random_tw_f16,
     exact_int_24_f16,
     exact_int_tw_f16,

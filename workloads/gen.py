@@ -160,6 +160,20 @@ def make_cfg3(seed=0):
                 A=A, W=W, Wp=prune_tilewise(W, G, d), densities=d)
 
 
+def make_cfg3_i8(seed=0):
+    """cfg3's shape, tiles and densities with the integer path's data (NEXT-3's
+    int8 tile-wise): A int8 U{-127..127}, W round(N(0,32)) clipped, tile-wise
+    pruned like cfg3, per-channel scales U(1e-3, 1e-2)."""
+    rng = np.random.default_rng(seed)
+    M, K, N, G = 32 * 128, 768, 3072, 128
+    A = i8_uniform(rng, (M, K))
+    W = i8_weights(rng, (K, N))
+    d = cfg3_densities(rng, N // G)
+    scale = f32_scales(rng, N)
+    return dict(name="cfg3_i8", kind="tw_i8", M=M, K=K, N=N, G=G,
+                A=A, W=W, Wp=prune_tilewise(W, G, d), densities=d, scale=scale)
+
+
 def make_cfg4(seed=0):
     rng = np.random.default_rng(seed)
     M, G = 16 * 384, 128
@@ -213,6 +227,12 @@ def random_24_f16(rng, M, K, N, std_a=1.0, std_w=0.02):
     A = f16_normal(rng, (M, K), std_a)
     W = f16_normal(rng, (K, N), std_w)
     return dict(A=A, W=W, Wp=prune24_magnitude(W))
+
+
+def random_tw_i8(rng, M, K, N, G, densities):
+    A = i8_uniform(rng, (M, K))
+    W = i8_weights(rng, (K, N))
+    return dict(A=A, W=W, Wp=prune_tilewise(W, G, densities), scale=f32_scales(rng, N))
 
 
 def random_24_i8(rng, M, K, N):
