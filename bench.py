@@ -548,7 +548,63 @@ def cfg5_stack(torch, ssg, perf, wl, dtype, timer, steps_gemm=20, passes=3, laye
                 by_shape=by_shape)
 
 
-WORKLOADS = ("cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg5stack", "cfg3_i8")
+def patterns(torch, ssg, perf, wl, timer, steps, warmup, emit):
+    """The pages' pattern comparison at the BERT-base FFN shape (M, K, N) =
+    (4096, 768, 3072), fp16, one input set (cache-warm): dense; 2:4; tile-wise
+    (G = 128) over a density sweep, with the critical density where it matches
+    dense; block-wise 64 x 64 (run by the tile-wise kernel with G = 64, since
+    a BW weight is a tile-wise weight of whole 64-row runs); element-wise
+    (unstructured) through torch's CSR sparse product in fp32, as the slides'
+    cuSparse baseline ran in fp32."""
+    rng = np.random.default_rng(0)
+    M, K, N = 4096, 768, 3072
+    A = wl.f16_normal(rng, (M, K))
+    W = wl.f16_normal(rng, (K, N), 0.02)
+    dev = torch.device("cuda")
+    A_d = torch.from_numpy(A).to(dev)
+    At = ssg.ssg_transpose_f16(A_d)
+    C = torch.empty((M, N), dtype=torch.float16, device=dev)
+    Wt = torch.from_numpy(np.ascontiguousarray(W.T)).to(dev)
+    t_dense = timer(lambda i: ssg.dense_gemm_f16(A_d, Wt, out=C), steps, warmup)
+    base = dict(shape=[M, K, N], t_dense_ms=t_dense, inputs="one set (cache-warm)")
+    vals, meta = ssg.w24_pack_f16(wl.prune24_magnitude(W))
+    v_d, m_d = torch.from_numpy(vals).to(dev), torch.from_numpy(meta.view(np.int32)).to(dev)
+    t = timer(lambda i: ssg.w24_gemm_f16(A_d, v_d, m_d, out=C), steps, warmup)
+    emit(dict(workload="patterns_2to4", density=0.5, t_ms=t, speedup_vs_dense=t_dense / t, **base))
+    sweep = []
+    for d in (0.1, 0.2, 0.3, 0.4, 0.5, 0.6, 0.7, 0.8, 0.9):
+        pk = ssg.tw_pack_f16(wl.prune_tilewise(W, 128, d), 128).to(dev)
+        t = timer(lambda i: ssg.tw_gemm_f16(At, pk, out=C), steps, warmup)
+        sweep.append((d, t_dense / t))
+        emit(dict(workload="patterns_tilewise_g128", density=d, t_ms=t, speedup_vs_dense=t_dense / t, **base))
+    crit = None
+    for (d0, s0), (d1, s1) in zip(sweep, sweep[1:]):
+        if s0 >= 1.0 > s1:
+            crit = d0 + (s0 - 1.0) * (d1 - d0) / (s0 - s1)
+    emit(dict(workload="patterns_tilewise_critical_density", critical_density=crit,
+              note="density at which the tile-wise kernel matches the dense kernel (linear interpolation)",
+              **base))
+    for d in (0.25, 0.5, 0.75):
+        pk = ssg.tw_pack_f16(wl.prune_blockwise(W, 64, d), 64).to(dev)
+        t = timer(lambda i: ssg.tw_gemm_f16(At, pk, out=C), steps, warmup)
+        emit(dict(workload="patterns_blockwise_64x64", density=d, t_ms=t, speedup_vs_dense=t_dense / t, **base))
+    A32 = A_d.float()
+    W32 = torch.from_numpy(W.astype(np.float32)).to(dev)
+    At32 = A32.t().contiguous()
+    t_dense32 = Timer(torch, graph=False)(lambda i: torch.matmul(A32, W32), steps, warmup)
+    for d in (0.37, 0.5):
+        Wp = wl.prune_elementwise(W, d)
+        S = torch.from_numpy(np.ascontiguousarray(Wp.T.astype(np.float32))).to(dev).to_sparse_csr()
+        try:
+            t = Timer(torch, graph=False)(lambda i: torch.sparse.mm(S, At32), steps, warmup)
+            emit(dict(workload="patterns_elementwise_csr_fp32", density=d, t_ms=t,
+                      speedup_vs_dense=t_dense / t, speedup_vs_dense_fp32=t_dense32 / t, t_dense_fp32_ms=t_dense32,
+                      timing="eager (library call)", **base))
+        except (RuntimeError, NotImplementedError) as e:
+            emit(dict(workload="patterns_elementwise_csr_fp32", density=d, error=str(e)[:200], **base))
+
+
+WORKLOADS = ("cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg5stack", "cfg3_i8", "patterns")
 
 
 def table(a, torch, ssg, perf, wl, timer):
@@ -597,6 +653,9 @@ def table(a, torch, ssg, perf, wl, timer):
                   tflops_nonzero=r["ops"] / r["t_sparse_ms"] / 1e9, gbs=r["bytes"] / r["t_sparse_ms"] / 1e6,
                   speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
                   speedup_vs_dense_incl_transpose=r["t_dense_ms"] / (r["t_sparse_ms"] + r["t_transpose_ms"])))
+        torch.cuda.empty_cache()
+    if "patterns" in want:
+        patterns(torch, ssg, perf, wl, timer, steps, warmup, emit)
         torch.cuda.empty_cache()
     if "cfg3_i8" in want:
         c = wl.make_cfg3_i8()

@@ -344,6 +344,19 @@ def test_tw_indexed_oracle_agrees(lib, gpu):
     assert oracle.loose_err(C, ref) <= 1e-2
 
 
+# ---------------------------------------------------------------- block-wise through the tile-wise kernel
+@pytest.mark.parametrize("d", [0.25, 0.5, 1.0])
+def test_blockwise_via_tilewise_kernel(lib, gpu, d):
+    # a 64x64 block-pruned weight is a tile-wise weight (G = 64) of whole 64-row runs
+    rng = np.random.default_rng(50)
+    A = wl.f16_normal(rng, (200, 512))
+    Wp = wl.prune_blockwise(wl.f16_normal(rng, (512, 256), 0.02), 64, d)
+    packed = lib.tw_pack_f16(Wp, 64)
+    assert (np.diff(packed.n_ptr) == 64).all() and (np.diff(packed.k_ptr) % 64 == 0).all()
+    C = run_tw(lib, A, Wp, 64)
+    check_f16(C, A, Wp, int(np.diff(packed.k_ptr).max()), f"BW d={d}")
+
+
 # ---------------------------------------------------------------- int8 tile-wise
 TW8_SHAPES = [(16, 64, 32, 16, [0.5, 1.0]), (144, 200, 96, 32, [0.3, 0.0, 0.9]),
               (256, 768, 384, 128, [0.1, 0.25, 0.4]), (48, 1000, 64, 64, 0.6), (208, 96, 128, 128, 1.0)]

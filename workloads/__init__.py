@@ -25,6 +25,8 @@ from .gen import (  # noqa: F401
     cfg5_layers,
     prune24_magnitude,
     prune_tilewise,
+    prune_blockwise,
+    prune_elementwise,
     tile_shape,
     f16_normal,
     f16_uniform,

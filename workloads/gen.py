@@ -125,6 +125,41 @@ def prune_tilewise(W, G, densities):
     return _plus_zero(Wp)
 
 
+def prune_blockwise(W, b, density):
+    """Block-wise (BW) pruning, the pattern the tile-wise slides compare against:
+    W [K x N] is cut into b x b blocks; each block column keeps the
+    round(density * K/b) blocks of largest L2 norm (ties to the lower block
+    index, at least one), everything else becomes +0.  With G = b a BW weight is
+    a tile-wise weight whose tiles keep whole b-row runs and every column."""
+    W = np.asarray(W)
+    K, N = W.shape
+    if K % b or N % b:
+        raise ValueError("K and N must be multiples of the block size")
+    nkb = K // b
+    keep = max(1, int(round(density * nkb)))
+    W64 = W.astype(np.float64).reshape(nkb, b, N // b, b)
+    norms = np.sqrt((W64 * W64).sum(axis=(1, 3)))  # [K/b, N/b]
+    Wp = np.zeros_like(W)
+    for jb in range(N // b):
+        rows = _top_indices(norms[:, jb], keep)
+        for kb in rows:
+            Wp[kb * b:(kb + 1) * b, jb * b:(jb + 1) * b] = W[kb * b:(kb + 1) * b, jb * b:(jb + 1) * b]
+    return _plus_zero(Wp)
+
+
+def prune_elementwise(W, density):
+    """Element-wise (EW, unstructured) magnitude pruning: every column keeps its
+    round(density * K) entries of largest |w| (ties to the lower k)."""
+    W = np.asarray(W)
+    K, N = W.shape
+    keep = max(1, int(round(density * K)))
+    order = np.argsort(-np.abs(W.astype(np.float64)), axis=0, kind="stable")[:keep]
+    Wp = np.zeros_like(W)
+    cols = np.arange(N)[None, :]
+    Wp[order, cols] = W[order, cols]
+    return _plus_zero(Wp)
+
+
 # ---------------------------------------------------------------- configs
 def make_cfg1(seed=0):
     rng = np.random.default_rng(seed)
