@@ -312,7 +312,7 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="table mode: every workload and kernel")
     ap.add_argument("--workloads", default="",
                     help="table mode: comma list from " + ",".join(WORKLOADS) +
-                         " or cfg5:<qkv|proj|fc1|fc2> for one layer-0 GEMM (default: all)")
+                         " or vit_large:<qkv|proj|fc1|fc2> for one layer-0 GEMM (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--no-tw-extras", action="store_true",
                     help="table mode: time only the grouped tile-wise kernel (not the fused, row-major-A "
@@ -351,7 +351,7 @@ def main(argv=None):
     if a.all:
         return table(a, torch, ssg, perf, wl, timer)
 
-    c = wl.make_cfg2()
+    c = wl.make_vit_base_fc1_i8()
     M, K, N = c["M"], c["K"], c["N"]
     log(f"workload vit_base_mlp_fc1 2:4 int8 {M}x{K}x{N}, steps {a.steps}, warmup {a.warmup}")
     r = w24_i8_case(torch, ssg, perf, c, a.steps, a.warmup, timer, rotate=not a.warm)
@@ -482,7 +482,7 @@ def summarize_profile(a):
     return 0
 
 
-def cfg5_stack(torch, ssg, perf, wl, dtype, timer, steps_gemm=20, passes=3, layers=24):
+def vit_large_stack(torch, ssg, perf, wl, dtype, timer, steps_gemm=20, passes=3, layers=24):
     """The ViT-Large stack: `layers` x (qkv, proj, fc1, fc2), each GEMM with its own
     2:4 weight and its own A, all resident in HBM.  Two views of "sum of GEMM time":
     the sum over the GEMMs of each one's own graph-timed time (a GEMM repeated on
@@ -493,7 +493,7 @@ def cfg5_stack(torch, ssg, perf, wl, dtype, timer, steps_gemm=20, passes=3, laye
     odt = torch.float16 if dtype == "f16" else torch.float32
     gemms, outs = [], {}
     t0 = time.perf_counter()
-    for g in wl.cfg5_layers(dtype, layers=layers):
+    for g in wl.vit_large_layers(dtype, layers=layers):
         vals, meta = (ssg.w24_pack_f16 if dtype == "f16" else ssg.w24_pack_i8)(g["Wp"])
         d = dict(shape=g["name"].rsplit("_", 1)[1], M=g["M"], K=g["K"], N=g["N"],
                  A=torch.from_numpy(g["A"]).to(dev), vals=torch.from_numpy(vals).to(dev),
@@ -506,7 +506,7 @@ def cfg5_stack(torch, ssg, perf, wl, dtype, timer, steps_gemm=20, passes=3, laye
         d["C"] = outs[key]
         gemms.append(d)
         if len(gemms) % 16 == 0:
-            log(f"cfg5 {dtype} stack: {len(gemms)} GEMMs generated and uploaded ({time.perf_counter() - t0:.0f} s)")
+            log(f"ViT-Large {dtype} stack: {len(gemms)} GEMMs generated and uploaded ({time.perf_counter() - t0:.0f} s)")
 
     def sparse(d):
         if dtype == "f16":
@@ -530,7 +530,7 @@ def cfg5_stack(torch, ssg, perf, wl, dtype, timer, steps_gemm=20, passes=3, laye
         e["dense_ms"] += td
         e["count"] += 1
         if (j + 1) % 32 == 0:
-            log(f"cfg5 {dtype} stack: {j + 1} GEMMs timed one by one")
+            log(f"ViT-Large {dtype} stack: {j + 1} GEMMs timed one by one")
     flops = sum(2.0 * d["M"] * d["N"] * d["K"] for d in gemms)
     t_b2b, t_b2b_de = b2b_sp["ms"] * n, b2b_de["ms"] * n
     t_sum = sum(e["sparse_ms"] for e in by_shape.values())
@@ -538,7 +538,7 @@ def cfg5_stack(torch, ssg, perf, wl, dtype, timer, steps_gemm=20, passes=3, laye
     unit = "tflops" if dtype == "f16" else "tops"
     del gemms, outs
     torch.cuda.empty_cache()
-    return dict(workload=f"cfg5_vit_large_stack_w24_{dtype}", gemms=n, layers=layers,
+    return dict(workload=f"vit_large_stack_w24_{dtype}", gemms=n, layers=layers,
                 t_back_to_back_ms=t_b2b, t_back_to_back_p10_ms=b2b_sp["p10"] * n,
                 t_back_to_back_p90_ms=b2b_sp["p90"] * n, t_dense_back_to_back_ms=t_b2b_de,
                 speedup_vs_dense_back_to_back=t_b2b_de / t_b2b,
@@ -604,7 +604,8 @@ def patterns(torch, ssg, perf, wl, timer, steps, warmup, emit):
             emit(dict(workload="patterns_elementwise_csr_fp32", density=d, error=str(e)[:200], **base))
 
 
-WORKLOADS = ("cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg5stack", "cfg3_i8", "patterns")
+WORKLOADS = ("small", "vit_base_fc1", "bert_base_fc1", "bert_large_ffn", "vit_large", "vit_large_stack",
+             "bert_base_fc1_i8", "patterns")
 
 
 def table(a, torch, ssg, perf, wl, timer):
@@ -616,20 +617,20 @@ def table(a, torch, ssg, perf, wl, timer):
     def emit(d):
         print(json.dumps(d), flush=True)
 
-    if "cfg1" in want:
-        c = wl.make_cfg1()
+    if "small" in want:
+        c = wl.make_small_w24_f16()
         r = w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate)
         nz, de = perf.w24_ops(c["M"], c["N"], c["K"])
-        emit(dict(workload="cfg1_w24_f16", shape=[c["M"], c["K"], c["N"]], **r,
+        emit(dict(workload=c["name"] + "_w24_f16", shape=[c["M"], c["K"], c["N"]], **r,
                   tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
                   speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
-    if "cfg2" in want:
-        c = wl.make_cfg2()
+    if "vit_base_fc1" in want:
+        c = wl.make_vit_base_fc1_i8()
         r = w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate, with_f16_dense=True)
         r.pop("sets")
         nz, de = perf.w24_ops(c["M"], c["N"], c["K"])
         b = perf.w24_bytes(c["M"], c["N"], c["K"], 1, 1, 4, True)
-        emit(dict(workload="cfg2_w24_i8", shape=[c["M"], c["K"], c["N"]], **r,
+        emit(dict(workload=c["name"] + "_w24_i8", shape=[c["M"], c["K"], c["N"]], **r,
                   tops_nonzero=nz / r["t_sparse_ms"] / 1e9, tops_dense_eq=de / r["t_sparse_ms"] / 1e9,
                   gbs=b / r["t_sparse_ms"] / 1e6, speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
                   speedup_vs_dense_f16=r["t_dense_f16_ms"] / r["t_sparse_ms"]))
@@ -637,15 +638,15 @@ def table(a, torch, ssg, perf, wl, timer):
         for out_type in ("f16", "i8"):
             r = w24_i8_out_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate)
             b = perf.w24_bytes(c["M"], c["N"], c["K"], 1, 1, r["out_bytes"], True)
-            emit(dict(workload=f"cfg2_w24_i8_{out_type}_out", shape=[c["M"], c["K"], c["N"]], **r,
+            emit(dict(workload=f"vit_base_fc1_w24_i8_{out_type}_out", shape=[c["M"], c["K"], c["N"]], **r,
                       tops_nonzero=nz / r["t_sparse_ms"] / 1e9, tops_dense_eq=de / r["t_sparse_ms"] / 1e9,
                       gbs=b / r["t_sparse_ms"] / 1e6, speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
             torch.cuda.empty_cache()
     tw_cases = []
-    if "cfg3" in want:
-        tw_cases.append(wl.make_cfg3())
-    if "cfg4" in want:
-        c4 = wl.make_cfg4()
+    if "bert_base_fc1" in want:
+        tw_cases.append(wl.make_bert_base_fc1_tw())
+    if "bert_large_ffn" in want:
+        c4 = wl.make_bert_large_ffn_tw()
         tw_cases += [c4["fc1"], c4["fc2"]]
     for c in tw_cases:
         r = tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate, extras=not a.no_tw_extras)
@@ -657,17 +658,17 @@ def table(a, torch, ssg, perf, wl, timer):
     if "patterns" in want:
         patterns(torch, ssg, perf, wl, timer, steps, warmup, emit)
         torch.cuda.empty_cache()
-    if "cfg3_i8" in want:
-        c = wl.make_cfg3_i8()
+    if "bert_base_fc1_i8" in want:
+        c = wl.make_bert_base_fc1_tw_i8()
         for out_type in ("f16", "i8"):
             r = tw_i8_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate)
-            emit(dict(workload=f"cfg3_shape_tw_i8_{out_type}_out", shape=[c["M"], c["K"], c["N"]], **r,
+            emit(dict(workload=f"bert_base_fc1_tw_i8_{out_type}_out", shape=[c["M"], c["K"], c["N"]], **r,
                       tops_nonzero=r["ops"] / r["t_sparse_ms"] / 1e9,
                       speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
             torch.cuda.empty_cache()
-    only5 = {w.split(":", 1)[1] for w in want if w.startswith("cfg5:")}
-    if "cfg5" in want or only5:
-        for g in wl.cfg5_layers("f16", layers=1):
+    only5 = {w.split(":", 1)[1] for w in want if w.startswith("vit_large:")}
+    if "vit_large" in want or only5:
+        for g in wl.vit_large_layers("f16", layers=1):
             if only5 and g["name"].rsplit("_", 1)[1] not in only5:
                 continue
             r = w24_f16_case(torch, ssg, perf, g, steps, warmup, timer, rotate)
@@ -676,10 +677,10 @@ def table(a, torch, ssg, perf, wl, timer):
                       tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
                       speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
             torch.cuda.empty_cache()
-    if "cfg5stack" in want:
-        f16 = cfg5_stack(torch, ssg, perf, wl, "f16", timer)
+    if "vit_large_stack" in want:
+        f16 = vit_large_stack(torch, ssg, perf, wl, "f16", timer)
         emit(f16)
-        i8 = cfg5_stack(torch, ssg, perf, wl, "i8", timer)
+        i8 = vit_large_stack(torch, ssg, perf, wl, "i8", timer)
         # int8 against the fp16 dense stack of the same shapes as well
         i8["t_dense_f16_back_to_back_ms"] = f16["t_dense_back_to_back_ms"]
         i8["speedup_vs_dense_f16_back_to_back"] = f16["t_dense_back_to_back_ms"] / i8["t_back_to_back_ms"]

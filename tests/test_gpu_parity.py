@@ -97,14 +97,14 @@ def test_w24_f16_every_position_pair(lib, gpu):
     check_f16_exact(run_w24_f16(lib, A, Wp), A, Wp, "position pairs")
 
 
-def test_w24_f16_cfg1(lib, gpu):
-    c = wl.make_cfg1()
-    check_f16(run_w24_f16(lib, c["A"], c["Wp"]), c["A"], c["Wp"], c["K"] // 2, "cfg1")
+def test_w24_f16_small(lib, gpu):
+    c = wl.make_small_w24_f16()
+    check_f16(run_w24_f16(lib, c["A"], c["Wp"]), c["A"], c["Wp"], c["K"] // 2, c["name"])
 
 
 @pytest.mark.parametrize("gname", ["qkv", "proj", "fc1", "fc2"])
-def test_w24_f16_cfg5_layer0(lib, gpu, gname):
-    for g in wl.cfg5_layers("f16", layers=1):
+def test_w24_f16_vit_large_layer0(lib, gpu, gname):
+    for g in wl.vit_large_layers("f16", layers=1):
         if g["name"].endswith(gname):
             check_f16(run_w24_f16(lib, g["A"], g["Wp"]), g["A"], g["Wp"], g["K"] // 2, g["name"])
 
@@ -143,8 +143,8 @@ def test_w24_i8_extreme_values(lib, gpu):
         assert np.array_equal(C.view(np.uint32), ref.view(np.uint32))
 
 
-def test_w24_i8_cfg2(lib, gpu):
-    c = wl.make_cfg2()
+def test_w24_i8_vit_base_fc1(lib, gpu):
+    c = wl.make_vit_base_fc1_i8()
     for s in (None, c["scale"]):
         C = run_w24_i8(lib, c["A"], c["Wp"], s)
         ref = oracle.ref_gemm_i8(c["A"], c["Wp"], s)
@@ -161,8 +161,8 @@ def test_i8_large_tile_path(lib, gpu):
 
 
 @pytest.mark.parametrize("gname", ["qkv", "fc2"])
-def test_w24_i8_cfg5_layer0(lib, gpu, gname):
-    for g in wl.cfg5_layers("i8", layers=1):
+def test_w24_i8_vit_large_layer0(lib, gpu, gname):
+    for g in wl.vit_large_layers("i8", layers=1):
         if g["name"].endswith(gname):
             C = run_w24_i8(lib, g["A"], g["Wp"], g["scale"])
             ref = oracle.ref_gemm_i8(g["A"], g["Wp"], g["scale"])
@@ -262,8 +262,8 @@ def test_i8_out_saturation_and_ties(lib, gpu):
 
 
 @pytest.mark.parametrize("out", ["f16", "i8"])
-def test_w24_i8_out_cfg2(lib, gpu, out):
-    c = wl.make_cfg2()
+def test_w24_i8_out_vit_base_fc1(lib, gpu, out):
+    c = wl.make_vit_base_fc1_i8()
     rng = np.random.default_rng(5)
     scale = (c["scale"] * np.float32(0.02)) if out == "i8" else c["scale"]
     bias = rng.normal(0, 2.0, size=c["N"]).astype(np.float32)
@@ -323,15 +323,15 @@ def test_tw_all_zero_weight(lib, gpu):
     assert (C.view(np.uint16) == 0).all()
 
 
-def test_tw_cfg3(lib, gpu):
-    c = wl.make_cfg3()
+def test_tw_bert_base_fc1(lib, gpu):
+    c = wl.make_bert_base_fc1_tw()
     C = run_tw(lib, c["A"], c["Wp"], c["G"])
-    check_f16(C, c["A"], c["Wp"], 512, "cfg3")
+    check_f16(C, c["A"], c["Wp"], 512, c["name"])
 
 
 @pytest.mark.parametrize("which", ["fc1", "fc2"])
-def test_tw_cfg4(lib, gpu, which):
-    c = wl.make_cfg4()[which]
+def test_tw_bert_large_ffn(lib, gpu, which):
+    c = wl.make_bert_large_ffn_tw()[which]
     C = run_tw(lib, c["A"], c["Wp"], c["G"])
     check_f16(C, c["A"], c["Wp"], 1311, c["name"])
 
@@ -395,7 +395,7 @@ def test_tw_i8_no_bias_pruned_columns(lib, gpu):
 
 @pytest.mark.parametrize("out", ["f16", "i8"])
 def test_tw_i8_workload(lib, gpu, out):
-    c = wl.make_cfg3_i8()
+    c = wl.make_bert_base_fc1_tw_i8()
     rng = np.random.default_rng(41)
     scale = c["scale"] if out == "f16" else (c["scale"] * np.float32(0.05))
     bias = rng.normal(0, 2.0, size=c["N"]).astype(np.float32)
@@ -475,7 +475,7 @@ def test_tw_tile_ranges(lib, gpu):
 
 def test_tw_multi_stream_schedule(lib, gpu):
     import torch
-    c = wl.make_cfg3()
+    c = wl.make_bert_base_fc1_tw()
     packed, At = _tw_setup(lib, c["A"], c["Wp"], c["G"])
     full = H(lib.tw_gemm_f16(At, packed))
     streams = [torch.cuda.Stream() for _ in range(4)]
@@ -496,7 +496,7 @@ def test_determinism(lib, gpu):
     a = run_w24_f16(lib, case["A"], case["Wp"])
     b = run_w24_f16(lib, case["A"], case["Wp"])
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
-    c = wl.make_cfg3()
+    c = wl.make_bert_base_fc1_tw()
     x = run_tw(lib, c["A"][:512], c["Wp"], 128)
     y = run_tw(lib, c["A"][:512], c["Wp"], 128)
     assert np.array_equal(x.view(np.uint16), y.view(np.uint16))

@@ -106,7 +106,7 @@ def test_prune_rank_definition_matches_generator():
 
 
 def test_generated_24_weights_have_at_most_two_per_group():
-    for case in (wl.make_cfg1(), wl.make_cfg2()):
+    for case in (wl.make_small_w24_f16(), wl.make_vit_base_fc1_i8()):
         Wp = case["Wp"]
         K, N = Wp.shape
         assert ((Wp != 0).reshape(K // 4, 4, N).sum(axis=1) <= 2).all()
@@ -161,8 +161,8 @@ def test_tw_full_density_tile_is_dense():
     assert np.array_equal(blk, W.T)
 
 
-def test_tw_cfg3_cfg4_structure():
-    c3 = wl.make_cfg3()
+def test_tw_bert_structure():
+    c3 = wl.make_bert_base_fc1_tw()
     p3 = oracle.ref_tw_pack(c3["Wp"], 128)
     _check_tw_invariants(c3["Wp"], 128, p3)
     kt, nt = np.diff(p3["k_ptr"]), np.diff(p3["n_ptr"])
@@ -170,7 +170,7 @@ def test_tw_cfg3_cfg4_structure():
         assert (nt[t], kt[t]) == wl.tile_shape(c3["densities"][t], 768, 128)
     density = (kt * nt).sum() / (768 * 3072)
     assert abs(density - 0.25) < 0.005
-    c4 = wl.make_cfg4()
+    c4 = wl.make_bert_large_ffn_tw()
     for sub, K, T in ((c4["fc1"], 1024, 32), (c4["fc2"], 4096, 8)):
         p = oracle.ref_tw_pack(sub["Wp"], 128)
         _check_tw_invariants(sub["Wp"], 128, p)

@@ -60,7 +60,7 @@ def test_w24_pack_property(lib, groups, N, seed):
 
 
 def test_w24_pack_full_configs(lib):
-    for c in (wl.make_cfg1(), wl.make_cfg2()):
+    for c in (wl.make_small_w24_f16(), wl.make_vit_base_fc1_i8()):
         pack = lib.w24_pack_f16 if c["Wp"].dtype == np.float16 else lib.w24_pack_i8
         vals, meta = pack(c["Wp"])
         rv, rm = oracle.ref_w24_pack(c["Wp"])
@@ -117,14 +117,14 @@ def test_tw_pack_i8_matches_oracle(lib, K, N, G, d):
 
 
 def test_tw_pack_i8_workload(lib):
-    c = wl.make_cfg3_i8()
+    c = wl.make_bert_base_fc1_tw_i8()
     _tw_equal(lib.tw_pack_i8(c["Wp"], 128), oracle.ref_tw_pack(c["Wp"], 128))
 
 
 def test_tw_pack_full_configs(lib):
-    c3 = wl.make_cfg3()
+    c3 = wl.make_bert_base_fc1_tw()
     _tw_equal(lib.tw_pack_f16(c3["Wp"], 128), oracle.ref_tw_pack(c3["Wp"], 128))
-    c4 = wl.make_cfg4()
+    c4 = wl.make_bert_large_ffn_tw()
     for sub in (c4["fc1"], c4["fc2"]):
         _tw_equal(lib.tw_pack_f16(sub["Wp"], 128), oracle.ref_tw_pack(sub["Wp"], 128))
 

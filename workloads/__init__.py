@@ -15,14 +15,14 @@ pages describe but which needs data and training:
 """
 
 from .gen import (  # noqa: F401
-    CONFIG_NAMES,
-    make_config,
-    make_cfg1,
-    make_cfg2,
-    make_cfg3,
-    make_cfg3_i8,
-    make_cfg4,
-    cfg5_layers,
+    WORKLOAD_NAMES,
+    make_workload,
+    make_small_w24_f16,
+    make_vit_base_fc1_i8,
+    make_bert_base_fc1_tw,
+    make_bert_base_fc1_tw_i8,
+    make_bert_large_ffn_tw,
+    vit_large_layers,
     prune24_magnitude,
     prune_tilewise,
     prune_blockwise,

@@ -4,16 +4,16 @@ Every workload is drawn from ``np.random.default_rng(seed)`` (PCG64) in a
 fixed order, so both sides of a parity test see identical bytes.  Shapes and
 distributions follow the five benchmark workloads:
 
-* cfg1 -- 2:4 fp16, tiny: A[256x512] ~ U(-1,1), W[512x512] ~ N(0,0.02).
-* cfg2 -- 2:4 int8, ViT-Base MLP fc1 (197 tokens x batch 64):
+* small -- 2:4 fp16, tiny: A[256x512] ~ U(-1,1), W[512x512] ~ N(0,0.02).
+* vit_base_fc1 -- 2:4 int8, ViT-Base MLP fc1 (197 tokens x batch 64):
   A[12608x768] ~ U{-127..127}, W[768x3072] = clip(rint(N(0,32)), +-127),
   per-output-channel fp32 scale ~ U(1e-3, 1e-2).
-* cfg3 -- tile-wise fp16, BERT-base FFN fc1 (seq 128 x batch 32):
+* bert_base_fc1 -- tile-wise fp16, BERT-base FFN fc1 (seq 128 x batch 32):
   A[4096x768] ~ N(0,1), W[768x3072] ~ N(0,0.02), G = 128, 75 % global
   sparsity with uneven per-tile densities drawn from U(0.1,0.5).
-* cfg4 -- tile-wise fp16, BERT-large FFN (seq 384 x batch 16) at 90 %:
+* bert_large_ffn -- tile-wise fp16, BERT-large FFN (seq 384 x batch 16) at 90 %:
   fc1 A[6144x1024] W[1024x4096]; fc2 A[6144x4096] W[4096x1024]; G = 128.
-* cfg5 -- ViT-Large stack (256 tokens x batch 16 = 4096): per layer qkv
+* vit_large -- ViT-Large stack (256 tokens x batch 16 = 4096): per layer qkv
   (1024->3072), proj (1024->1024), fc1 (1024->4096), fc2 (4096->1024), 24
   layers, all 2:4, once in fp16 and once in int8.
 
@@ -26,7 +26,7 @@ from __future__ import annotations
 import numpy as np
 
 F16 = np.float16
-CONFIG_NAMES = ("cfg1", "cfg2", "cfg3", "cfg4", "cfg5")
+WORKLOAD_NAMES = ("small", "vit_base_fc1", "bert_base_fc1", "bert_large_ffn")
 
 
 # ---------------------------------------------------------------- value draws
@@ -161,100 +161,100 @@ def prune_elementwise(W, density):
 
 
 # ---------------------------------------------------------------- configs
-def make_cfg1(seed=0):
+def make_small_w24_f16(seed=0):
     rng = np.random.default_rng(seed)
     A = f16_uniform(rng, (256, 512))
     W = f16_normal(rng, (512, 512), 0.02)
-    return dict(name="cfg1", kind="w24_f16", M=256, K=512, N=512,
+    return dict(name="small_256x512x512", kind="w24_f16", M=256, K=512, N=512,
                 A=A, W=W, Wp=prune24_magnitude(W))
 
 
-def make_cfg2(seed=0, M=64 * 197):
+def make_vit_base_fc1_i8(seed=0, M=64 * 197):
     rng = np.random.default_rng(seed)
     K, N = 768, 3072
     A = i8_uniform(rng, (M, K))
     W = i8_weights(rng, (K, N))
     scale = f32_scales(rng, N)
-    return dict(name="cfg2", kind="w24_i8", M=M, K=K, N=N,
+    return dict(name="vit_base_fc1", kind="w24_i8", M=M, K=K, N=N,
                 A=A, W=W, Wp=prune24_magnitude(W), scale=scale)
 
 
-def cfg3_densities(rng, T, target=0.25):
+def uneven_tile_densities(rng, T, target=0.25):
     """Uneven per-tile densities: u ~ U(0.1,0.5), rescaled to the global target."""
     u = rng.uniform(0.1, 0.5, size=T)
     return u * (target / u.mean())
 
 
-def make_cfg3(seed=0):
+def make_bert_base_fc1_tw(seed=0):
     rng = np.random.default_rng(seed)
     M, K, N, G = 32 * 128, 768, 3072, 128
     A = f16_normal(rng, (M, K))
     W = f16_normal(rng, (K, N), 0.02)
-    d = cfg3_densities(rng, N // G)
-    return dict(name="cfg3", kind="tw_f16", M=M, K=K, N=N, G=G,
+    d = uneven_tile_densities(rng, N // G)
+    return dict(name="bert_base_fc1", kind="tw_f16", M=M, K=K, N=N, G=G,
                 A=A, W=W, Wp=prune_tilewise(W, G, d), densities=d)
 
 
-def make_cfg3_i8(seed=0):
-    """cfg3's shape, tiles and densities with the integer path's data (NEXT-3's
-    int8 tile-wise): A int8 U{-127..127}, W round(N(0,32)) clipped, tile-wise
-    pruned like cfg3, per-channel scales U(1e-3, 1e-2)."""
+def make_bert_base_fc1_tw_i8(seed=0):
+    """The BERT-base fc1 shape, tiles and densities with the integer path's
+    data (int8 tile-wise): A int8 U{-127..127}, W round(N(0,32)) clipped,
+    tile-wise pruned like the fp16 case, per-channel scales U(1e-3, 1e-2)."""
     rng = np.random.default_rng(seed)
     M, K, N, G = 32 * 128, 768, 3072, 128
     A = i8_uniform(rng, (M, K))
     W = i8_weights(rng, (K, N))
-    d = cfg3_densities(rng, N // G)
+    d = uneven_tile_densities(rng, N // G)
     scale = f32_scales(rng, N)
-    return dict(name="cfg3_i8", kind="tw_i8", M=M, K=K, N=N, G=G,
+    return dict(name="bert_base_fc1_i8", kind="tw_i8", M=M, K=K, N=N, G=G,
                 A=A, W=W, Wp=prune_tilewise(W, G, d), densities=d, scale=scale)
 
 
-def make_cfg4(seed=0):
+def make_bert_large_ffn_tw(seed=0):
     rng = np.random.default_rng(seed)
     M, G = 16 * 384, 128
     A1 = f16_normal(rng, (M, 1024))
     W1 = f16_normal(rng, (1024, 4096), 0.02)
     A2 = f16_normal(rng, (M, 4096))
     W2 = f16_normal(rng, (4096, 1024), 0.02)
-    fc1 = dict(name="cfg4_fc1", kind="tw_f16", M=M, K=1024, N=4096, G=G,
+    fc1 = dict(name="bert_large_fc1", kind="tw_f16", M=M, K=1024, N=4096, G=G,
                A=A1, W=W1, Wp=prune_tilewise(W1, G, 0.1), densities=0.1)
-    fc2 = dict(name="cfg4_fc2", kind="tw_f16", M=M, K=4096, N=1024, G=G,
+    fc2 = dict(name="bert_large_fc2", kind="tw_f16", M=M, K=4096, N=1024, G=G,
                A=A2, W=W2, Wp=prune_tilewise(W2, G, 0.1), densities=0.1)
-    return dict(name="cfg4", kind="tw_f16", fc1=fc1, fc2=fc2)
+    return dict(name="bert_large_ffn", kind="tw_f16", fc1=fc1, fc2=fc2)
 
 
-CFG5_M = 16 * 256
-CFG5_GEMMS = (("qkv", 1024, 3072), ("proj", 1024, 1024),
+VIT_LARGE_M = 16 * 256
+VIT_LARGE_GEMMS = (("qkv", 1024, 3072), ("proj", 1024, 1024),
               ("fc1", 1024, 4096), ("fc2", 4096, 1024))
 
 
-def cfg5_layers(dtype="f16", seed=0, layers=24, M=CFG5_M):
+def vit_large_layers(dtype="f16", seed=0, layers=24, M=VIT_LARGE_M):
     """Yield the 4*layers GEMMs of the ViT-Large stack, one dict at a time.
 
-    fp16: A ~ N(0,1), W ~ N(0,0.02).  int8: the cfg2 draws.  Every GEMM has
+    fp16: A ~ N(0,1), W ~ N(0,0.02).  int8: the ViT-Base fc1 draws.  Every GEMM has
     its own A.  The fp16 and int8 stacks each start from default_rng(seed).
     """
     rng = np.random.default_rng(seed)
     for layer in range(layers):
-        for gname, K, N in CFG5_GEMMS:
+        for gname, K, N in VIT_LARGE_GEMMS:
             if dtype == "f16":
                 A = f16_normal(rng, (M, K))
                 W = f16_normal(rng, (K, N), 0.02)
-                yield dict(name=f"cfg5_l{layer}_{gname}", kind="w24_f16", M=M, K=K, N=N,
+                yield dict(name=f"vit_large_l{layer}_{gname}", kind="w24_f16", M=M, K=K, N=N,
                            A=A, W=W, Wp=prune24_magnitude(W))
             elif dtype == "i8":
                 A = i8_uniform(rng, (M, K))
                 W = i8_weights(rng, (K, N))
                 scale = f32_scales(rng, N)
-                yield dict(name=f"cfg5_l{layer}_{gname}", kind="w24_i8", M=M, K=K, N=N,
+                yield dict(name=f"vit_large_l{layer}_{gname}", kind="w24_i8", M=M, K=K, N=N,
                            A=A, W=W, Wp=prune24_magnitude(W), scale=scale)
             else:
                 raise ValueError(dtype)
 
 
-def make_config(name, seed=0):
-    return {"cfg1": make_cfg1, "cfg2": make_cfg2, "cfg3": make_cfg3,
-            "cfg4": make_cfg4}[name](seed)
+def make_workload(name, seed=0):
+    return {"small": make_small_w24_f16, "vit_base_fc1": make_vit_base_fc1_i8,
+            "bert_base_fc1": make_bert_base_fc1_tw, "bert_large_ffn": make_bert_large_ffn_tw}[name](seed)
 
 
 # ---------------------------------------------------------------- small cases
