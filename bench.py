@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "effective TFLOPS/TOPS of sparse GEMM + speedup vs dense MFMA GEMM, same shape"
+HEADLINE_REPLAYS = 5  # graph replays of the K timed steps; the median is reported
 CACHE_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w24_gemm_i8_vit_base_fc1.txt")
 
@@ -328,6 +329,9 @@ def main(argv=None):
                     help="kernel source file whose hash the --summarize-profile summary records")
     ap.add_argument("--out", help="summary file for --summarize-profile")
     ap.add_argument("--command", default="", help="the profiled command line, recorded in the summary")
+    ap.add_argument("--profile-steps", type=int, default=20, help="--steps of the profiled command (dispatch groups)")
+    ap.add_argument("--profile-warmup", type=int, default=5, help="--warmup of the profiled command")
+    ap.add_argument("--bench-log", help="stdout of the profiled command (its bench line is quoted in the summary)")
     a = ap.parse_args(argv)
     if a.summarize_profile:
         return summarize_profile(a)
@@ -354,8 +358,11 @@ def main(argv=None):
     c = wl.make_vit_base_fc1_i8()
     M, K, N = c["M"], c["K"], c["N"]
     log(f"workload vit_base_mlp_fc1 2:4 int8 {M}x{K}x{N}, steps {a.steps}, warmup {a.warmup}")
+    # the graph of K steps is replayed HEADLINE_REPLAYS times (each replay a
+    # timed region of exactly K steps); ms_per_step is the median replay
+    timer.reps = HEADLINE_REPLAYS
     r = w24_i8_case(torch, ssg, perf, c, a.steps, a.warmup, timer, rotate=not a.warm)
-    t_eager = Timer(torch, graph=False)(
+    t_eager = Timer(torch, graph=False, reps=HEADLINE_REPLAYS)(
         lambda i: ssg.w24_gemm_i8(r["sets"][i % r["rotate_sets"]]["A"], r["sets"][i % r["rotate_sets"]]["vals"],
                                   r["sets"][i % r["rotate_sets"]]["meta"], r["sets"][i % r["rotate_sets"]]["scale"],
                                   out=r["sets"][i % r["rotate_sets"]]["C"]), a.steps, a.warmup)
@@ -385,7 +392,11 @@ def main(argv=None):
         "dense_equivalent_tops": de / t / 1e12,
         "speedup_vs_dense": perf.speedup(r["t_dense_ms"], r["t_sparse_ms"]),
         "dense_i8_ms": r["t_dense_ms"],
-        "timing": "HIP graph of the timed steps replayed on one stream, HIP events around the replay",
+        "timing": f"HIP graph of the {a.steps} timed steps replayed on one stream, HIP events around each replay; "
+                  f"median of {HEADLINE_REPLAYS} replays (p10 / p90 beside)",
+        "replays": HEADLINE_REPLAYS,
+        "ms_per_step_p10": r["t_sparse_p10_ms"],
+        "ms_per_step_p90": r["t_sparse_p90_ms"],
         "eager_ms_per_step": t_eager,
         "roofline": perf.roofline(achieved, perf.PEAK_HBM_GBS, "GB/s", "hbm", traffic),
         "cpu_baseline": None,
@@ -451,6 +462,31 @@ def summarize_profile(a):
 
     is_target = lambda n: a.kernel in n
     is_copy = lambda n: "copy" in n.lower() and "elementwise" not in n.lower()
+    # the target's dispatches in launch order: the profiled bench does `warmup`
+    # eager calls, then groups of `steps` (one graph replay or one eager
+    # repetition each), so per-group medians show the timed replays apart
+    # from the warm-up, and the clock's drift under sustained load
+    tr = [r for r in _csv_rows(os.path.join(root, "trace"), "kernel_trace.csv") if is_target(r.get("Kernel_Name", ""))]
+    if tr:
+        tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+        d = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr]) / 1e3
+        out.append(f"target '{a.kernel}': {d.size} dispatches, mean {d.mean():.1f} us, median {np.median(d):.1f} us")
+        w, st = max(0, a.profile_warmup), max(1, a.profile_steps)
+        groups = [d[:w]] + [d[i:i + st] for i in range(w, d.size, st)]
+        out.append(f"  per-group median us (warm-up {w}, then groups of {st}): " +
+                   " ".join(f"{np.median(g):.1f}" for g in groups if g.size))
+    if a.bench_log and os.path.exists(a.bench_log):
+        lines = [ln for ln in open(a.bench_log) if ln.startswith("{")]
+        for ln in lines:
+            j = json.loads(ln)
+            if "ms_per_step" in j:
+                out.append(f"bench line of the profiled command: ms_per_step {j['ms_per_step'] * 1e3:.1f} us "
+                           f"(p10 {j.get('ms_per_step_p10', float('nan')) * 1e3:.1f}, "
+                           f"p90 {j.get('ms_per_step_p90', float('nan')) * 1e3:.1f}), "
+                           f"dense {j.get('dense_i8_ms', float('nan')) * 1e3:.1f} us")
+            elif "t_sparse_ms" in j:
+                out.append(f"bench line of the profiled command: {j.get('workload')} t_sparse {j['t_sparse_ms'] * 1e3:.1f} us, "
+                           f"t_dense {j.get('t_dense_ms', float('nan')) * 1e3:.1f} us")
     tf, ntf = counter("fetch", "FETCH_SIZE", is_target)
     tw, ntw = counter("write", "WRITE_SIZE", is_target)
     cf, ncf = counter("copy_fetch", "FETCH_SIZE", is_copy)

@@ -493,15 +493,16 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 }
 
 // Tile shapes (measured on MI355X at the ViT / BERT / ViT-Base shapes):
-//   Big   256 x 256, 8 waves of 64 tokens x 128 channels, one workgroup per
-//         CU with eight load-issuing waves -- best once there are about as
-//         many tiles as CUs and K is long enough to amortise the prologue;
-//   Mid   128 x 256, 4 waves, 2 stages (68 KiB LDS, two workgroups per CU) --
-//         the int8 fp32-output GEMMs with short K, whose time is dominated by
-//         the output stream: two resident workgroups overlap one tile's
-//         stores with the other's loads;
-//   Small 128 x 128, 4 waves, 3 stages (two workgroups per CU) -- narrow
-//         outputs (N = 1024) that would leave CUs idle with big tiles.
+//   Big    256 x 256, 8 waves of 64 tokens x 128 channels, one workgroup per
+//          CU with eight load-issuing waves -- best once there are about as
+//          many tiles as CUs and K is long enough to amortise the prologue;
+//   Mid    128 x 256, 4 waves, 2 stages (two workgroups per CU) -- short-K
+//          int8 GEMMs with one to two such tiles per CU;
+//   Small  128 x 128, 4 waves, 3 stages (two workgroups per CU) -- narrow
+//          outputs (N = 1024) that would leave CUs idle with big tiles;
+//   Small2 128 x 128, 4 waves, 2 stages (three int8 workgroups per CU) --
+//          short-K int8 GEMMs whose Mid tiles would fill the chip more than
+//          twice or less than once, and the dense int8 GEMMs at short K.
 template <bool NTS>
 using CfgBig = Cfg<4, 2, 2, 4, 3, 8, NTS>;
 template <bool NTS>
@@ -510,19 +511,34 @@ template <bool NTS>
 using CfgMid = Cfg<2, 2, 2, 4, 2, 8, NTS>;
 template <bool NTS>
 using CfgSmall = Cfg<2, 2, 2, 2, 3, 8, NTS>;
+template <bool NTS>
+using CfgSmall2 = Cfg<2, 2, 2, 2, 2, 8, NTS>;
 
-enum Shape { SHAPE_BIG, SHAPE_MID, SHAPE_SMALL };
+enum Shape { SHAPE_BIG, SHAPE_MID, SHAPE_SMALL, SHAPE_SMALL2 };
+
+static long tiles(int M, int N, int bm, int bn) { return long((M + bm - 1) / bm) * long((N + bn - 1) / bn); }
 
 // f16 kinds: big tiles when they still give >= 3/4 of a tile per CU.
-static Shape pick_f16(int M, int N) {
-    const long big = long((M + 255) / 256) * long((N + 255) / 256);
-    return big >= 192 ? SHAPE_BIG : SHAPE_SMALL;
-}
-// int8 kinds write 4-byte outputs: short-K problems are output-bound.
-static Shape pick_i8(int M, int N, int K) {
-    if (K <= 1024) return SHAPE_MID;
-    const long big = long((M + 255) / 256) * long((N + 255) / 256);
-    return big >= 192 ? SHAPE_BIG : SHAPE_SMALL;
+static Shape pick_f16(int M, int N) { return tiles(M, N, 256, 256) >= 192 ? SHAPE_BIG : SHAPE_SMALL; }
+
+// int8 kinds.  Short K (<= 1024): the per-tile prologue and the output
+// stream weigh most, so the choice follows how evenly the tiles fill the
+// chip's workgroup slots (ViT-Base fc1 12608x768x3072: 1188 Mid tiles, Small2
+// 45 us vs Mid 47.6; ViT-L qkv / fc1: 384 / 512 Mid tiles, Mid best; ViT-L
+// proj: 128 Mid tiles, Small2 10.4 us vs Mid 14.0).  The dense kind keeps
+// 2 x 96 KiB of stages for a Mid tile, i.e. one workgroup per CU, so it
+// takes Small2 unless Big tiles fill the chip one to two times (ViT-L fc1).
+// Long K: as the f16 kinds.
+static Shape pick_i8(int M, int N, int K, bool dense) {
+    if (K <= 1024) {
+        if (dense) {
+            const long big = tiles(M, N, 256, 256);
+            return (big >= 256 && big <= 512) ? SHAPE_BIG : SHAPE_SMALL2;
+        }
+        const long mid = tiles(M, N, 128, 256);
+        return (mid >= 256 && mid <= 512) ? SHAPE_MID : SHAPE_SMALL2;
+    }
+    return tiles(M, N, 256, 256) >= 192 ? SHAPE_BIG : SHAPE_SMALL;
 }
 
 template <int KIND, int EPI, bool NTS, bool DENSE>
@@ -533,6 +549,8 @@ static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const ui
         else return launch<KIND, EPI, CfgBig<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
     }
     if (sh == SHAPE_MID) return launch<KIND, EPI, CfgMid<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
+    if constexpr (KindTraits<KIND>::kI8)  // (only the int8 kinds pick Small2)
+        if (sh == SHAPE_SMALL2) return launch<KIND, EPI, CfgSmall2<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
     return launch<KIND, EPI, CfgSmall<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
 }
 
@@ -555,7 +573,7 @@ hipError_t launch_w24_f16(const void *A, const void *vals, const uint32_t *meta,
 template <int KIND, bool DENSE>
 static hipError_t launch_i8(const void *A, const void *Wv, const uint32_t *meta, const float *scale,
                             const float *bias, void *C, int out, int M, int N, int K, hipStream_t st) {
-    const Shape sh = pick_i8(M, N, K);
+    const Shape sh = pick_i8(M, N, K, DENSE);
     switch (out) {
         case OUT_I32:
             return launch_shape<KIND, EPI_I32, true, DENSE>(sh, A, Wv, meta, nullptr, nullptr, C, M, N, K, st);

@@ -160,6 +160,26 @@ def test_i8_large_tile_path(lib, gpu):
     assert np.array_equal(Cd, oracle.ref_gemm_i8(case["A"], case["W"]))
 
 
+# Short-K int8 tile choice: (M, K, N) -> sparse tile / dense tile.  Ragged M
+# (not a multiple of 128) so every path also runs a partial last tile row.
+I8_SHORT_K_PATHS = [
+    (4000, 512, 4096),   # 512 Mid tiles -> sparse 128x256; 256 Big tiles -> dense 256x256
+    (3000, 768, 2048),   # 192 Mid tiles -> sparse 128x128 two-stage; 96 Big tiles -> dense 128x128
+    (9000, 256, 3072),   # 852 Mid tiles -> sparse 128x128 two-stage; 432 Big tiles -> dense 256x256
+]
+
+
+@pytest.mark.parametrize("M,K,N", I8_SHORT_K_PATHS)
+def test_i8_short_k_tile_paths(lib, gpu, M, K, N):
+    case = wl.random_24_i8(np.random.default_rng(M + N), M, K, N)
+    C = run_w24_i8(lib, case["A"], case["Wp"], case["scale"])
+    ref = oracle.ref_gemm_i8(case["A"], case["Wp"], case["scale"])
+    assert np.array_equal(C.view(np.uint32), ref.view(np.uint32))
+    Cd = H(lib.dense_gemm_i8(T(case["A"]), T(case["W"].T), T(case["scale"])))
+    refd = oracle.ref_gemm_i8(case["A"], case["W"], case["scale"])
+    assert np.array_equal(Cd.view(np.uint32), refd.view(np.uint32))
+
+
 @pytest.mark.parametrize("gname", ["qkv", "fc2"])
 def test_w24_i8_vit_large_layer0(lib, gpu, gname):
     for g in wl.vit_large_layers("i8", layers=1):
