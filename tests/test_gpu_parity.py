@@ -531,6 +531,72 @@ def test_w24_writes_every_output(lib, gpu):
     assert np.isfinite(C.astype(np.float32)).all()
 
 
+# ---------------------------------------------------------------- largest operands
+# The row-major GEMMs address A and W with 32-bit byte offsets and accept
+# operands up to just under 4 GiB; the tile-wise kernels index At with 64-bit
+# offsets.  Operands at those sizes are drawn on the GPU (integer values, so
+# fp16 results are exact and compare bit for bit) and sampled output rows --
+# the first and last 64 and 64 random ones -- are checked against the oracle.
+def _sample_rows(M, seed):
+    r = np.random.default_rng(seed).integers(0, M, 64)
+    return np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), r]))
+
+
+def _rows(t, rows):
+    import torch
+    return t.index_select(0, torch.from_numpy(rows).cuda()).cpu().numpy()
+
+
+def test_w24_largest_a(lib, gpu):
+    import torch
+    K, N = 1024, 64
+    M = (1 << 32) // (2 * K) - 8  # A is 4 GiB - 16 KiB of fp16
+    rows = _sample_rows(M, 41)
+    w = wl.exact_int_24_f16(np.random.default_rng(41), 1, K, N)
+    A = wl.device_int_matrix(torch, M, K, -3, 3, 41, torch.float16)
+    vals, meta = lib.w24_pack_f16(w["Wp"])
+    C = lib.w24_gemm_f16(A, T(vals), meta_t(meta))
+    A_s, C_s = _rows(A, rows), _rows(C, rows)
+    del A, C
+    _, ref = oracle.ref_gemm_f16(A_s, w["Wp"])
+    assert np.array_equal(C_s.view(np.uint16), ref.view(np.uint16))
+    # int8 at the same row count (the limit check is the same for both kinds)
+    c8 = wl.random_24_i8(np.random.default_rng(42), 1, K, N)
+    A8 = wl.device_int_matrix(torch, M, K, -127, 127, 42, torch.int8)
+    vals8, meta8 = lib.w24_pack_i8(c8["Wp"])
+    C8 = lib.w24_gemm_i8(A8, T(vals8), meta_t(meta8), T(c8["scale"]))
+    Cd = lib.dense_gemm_i8(A8, T(np.ascontiguousarray(c8["Wp"].T)), T(c8["scale"]))
+    A8_s, C8_s, Cd_s = _rows(A8, rows), _rows(C8, rows), _rows(Cd, rows)
+    ref8 = oracle.ref_gemm_i8(A8_s, c8["Wp"], c8["scale"])
+    assert np.array_equal(C8_s.view(np.uint32), ref8.view(np.uint32))
+    assert np.array_equal(Cd_s.view(np.uint32), ref8.view(np.uint32))
+
+
+def test_tw_largest_at(lib, gpu):
+    import torch
+    K, N, G = 1024, 256, 128
+    M = (1 << 31) // K + 16  # At holds more than 2^31 elements
+    rows = _sample_rows(M, 43)
+    c = wl.exact_int_tw_f16(np.random.default_rng(43), 1, K, N, G, [0.3, 0.7])
+    At = wl.device_int_matrix(torch, K, M, -3, 3, 43, torch.float16)
+    C = lib.tw_gemm_f16(At, lib.tw_pack_f16(c["Wp"], G).to("cuda"))
+    idx = torch.from_numpy(rows).cuda()
+    A_s = At.index_select(1, idx).t().contiguous().cpu().numpy()
+    C_s = _rows(C, rows)
+    del C
+    _, ref = oracle.ref_gemm_f16(A_s, c["Wp"])
+    assert np.array_equal(C_s.view(np.uint16), ref.view(np.uint16))
+    # int8 tile-wise on the same At, as int8
+    del At
+    c8 = wl.random_tw_i8(np.random.default_rng(44), 1, K, N, G, [0.3, 0.7])
+    At8 = wl.device_int_matrix(torch, K, M, -127, 127, 44, torch.int8)
+    C8 = lib.tw_gemm_i8(At8, lib.tw_pack_i8(c8["Wp"], G).to("cuda"), T(c8["scale"]), None, out_type="f32")
+    A8_s = At8.index_select(1, idx).t().contiguous().cpu().numpy()
+    C8_s = _rows(C8, rows)
+    ref8 = oracle.ref_gemm_i8_out(A8_s, c8["Wp"], c8["scale"], None, "f32")
+    assert np.array_equal(C8_s.view(np.uint32), ref8.view(np.uint32))
+
+
 def test_device_arch_is_gfx950(lib, gpu):
     assert lib.ssg_device_arch().startswith("gfx950")
 

@@ -40,5 +40,6 @@ from .gen import (  # noqa: F401
     exact_int_24_f16,
     exact_int_tw_f16,
     one_hot_24,
+    device_int_matrix,
     one_hot_tw,
 )

@@ -295,6 +295,16 @@ def exact_int_tw_f16(rng, M, K, N, G, densities):
     return dict(A=A, W=W, Wp=prune_tilewise(W, G, densities))
 
 
+def device_int_matrix(torch, rows, cols, lo, hi, seed, dtype):
+    """Integer values in [lo, hi] drawn on the GPU by torch's seeded
+    generator, as a rows x cols tensor of `dtype`: for operands of several
+    GiB that would take too long to draw on the host and upload."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randint(lo, hi + 1, (rows, cols), generator=g, device="cuda", dtype=torch.int8)
+    return x if dtype == torch.int8 else x.to(dtype)
+
+
 def one_hot_24(rng, M, K, N, dtype=F16):
     """Each column n holds a single 1 at a random k(n); C[:, n] must equal A[:, k(n)]."""
     if dtype == np.int8:
