@@ -114,13 +114,20 @@ __device__ __forceinline__ u32x4 lds16(const uint8_t *p) { return *reinterpret_c
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-// Direct-to-LDS loads: lane i of the wave writes its 16 (4) bytes to
-// wave_base + 16*i (4*i).  wave_base must be uniform across the wave.
-__device__ __forceinline__ void dma16(const void *g, uint8_t *wave_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)wave_base, 16, 0, 0);
+// Direct-to-LDS loads through a buffer resource: lane i of the wave reads
+// 16 (4) bytes at byte offset `off` of the buffer and writes them to
+// wave_base + 16*i (4*i); wave_base must be uniform across the wave.  The
+// buffer form moves a few per cent more per wave than the flat-address form
+// (L2 → LDS microbenchmark on MI355X), and reads past the buffer's size
+// return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, int(bytes), 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void *g, uint8_t *wave_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)wave_base, 4, 0, 0);
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t *wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)wave_base, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t *wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)wave_base, 4, off, 0, 0, 0);
 }
 
 // Waits until at most N vector-memory operations of this wave are
@@ -283,17 +290,21 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     // different K slices and spread over all channels.  The order is fixed per
     // tile, so results stay deterministic.
     const int rot = b % S;
+    // (the host caps A and W below 4 GiB, so every byte count fits 32 bits)
+    const __amdgpu_buffer_rsrc_t bufA = buffer_of(A, uint32_t(int64_t(M) * a_row));
+    const __amdgpu_buffer_rsrc_t bufW = buffer_of(Wv, uint32_t(int64_t(N) * w_row));
+    const __amdgpu_buffer_rsrc_t bufM = buffer_of(meta_b, KT::kSparse ? uint32_t(int64_t(N) * m_row * 4) : 0u);
     auto issue = [&](int s) {
         uint8_t *base = smem + (s % NB) * STAGE;
         const int sg = (s + rot < S) ? s + rot : s + rot - S;  // global K stage
 #pragma unroll
-        for (int j = 0; j < LY::LA; ++j) dma16(A + (oa[j] + uint32_t(sg * 128)), base + (j * LY::NW + wave) * 1024);
+        for (int j = 0; j < LY::LA; ++j) dma16(bufA, oa[j] + uint32_t(sg * 128), base + (j * LY::NW + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < LY::LW; ++j)
-            dma16(Wv + (ow[j] + uint32_t(sg * WB)), base + A_STAGE + (j * LY::NW + wave) * 1024);
+            dma16(bufW, ow[j] + uint32_t(sg * WB), base + A_STAGE + (j * LY::NW + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < LY::LM; ++j)
-            dma4(meta_b + (om[j] + uint32_t(sg * MW * 4)), base + A_STAGE + W_STAGE + (j * LY::NW + wave) * 256);
+            dma4(bufM, om[j] + uint32_t(sg * MW * 4), base + A_STAGE + W_STAGE + (j * LY::NW + wave) * 256);
     };
 
     // Fragments of one k-step (one matrix instruction deep) for the wave's
