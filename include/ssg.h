@@ -120,6 +120,11 @@ int w24_unpack_i8(const int8_t *vals, const uint32_t *meta, int64_t K, int64_t N
  * needed.  The int8 forms are the same format with int8 values (the
  * quantised deployment of the integer path).  Requires G > 0, K > 0, N > 0,
  * K < 2^31, and sum of tile sizes < 2^31.
+ * tw_unpack_f16 (tw_unpack_i8) writes the dense W [K][N] (pruned entries +0)
+ * after checking the arrays against each other: prefix sums starting at 0
+ * and non-decreasing, each tile's vals span equal to N_t * ld_t, offsets in
+ * range (offset_k < K, offset_n < the tile's width), no null array of
+ * nonzero length; a violation returns SSG_EINVAL with nothing written.
  * ------------------------------------------------------------------------ */
 typedef struct {
     int64_t T;          /* number of tiles                 */

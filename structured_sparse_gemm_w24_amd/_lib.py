@@ -228,6 +228,14 @@ def _tw_unpack(p: TwPacked, dt, fn):
     W = np.empty((p.K, p.N), dt)
     arrs = [_host(p.vals, dt), _host(p.offset_k, np.int32), _host(p.offset_n, np.int32),
             _host(p.v_ptr, np.int32), _host(p.k_ptr, np.int32), _host(p.n_ptr, np.int32)]
+    # the library reads T+1 prefix sums and as many values / offsets as they
+    # claim: check the lengths here, where they are known
+    T = -(-p.N // p.G)
+    vals, offk, offn, vp, kp, np_ = arrs
+    if vp.size != T + 1 or kp.size != T + 1 or np_.size != T + 1:
+        raise ValueError(f"prefix-sum arrays must hold T+1 = {T + 1} entries")
+    if vals.size < vp[-1] or offk.size < kp[-1] or offn.size < np_[-1]:
+        raise ValueError("vals / offset_k / offset_n shorter than their prefix sums claim")
     _check(getattr(load(), fn)(*[_np_ptr(a) for a in arrs], p.K, p.N, p.G, _np_ptr(W)))
     return W
 
@@ -263,6 +271,17 @@ def _ptr(t):
     return ct.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _on(first, *others):
+    """Every tensor of a call on first's device; returns the context that
+    makes that device current for the launch (the library checks and launches
+    on the current device, on that device's current torch stream)."""
+    torch = _torch()
+    for t in others:
+        if t is not None and t.device != first.device:
+            raise ValueError(f"all tensors must be on {first.device}, found one on {t.device}")
+    return torch.cuda.device(first.device)
+
+
 def _stream(t):
     torch = _torch()
     return ct.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
@@ -289,7 +308,8 @@ def dense_gemm_f16(A, Wt, out=None):
     _dev(A, torch.float16, (M, K), "A")
     _dev(Wt, torch.float16, (N, K), "Wt")
     C = _out(out, (M, N), torch.float16, A)
-    _check(load().dense_gemm_f16(_ptr(A), _ptr(Wt), _ptr(C), M, N, K, _stream(A)))
+    with _on(A, Wt, C):
+        _check(load().dense_gemm_f16(_ptr(A), _ptr(Wt), _ptr(C), M, N, K, _stream(A)))
     return C
 
 
@@ -303,7 +323,8 @@ def dense_gemm_i8(A, Wt, scale=None, out=None):
     if scale is not None:
         _dev(scale, torch.float32, (N,), "scale")
     C = _out(out, (M, N), torch.int32 if scale is None else torch.float32, A)
-    _check(load().dense_gemm_i8(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(C), M, N, K, _stream(A)))
+    with _on(A, Wt, scale, C):
+        _check(load().dense_gemm_i8(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(C), M, N, K, _stream(A)))
     return C
 
 
@@ -339,7 +360,9 @@ def dense_gemm_i8_out(A, Wt, scale, bias=None, out_type="f16", out=None):
     code, dt = _out_kind(out_type)
     _epilogue_args(N, scale, bias)
     C = _out(out, (M, N), dt, A)
-    _check(load().dense_gemm_i8_out(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(bias), _ptr(C), code, M, N, K, _stream(A)))
+    with _on(A, Wt, scale, bias, C):
+        _check(load().dense_gemm_i8_out(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(bias), _ptr(C), code, M, N, K,
+                                        _stream(A)))
     return C
 
 
@@ -354,8 +377,9 @@ def w24_gemm_i8_out(A, vals, meta, scale, bias=None, out_type="f16", out=None):
     code, dt = _out_kind(out_type)
     _epilogue_args(N, scale, bias)
     C = _out(out, (M, N), dt, A)
-    _check(load().w24_gemm_i8_out(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), _ptr(bias), _ptr(C), code,
-                                  M, N, K, _stream(A)))
+    with _on(A, vals, meta, scale, bias, C):
+        _check(load().w24_gemm_i8_out(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), _ptr(bias), _ptr(C), code,
+                                      M, N, K, _stream(A)))
     return C
 
 
@@ -368,7 +392,8 @@ def w24_gemm_f16(A, vals, meta, out=None):
     _dev(vals, torch.float16, (N, K // 2), "vals")
     _dev(meta, torch.int32, (N, -(-K // 32)), "meta")
     C = _out(out, (M, N), torch.float16, A)
-    _check(load().w24_gemm_f16(_ptr(A), _ptr(vals), _ptr(meta), _ptr(C), M, N, K, _stream(A)))
+    with _on(A, vals, meta, C):
+        _check(load().w24_gemm_f16(_ptr(A), _ptr(vals), _ptr(meta), _ptr(C), M, N, K, _stream(A)))
     return C
 
 
@@ -382,7 +407,8 @@ def w24_gemm_i8(A, vals, meta, scale=None, out=None):
     if scale is not None:
         _dev(scale, torch.float32, (N,), "scale")
     C = _out(out, (M, N), torch.int32 if scale is None else torch.float32, A)
-    _check(load().w24_gemm_i8(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), _ptr(C), M, N, K, _stream(A)))
+    with _on(A, vals, meta, scale, C):
+        _check(load().w24_gemm_i8(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), _ptr(C), M, N, K, _stream(A)))
     return C
 
 
@@ -398,9 +424,10 @@ def tw_gemm_f16(At, packed: TwPacked, out=None):
     for key in ("offset_k", "offset_n", "v_ptr", "k_ptr", "n_ptr", "tile_order"):
         _dev(arrs[key], torch.int32, None, key)
     C = _out(out, (M, packed.N), torch.float16, At)
-    _check(load().tw_gemm_f16(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
-                              _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]),
-                              _ptr(arrs["tile_order"]), packed.T, packed.G, _ptr(C), M, packed.N, K, _stream(At)))
+    with _on(At, C, *arrs.values()):
+        _check(load().tw_gemm_f16(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
+                                  _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]),
+                                  _ptr(arrs["tile_order"]), packed.T, packed.G, _ptr(C), M, packed.N, K, _stream(At)))
     return C
 
 
@@ -420,10 +447,11 @@ def tw_gemm_i8(At, packed: TwPacked, scale, bias=None, out_type="f16", out=None)
     code, dt = _out_kind(out_type)
     _epilogue_args(packed.N, scale, bias)
     C = _out(out, (M, packed.N), dt, At)
-    _check(load().tw_gemm_i8(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
-                             _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]), _ptr(arrs["tile_order"]),
-                             packed.T, packed.G, _ptr(scale), _ptr(bias), _ptr(C), code, M, packed.N, K,
-                             _stream(At)))
+    with _on(At, C, scale, bias, *arrs.values()):
+        _check(load().tw_gemm_i8(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
+                                 _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]),
+                                 _ptr(arrs["tile_order"]), packed.T, packed.G, _ptr(scale), _ptr(bias), _ptr(C),
+                                 code, M, packed.N, K, _stream(At)))
     return C
 
 
@@ -454,10 +482,11 @@ def tw_gemm_f16_ex(At, packed: TwPacked, t_first=0, t_count=None, out_t=False, a
         _dev(arrs[key], torch.int32, None, key)
     C = _out(out, (packed.N, M) if out_t else (M, packed.N), torch.float16, At)
     flags = (SSG_TW_OUT_T if out_t else 0) | (SSG_TW_A_ROWMAJOR if a_rowmajor else 0)
-    _check(load().tw_gemm_f16_ex(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
-                                 _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]),
-                                 _ptr(arrs["tile_order"]), packed.T, packed.G, int(t_first), int(t_count),
-                                 flags, _ptr(C), M, packed.N, K, _stream(At)))
+    with _on(At, C, *arrs.values()):
+        _check(load().tw_gemm_f16_ex(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
+                                     _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]),
+                                     _ptr(arrs["tile_order"]), packed.T, packed.G, int(t_first), int(t_count),
+                                     flags, _ptr(C), M, packed.N, K, _stream(At)))
     return C
 
 
@@ -485,5 +514,6 @@ def ssg_transpose_f16(A, out=None):
     M, K = A.shape
     _dev(A, torch.float16, (M, K), "A")
     At = _out(out, (K, M), torch.float16, A)
-    _check(load().ssg_transpose_f16(_ptr(A), _ptr(At), M, K, _stream(A)))
+    with _on(A, At):
+        _check(load().ssg_transpose_f16(_ptr(A), _ptr(At), M, K, _stream(A)))
     return At

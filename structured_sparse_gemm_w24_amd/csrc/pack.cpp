@@ -228,11 +228,19 @@ int tw_unpack(const char *fn, const T *vals, const int32_t *offset_k, const int3
     if (!W || !v_ptr || !k_ptr || !n_ptr) return ssg::fail(SSG_EINVAL, "%s: null pointer", fn);
     if (K <= 0 || N <= 0 || G <= 0) return ssg::fail(SSG_EINVAL, "%s: bad shape", fn);
     const int64_t T_ = (N + G - 1) / G;
+    if (v_ptr[0] != 0 || k_ptr[0] != 0 || n_ptr[0] != 0)
+        return ssg::fail(SSG_EINVAL, "%s: prefix sums must start at 0", fn);
     for (int64_t t = 0; t < T_; ++t) {
         const int64_t kt = k_ptr[t + 1] - k_ptr[t], nt = n_ptr[t + 1] - n_ptr[t];
         const int64_t g = std::min<int64_t>(G, N - t * G);
         if (kt < 0 || nt < 0 || v_ptr[t + 1] - v_ptr[t] != nt * tw_ld<T>(kt))
             return ssg::fail(SSG_EINVAL, "%s: inconsistent pointers at tile %lld", fn, (long long)t);
+    }
+    if ((k_ptr[T_] && !offset_k) || (n_ptr[T_] && !offset_n) || (v_ptr[T_] && !vals))
+        return ssg::fail(SSG_EINVAL, "%s: null array with nonzero length", fn);
+    for (int64_t t = 0; t < T_; ++t) {
+        const int64_t kt = k_ptr[t + 1] - k_ptr[t], nt = n_ptr[t + 1] - n_ptr[t];
+        const int64_t g = std::min<int64_t>(G, N - t * G);
         for (int64_t kk = 0; kk < kt; ++kk)
             if (offset_k[k_ptr[t] + kk] < 0 || offset_k[k_ptr[t] + kk] >= K)
                 return ssg::fail(SSG_EINVAL, "%s: offset_k out of range in tile %lld", fn, (long long)t);

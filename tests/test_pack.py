@@ -152,3 +152,30 @@ def test_tw_unpack_rejects_inconsistent_pointers(lib):
     p.v_ptr[1] += 1
     with pytest.raises(lib.SsgError, match="inconsistent"):
         lib.tw_unpack_f16(p)
+
+
+def test_tw_unpack_rejects_bad_prefix_sums_and_lengths(lib):
+    import copy
+    case = wl.random_tw_f16(np.random.default_rng(4), 1, 32, 32, 16, 0.5)
+    p0 = lib.tw_pack_f16(case["Wp"], 16)
+    p = copy.copy(p0)
+    p.k_ptr = p0.k_ptr - 1  # every tile keeps its size, but the sums start at -1
+    with pytest.raises(lib.SsgError, match="start at 0"):
+        lib.tw_unpack_f16(p)
+    p = copy.copy(p0)
+    p.n_ptr = p0.n_ptr[:-1]
+    with pytest.raises(ValueError, match="T\\+1"):
+        lib.tw_unpack_f16(p)
+    p = copy.copy(p0)
+    p.offset_k = p0.offset_k[:-1]
+    with pytest.raises(ValueError, match="shorter"):
+        lib.tw_unpack_f16(p)
+    # raw C ABI: a null offset array with a nonzero length is refused
+    raw = lib.load()
+    import ctypes as ct
+    W = np.empty((32, 32), np.float16)
+    arrs = [np.ascontiguousarray(a) for a in (p0.vals, p0.offset_k, p0.offset_n, p0.v_ptr, p0.k_ptr, p0.n_ptr)]
+    ptrs = [a.ctypes.data_as(ct.c_void_p) for a in arrs]
+    ptrs[1] = None
+    rc = raw.tw_unpack_f16(*ptrs, 32, 32, 16, W.ctypes.data_as(ct.c_void_p))
+    assert rc == 1 and "null array" in raw.ssg_last_error().decode()
