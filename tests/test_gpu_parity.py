@@ -607,3 +607,54 @@ def test_zero_tokens_is_noop(lib, gpu):
     vals, meta = lib.w24_pack_f16(np.zeros((128, 64), np.float16))
     C = lib.w24_gemm_f16(A, T(vals), meta_t(meta))
     assert C.shape == (0, 64)
+
+
+# ---------------------------------------------------------------- randomised shapes
+# A fixed, seeded draw of shapes inside each entry point's documented limits
+# (2:4: K % 128 == 0 for int8 and % 64 for fp16, N % 64 == 0, any M; tile-wise:
+# N % G == 0, G % 16 == 0, M % 8 (fp16) or % 16 (int8)), so tile-path choices,
+# ragged token tails and K lengths not used elsewhere are all exercised.
+def _random_shapes(seed, n, k_mult, m_mult, g_choices=None):
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(r.integers(1, 3000)) // m_mult * m_mult or m_mult
+        K = int(r.integers(1, 24)) * k_mult
+        if g_choices is None:
+            out.append((M, K, int(r.integers(1, 40)) * 64))
+        else:
+            G = int(r.choice(g_choices))
+            out.append((M, K, int(r.integers(1, 24)) * G, G, float(r.uniform(0.05, 0.9))))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N", _random_shapes(101, 6, 64, 1))
+def test_w24_f16_random_shapes(lib, gpu, M, K, N):
+    case = wl.random_24_f16(np.random.default_rng(M + K + N), M, K, N)
+    check_f16(run_w24_f16(lib, case["A"], case["Wp"]), case["A"], case["Wp"], K // 2, f"2:4 f16 {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M,K,N", _random_shapes(102, 6, 128, 1))
+def test_w24_i8_random_shapes(lib, gpu, M, K, N):
+    case = wl.random_24_i8(np.random.default_rng(M + K + N), M, K, N)
+    C = run_w24_i8(lib, case["A"], case["Wp"], case["scale"])
+    assert np.array_equal(C.view(np.uint32), oracle.ref_gemm_i8(case["A"], case["Wp"], case["scale"]).view(np.uint32))
+    Cd = H(lib.dense_gemm_i8(T(case["A"]), T(case["W"].T), T(case["scale"])))
+    assert np.array_equal(Cd.view(np.uint32), oracle.ref_gemm_i8(case["A"], case["W"], case["scale"]).view(np.uint32))
+
+
+@pytest.mark.parametrize("M,K,N,G,d", _random_shapes(103, 6, 8, 8, [16, 32, 64, 128]))
+def test_tw_random_shapes(lib, gpu, M, K, N, G, d):
+    case = wl.random_tw_f16(np.random.default_rng(M + K + N), M, K, N, G, d)
+    packed = lib.tw_pack_f16(case["Wp"], G)
+    n_terms = int(max(np.diff(packed.k_ptr).max(), 1))
+    check_f16(run_tw(lib, case["A"], case["Wp"], G), case["A"], case["Wp"], n_terms, f"TW {M}x{K}x{N} G={G}")
+
+
+@pytest.mark.parametrize("M,K,N,G,d", _random_shapes(104, 4, 16, 16, [16, 64, 128]))
+def test_tw_i8_random_shapes(lib, gpu, M, K, N, G, d):
+    rng = np.random.default_rng(M + K + N)
+    case = wl.random_tw_i8(rng, M, K, N, G, d)
+    C = run_tw_i8(lib, case["A"], case["Wp"], G, case["scale"], None, "f32")
+    ref = oracle.ref_gemm_i8_out(case["A"], case["Wp"], case["scale"], None, "f32")
+    assert np.array_equal(C.view(np.uint32), ref.view(np.uint32))
