@@ -338,8 +338,8 @@ def main(argv=None):
     if a.summarize_profile:
         return summarize_profile(a)
     if a.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {a.gpus}); the sparse GEMM "
-              "is measured on one GPU's share and multi-GPU sharding is not part of it", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}): the sparse GEMM is timed on one "
+              "GPU's share of the work, and sharding it across GPUs is not implemented", file=sys.stderr)
         return 2
 
     import torch

@@ -13,11 +13,13 @@ The dense kernels only need that element e of a lane's row operand and of its
 column operand refer to the same k, plus the accumulator layout.
 
 On a mismatch the test writes basis experiments (one 1 in the sparse operand,
-distinct ids in the dense operand) to gpurun_out/ for offline decoding.
+distinct ids in the dense operand) to the directory named by SSG_PROBE_DUMP (or
+the system temporary directory) for offline decoding.
 """
 
 import ctypes as ct
 import os
+import tempfile
 
 import numpy as np
 import pytest
@@ -122,7 +124,7 @@ def dump_discovery(probe, op):
     rng = np.random.default_rng(99)
     ridx = np.stack([random_idx(rng, na // 2) for _ in range(E)])
     d_rand = run(probe, op, a, b, ridx)
-    out = os.path.join(ROOT, "gpurun_out")
+    out = os.environ.get("SSG_PROBE_DUMP") or tempfile.gettempdir()
     os.makedirs(out, exist_ok=True)
     path = os.path.join(out, f"isa_discovery_op{op}.npz")
     np.savez(path, a=a, b=b, idx_fixed=fixed, d_fixed=d_fixed, idx_rand=ridx, d_rand=d_rand)
