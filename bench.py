@@ -124,6 +124,18 @@ class Timer:
                     replays=reps)  # ms per call
 
 
+def host_time_ms(fn, reps=3):
+    """Median wall time of a host call (the pack stage runs offline, outside the
+    timed GPU region; it is reported beside it)."""
+    ts = []
+    out = None
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        out = fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)) * 1e3, out
+
+
 def rotation(bytes_per_set):
     return max(2, int(np.ceil(2 * CACHE_BYTES / max(1, bytes_per_set))))
 
@@ -132,7 +144,7 @@ def rotation(bytes_per_set):
 def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, with_f16_dense=False):
     dev = torch.device("cuda")
     M, K, N = c["M"], c["K"], c["N"]
-    vals, meta = ssg.w24_pack_i8(c["Wp"])
+    t_pack, (vals, meta) = host_time_ms(lambda: ssg.w24_pack_i8(c["Wp"]))
     sets_bytes = perf.w24_bytes(M, N, K, 1, 1, 4, scale=True)
     R = rotation(sets_bytes) if rotate else 1
     A0 = torch.from_numpy(c["A"]).to(dev)
@@ -150,7 +162,7 @@ def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, with_f16
     st = timer.stats(sp, steps, warmup)
     t_de = timer(de, steps, warmup)
     out = dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"], t_dense_ms=t_de,
-               rotate_sets=R, sets=sets)
+               rotate_sets=R, t_pack_host_ms=t_pack, sets=sets)
     if with_f16_dense:
         # the same shape through the fp16 dense kernel (int8 values are exact in fp16)
         for d in sets:
@@ -211,7 +223,7 @@ def tw_i8_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate=True)
 def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
     dev = torch.device("cuda")
     M, K, N = c["M"], c["K"], c["N"]
-    vals, meta = ssg.w24_pack_f16(c["Wp"])
+    t_pack, (vals, meta) = host_time_ms(lambda: ssg.w24_pack_f16(c["Wp"]))
     R = rotation(perf.w24_bytes(M, N, K, 2, 2, 2)) if rotate else 1
     sets = [dict(A=torch.from_numpy(c["A"]).to(dev), vals=torch.from_numpy(vals).to(dev),
                  meta=torch.from_numpy(meta.view(np.int32)).to(dev),
@@ -222,13 +234,14 @@ def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
     tm = lambda i: torch.matmul(sets[i % R]["A"], sets[i % R]["Wt"].T)
     st = timer.stats(sp, steps, warmup)
     return dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
-                t_dense_ms=timer(de, steps, warmup), t_torch_ms=timer(tm, steps, warmup), rotate_sets=R)
+                t_dense_ms=timer(de, steps, warmup), t_torch_ms=timer(tm, steps, warmup), rotate_sets=R,
+                t_pack_host_ms=t_pack)
 
 
 def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, extras=True):
     dev = torch.device("cuda")
     M, K, N, G = c["M"], c["K"], c["N"], c["G"]
-    host = ssg.tw_pack_f16(c["Wp"], G)
+    t_pack, host = host_time_ms(lambda: ssg.tw_pack_f16(c["Wp"], G))
     union = int(np.unique(host.offset_k).size)
     bytes_ = perf.tw_bytes(M, N, union, host.vals.size, host.offset_k.size, host.offset_n.size, host.T)
     R = rotation(bytes_ + M * K * 2) if rotate else 1
@@ -245,7 +258,7 @@ def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, extras=True)
     out = dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
                t_transpose_ms=timer(tr, steps, warmup), t_dense_ms=timer(de, steps, warmup),
                t_torch_ms=timer(tm, steps, warmup), rotate_sets=R, bytes=bytes_, ops=perf.tw_ops(M, nnz),
-               union_rows=union)
+               union_rows=union, t_pack_host_ms=t_pack)
     if not extras:
         return out
     # fused transpose: the same GEMM writing Ct [N][M], the next tile-wise layer's At
@@ -394,6 +407,7 @@ def main(argv=None):
         "dense_equivalent_tops": de / t / 1e12,
         "speedup_vs_dense": perf.speedup(r["t_dense_ms"], r["t_sparse_ms"]),
         "dense_i8_ms": r["t_dense_ms"],
+        "pack_host_ms": r["t_pack_host_ms"],
         "timing": f"HIP graph of the {a.steps} timed steps replayed on one stream, HIP events around each replay; "
                   f"median of {HEADLINE_REPLAYS} replays (p10 / p90 beside)",
         "replays": HEADLINE_REPLAYS,
