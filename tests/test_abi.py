@@ -110,3 +110,45 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_LIB", None)
     with pytest.raises(RuntimeError, match="missing"):
         L.w24_pack_f16(np.zeros((4, 1), np.float16))
+
+
+def test_concurrent_packs_and_thread_local_errors(lib):
+    """Host calls are re-entrant: packs from several threads at once give the
+    sequential results, and each thread's ssg_last_error() reports its own
+    call (a failing pack on one thread does not overwrite another's message)."""
+    import threading
+
+    import workloads as wl
+
+    raw = lib.load()
+    cases = [wl.random_24_i8(np.random.default_rng(s), 1, 256, 192)["Wp"] for s in range(8)]
+    want = [lib.w24_pack_i8(W) for W in cases]
+    got = [None] * len(cases)
+    errors = [None] * len(cases)
+    bad = np.ones((8, 64), np.int8)  # four nonzeros per group: not 2:4
+
+    def work(i):
+        for _ in range(20):
+            got[i] = lib.w24_pack_i8(cases[i])
+            if i % 2:
+                vals = np.empty((64, 4), np.int8)
+                meta = np.empty((64, 1), np.uint32)
+                rc = raw.w24_pack_i8(bad.ctypes.data_as(ct.c_void_p), 8, 64, vals.ctypes.data_as(ct.c_void_p),
+                                     meta.ctypes.data_as(ct.c_void_p))
+                errors[i] = (rc, raw.ssg_last_error().decode())
+            else:
+                rc = raw.ssg_version()
+                errors[i] = (0, raw.ssg_last_error().decode())
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for i in range(len(cases)):
+        assert np.array_equal(got[i][0], want[i][0]) and np.array_equal(got[i][1], want[i][1])
+        rc, msg = errors[i]
+        if i % 2:
+            assert rc == 2 and "nonzeros" in msg
+        else:
+            assert msg == ""  # the last call on this thread (a successful pack) cleared it
