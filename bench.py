@@ -676,7 +676,9 @@ def table(a, torch, ssg, perf, wl, timer):
         emit(dict(workload=c["name"] + "_w24_f16", shape=[c["M"], c["K"], c["N"]], **r,
                   tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
                   speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
-                  speedup_vs_best_dense=min(r["t_dense_ms"], r["t_torch_ms"]) / r["t_sparse_ms"]))
+                  speedup_vs_best_dense=min(r["t_dense_ms"], r["t_torch_ms"]) / r["t_sparse_ms"],
+                  **perf.bound_report(nz, perf.w24_bytes(c["M"], c["N"], c["K"], 2, 2, 2), r["t_sparse_ms"],
+                                      perf.PEAK_F16_TFLOPS * 1e12)))
     if "vit_base_fc1" in want:
         c = wl.make_vit_base_fc1_i8()
         r = w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate, with_f16_dense=True)
@@ -686,14 +688,16 @@ def table(a, torch, ssg, perf, wl, timer):
         emit(dict(workload=c["name"] + "_w24_i8", shape=[c["M"], c["K"], c["N"]], **r,
                   tops_nonzero=nz / r["t_sparse_ms"] / 1e9, tops_dense_eq=de / r["t_sparse_ms"] / 1e9,
                   gbs=b / r["t_sparse_ms"] / 1e6, speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
-                  speedup_vs_dense_f16=r["t_dense_f16_ms"] / r["t_sparse_ms"]))
+                  speedup_vs_dense_f16=r["t_dense_f16_ms"] / r["t_sparse_ms"],
+                  **perf.bound_report(nz, b, r["t_sparse_ms"], perf.PEAK_I8_TOPS * 1e12)))
         torch.cuda.empty_cache()
         for out_type in ("f16", "i8"):
             r = w24_i8_out_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate)
             b = perf.w24_bytes(c["M"], c["N"], c["K"], 1, 1, r["out_bytes"], True)
             emit(dict(workload=f"vit_base_fc1_w24_i8_{out_type}_out", shape=[c["M"], c["K"], c["N"]], **r,
                       tops_nonzero=nz / r["t_sparse_ms"] / 1e9, tops_dense_eq=de / r["t_sparse_ms"] / 1e9,
-                      gbs=b / r["t_sparse_ms"] / 1e6, speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"]))
+                      gbs=b / r["t_sparse_ms"] / 1e6, speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
+                      **perf.bound_report(nz, b, r["t_sparse_ms"], perf.PEAK_I8_TOPS * 1e12)))
             torch.cuda.empty_cache()
     tw_cases = []
     if "bert_base_fc1" in want:
@@ -707,7 +711,8 @@ def table(a, torch, ssg, perf, wl, timer):
                   tflops_nonzero=r["ops"] / r["t_sparse_ms"] / 1e9, gbs=r["bytes"] / r["t_sparse_ms"] / 1e6,
                   speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
                   speedup_vs_best_dense=min(r["t_dense_ms"], r["t_torch_ms"]) / r["t_sparse_ms"],
-                  speedup_vs_dense_incl_transpose=r["t_dense_ms"] / (r["t_sparse_ms"] + r["t_transpose_ms"])))
+                  speedup_vs_dense_incl_transpose=r["t_dense_ms"] / (r["t_sparse_ms"] + r["t_transpose_ms"]),
+                  **perf.bound_report(r["ops"], r["bytes"], r["t_sparse_ms"], perf.PEAK_F16_TFLOPS * 1e12)))
         torch.cuda.empty_cache()
     if "patterns" in want:
         patterns(torch, ssg, perf, wl, timer, steps, warmup, emit)
@@ -730,7 +735,9 @@ def table(a, torch, ssg, perf, wl, timer):
             emit(dict(workload=g["name"] + "_w24_f16", shape=[g["M"], g["K"], g["N"]], **r,
                       tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
                       speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
-                      speedup_vs_best_dense=min(r["t_dense_ms"], r["t_torch_ms"]) / r["t_sparse_ms"]))
+                      speedup_vs_best_dense=min(r["t_dense_ms"], r["t_torch_ms"]) / r["t_sparse_ms"],
+                      **perf.bound_report(nz, perf.w24_bytes(g["M"], g["N"], g["K"], 2, 2, 2), r["t_sparse_ms"],
+                                          perf.PEAK_F16_TFLOPS * 1e12)))
             torch.cuda.empty_cache()
     if "vit_large_stack" in want:
         f16 = vit_large_stack(torch, ssg, perf, wl, "f16", timer)

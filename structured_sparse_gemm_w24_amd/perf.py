@@ -66,3 +66,13 @@ def transpose_bytes(M, K):
 def roofline(achieved, peak, unit, bound, traffic=None):
     return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
             "frac": achieved / peak, "traffic": traffic}
+
+
+def bound_report(ops, bytes_, t_ms, peak_ops):
+    """Ideal times at the MFMA peak (peak_ops, ops/s) and at the HBM peak, the
+    bound that binds (the larger), and the roofline fraction ideal / measured."""
+    t_mfma = ops / peak_ops
+    t_hbm = bytes_ / (PEAK_HBM_GBS * 1e9)
+    t = t_ms * 1e-3
+    return {"t_ideal_mfma_us": t_mfma * 1e6, "t_ideal_hbm_us": t_hbm * 1e6,
+            "bound": "mfma" if t_mfma >= t_hbm else "hbm", "roofline_frac": max(t_mfma, t_hbm) / t}

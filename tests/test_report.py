@@ -58,3 +58,18 @@ def test_work_models_closed_form():
     assert perf.transpose_bytes(3, 5) == 60
     r = perf.roofline(4000.0, perf.PEAK_HBM_GBS, "GB/s", "hbm")
     assert r["frac"] == 0.5 and r["traffic"] is None
+
+
+def test_bound_report_matches_the_closed_forms():
+    # 2:4 int8 at 12608x768x3072 with fp32 output: 29.7 G nonzero ops at 5 POP/s
+    # is 5.95 us, 166.1 MB at 8 TB/s is 20.76 us, so HBM binds
+    nz, _ = perf.w24_ops(12608, 3072, 768)
+    r = perf.bound_report(nz, perf.w24_bytes(12608, 3072, 768, 1, 1, 4, scale=True), 0.04152,
+                          perf.PEAK_I8_TOPS * 1e12)
+    assert r["bound"] == "hbm"
+    assert abs(r["t_ideal_hbm_us"] - 20.762) < 0.01 and abs(r["t_ideal_mfma_us"] - 5.949) < 0.01
+    assert abs(r["roofline_frac"] - 0.5) < 1e-3
+    # 2:4 fp16 ViT-L qkv 4096x1024x3072: MFMA binds (5.15 us vs 4.64 us)
+    nz, _ = perf.w24_ops(4096, 3072, 1024)
+    r = perf.bound_report(nz, perf.w24_bytes(4096, 3072, 1024, 2, 2, 2), 0.0103, perf.PEAK_F16_TFLOPS * 1e12)
+    assert r["bound"] == "mfma" and abs(r["roofline_frac"] - 0.5) < 1e-3
