@@ -178,14 +178,14 @@ __device__ __forceinline__ void store16(void *p, u32x4 v) {
 
 // Tile configuration: WM x WN waves, TM x TN 32x32 blocks per wave, STAGES
 // LDS stage buffers (prefetch distance), GM tile-rows per L2 group,
-// nontemporal C stores.  Direct-to-LDS loads are issued by every wave: their
+// nontemporal C stores, ROT: each tile starts its K loop at its own stage.  Direct-to-LDS loads are issued by every wave: their
 // throughput is limited per wavefront (about 4 bytes per clock each on
 // gfx950), so a CU needs 8 or more issuing waves to feed the sparse matrix
 // cores.
-template <int WM_, int WN_, int TM_, int TN_, int STAGES_, int GM_, bool NTS_>
+template <int WM_, int WN_, int TM_, int TN_, int STAGES_, int GM_, bool NTS_, bool ROT_>
 struct Cfg {
     static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_, STAGES = STAGES_, GM = GM_;
-    static constexpr bool NTS = NTS_;
+    static constexpr bool NTS = NTS_, ROT = ROT_;
 };
 
 template <int KIND, class CF>
@@ -283,13 +283,15 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     }
     const uint8_t *meta_b = reinterpret_cast<const uint8_t *>(meta);
 
-    // Row pitches are often powers of two (K = 1024, 4096), so one stage's
-    // 128-byte slice of every row falls into the same few memory channels.
-    // The K reduction may run in any order, so each tile starts at its own
-    // stage (rotation by tile id): at any moment the tiles in flight read
-    // different K slices and spread over all channels.  The order is fixed per
-    // tile, so results stay deterministic.
-    const int rot = b % S;
+    // Where a tile starts its K loop.  From stage 0, the tiles in flight on an
+    // XCD read the same K slice at about the same time, so one L2 fill serves
+    // several of them; rotated (tile b starts at stage b mod S), they read
+    // different slices, which spreads their requests over more memory
+    // channels but gives up that sharing.  The K reduction may run in any
+    // order, and the order is fixed per tile, so results stay deterministic
+    // either way.  Which one is faster was measured per tile shape on MI355X
+    // (ROT in the tile configurations below).
+    const int rot = CF::ROT ? b % S : 0;
     // (the host caps A and W below 4 GiB, so every byte count fits 32 bits)
     const __amdgpu_buffer_rsrc_t bufA = buffer_of(A, uint32_t(int64_t(M) * a_row));
     const __amdgpu_buffer_rsrc_t bufW = buffer_of(Wv, uint32_t(int64_t(N) * w_row));
@@ -514,16 +516,24 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 //   Small2 128 x 128, 4 waves, 2 stages (three int8 workgroups per CU) --
 //          short-K int8 GEMMs whose Mid tiles would fill the chip more than
 //          twice or less than once, and the dense int8 GEMMs at short K.
+// K-loop start (ROT), measured with both variants timed in one process over
+// alternating rounds, on input sets rotated through more than twice the
+// 256 MB Infinity Cache: every dense kind and the sparse Big and Mid tiles run
+// 3-10 % faster from stage 0 (ViT-L qkv / fc1 / fc2, 4096x8192x1024,
+// 4096x2048x4096), while the sparse 128 x 128 tiles run 4-10 % faster rotated
+// (fp16 ViT-L fc2 42.1 vs 46.2 us, int8 4096x8192x1024 43.7 vs 47.7 us; the
+// short-K int8 one is within noise either way).  So ROT = sparse kind on a
+// 128 x 128 tile.
 template <bool NTS>
-using CfgBig = Cfg<4, 2, 2, 4, 3, 8, NTS>;
+using CfgBig = Cfg<4, 2, 2, 4, 3, 8, NTS, false>;
 template <bool NTS>
-using CfgBigDense = Cfg<4, 2, 2, 4, 2, 8, NTS>;
+using CfgBigDense = Cfg<4, 2, 2, 4, 2, 8, NTS, false>;
 template <bool NTS>
-using CfgMid = Cfg<2, 2, 2, 4, 2, 8, NTS>;
-template <bool NTS>
-using CfgSmall = Cfg<2, 2, 2, 2, 3, 8, NTS>;
-template <bool NTS>
-using CfgSmall2 = Cfg<2, 2, 2, 2, 2, 8, NTS>;
+using CfgMid = Cfg<2, 2, 2, 4, 2, 8, NTS, false>;
+template <bool NTS, bool ROT>
+using CfgSmall = Cfg<2, 2, 2, 2, 3, 8, NTS, ROT>;
+template <bool NTS, bool ROT>
+using CfgSmall2 = Cfg<2, 2, 2, 2, 2, 8, NTS, ROT>;
 
 enum Shape { SHAPE_BIG, SHAPE_MID, SHAPE_SMALL, SHAPE_SMALL2 };
 
@@ -561,8 +571,10 @@ static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const ui
     }
     if (sh == SHAPE_MID) return launch<KIND, EPI, CfgMid<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
     if constexpr (KindTraits<KIND>::kI8)  // (only the int8 kinds pick Small2)
-        if (sh == SHAPE_SMALL2) return launch<KIND, EPI, CfgSmall2<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
-    return launch<KIND, EPI, CfgSmall<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
+        if (sh == SHAPE_SMALL2)
+            return launch<KIND, EPI, CfgSmall2<NTS, KindTraits<KIND>::kSparse>>(A, Wv, meta, scale, bias, C, M, N, K,
+                                                                                st);
+    return launch<KIND, EPI, CfgSmall<NTS, KindTraits<KIND>::kSparse>>(A, Wv, meta, scale, bias, C, M, N, K, st);
 }
 
 hipError_t launch_dense_f16(const void *A, const void *Wt, void *C, int M, int N, int K, hipStream_t st) {
