@@ -1,0 +1,84 @@
+"""Register, LDS and scratch budget of every gfx950 kernel (host-only check).
+
+Compiles the kernel sources to gfx950 assembly and reads each kernel's
+descriptor: the LDS it reserves, its unified VGPR + AGPR count and its
+private (scratch) segment.  The tile configurations are chosen for a target
+number of resident workgroups per CU, set by LDS (160 KiB per CU); the
+registers must never be the tighter limit (512 per SIMD lane, allocated in
+granules of 8, shared by the waves a workgroup places on each of the 4
+SIMDs), and no kernel may spill to scratch.  A few extra registers in a
+kernel near a boundary halve its occupancy without any other symptom.
+"""
+
+import math
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KDIR = os.path.join(ROOT, "structured_sparse_gemm_w24_amd", "csrc", "kernels")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SOURCES = ("gemm.hip", "tw_gemm.hip", "tw_gemm_i8.hip", "transpose.hip")
+
+LDS_PER_CU = 160 * 1024
+VGPRS_PER_SIMD_LANE = 512
+VGPR_GRANULE = 8
+SIMDS_PER_CU = 4
+
+
+def _kernels(asm):
+    """name -> {lds, vgpr, scratch, wg} from one assembly file."""
+    out = {}
+    for m in re.finditer(r"^\s*\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", asm, re.M | re.S):
+        body = m.group(2)
+        val = lambda k: int(re.search(r"\.amdhsa_" + k + r"\s+(\d+)", body).group(1))
+        out[m.group(1)] = dict(lds=val("group_segment_fixed_size"), vgpr=val("next_free_vgpr"),
+                               scratch=val("private_segment_fixed_size"))
+    for m in re.finditer(r"\.max_flat_workgroup_size:\s*(\d+)\s*\n(?:.*\n){0,40}?\s*\.name:\s*(\S+)", asm):
+        if m.group(2) in out:
+            out[m.group(2)]["wg"] = int(m.group(1))
+    return out
+
+
+@pytest.fixture(scope="module")
+def kernels():
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    found = {}
+    with tempfile.TemporaryDirectory() as d:
+        for src in SOURCES:
+            out = os.path.join(d, src + ".s")
+            cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+                   "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                   "-Wno-unused-command-line-argument", os.path.join(KDIR, src), "-o", out]
+            p = subprocess.run(cmd, capture_output=True, text=True)
+            assert p.returncode == 0, p.stderr
+            found.update(_kernels(open(out).read()))
+    return found
+
+
+def test_every_kernel_was_found(kernels):
+    assert sum("gemm_kernel" in k for k in kernels) >= 20
+    assert any("tw_gemm_kernel" in k for k in kernels)
+    assert any("tw_gemm_i8_kernel" in k for k in kernels)
+    assert all("wg" in v for v in kernels.values()), [k for k, v in kernels.items() if "wg" not in v]
+
+
+def test_no_kernel_spills_to_scratch(kernels):
+    assert {k: v["scratch"] for k, v in kernels.items() if v["scratch"]} == {}
+
+
+def test_registers_never_limit_occupancy_below_lds(kernels):
+    bad = {}
+    for name, v in kernels.items():
+        waves_per_simd = math.ceil(v["wg"] // 64 / SIMDS_PER_CU)
+        alloc = -(-v["vgpr"] // VGPR_GRANULE) * VGPR_GRANULE
+        by_regs = (VGPRS_PER_SIMD_LANE // alloc) // waves_per_simd
+        by_lds = LDS_PER_CU // v["lds"] if v["lds"] else 8
+        if by_regs < min(by_lds, 8):
+            bad[name] = dict(v, workgroups_by_registers=by_regs, workgroups_by_lds=by_lds)
+    assert bad == {}
