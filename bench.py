@@ -21,6 +21,8 @@ import hashlib
 import json
 import os
 import platform
+import shutil
+import subprocess
 import sys
 import time
 
@@ -122,6 +124,98 @@ class Timer:
         t = np.array(times)
         return dict(ms=float(np.median(t)), p10=float(np.percentile(t, 10)), p90=float(np.percentile(t, 90)),
                     replays=reps)  # ms per call
+
+
+def _gfx_clocks(node):
+    """Current clocks (MHz) of the gfx domains (one per XCD) in amd-smi's JSON."""
+    found = []
+    if isinstance(node, dict):
+        for k, v in node.items():
+            if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict):
+                try:
+                    found.append(float(v["clk"]["value"]))
+                except (TypeError, ValueError):
+                    pass
+            else:
+                found += _gfx_clocks(v)
+    elif isinstance(node, list):
+        for v in node:
+            found += _gfx_clocks(v)
+    return found
+
+
+def _gfx_activity(node):
+    """gfx_activity (%) from amd-smi's usage metrics, or None."""
+    if isinstance(node, dict):
+        v = node.get("gfx_activity")
+        if isinstance(v, dict) and "value" in v:
+            try:
+                return float(v["value"])
+            except (TypeError, ValueError):
+                return None
+        for w in node.values():
+            r = _gfx_activity(w)
+            if r is not None:
+                return r
+    elif isinstance(node, list):
+        for w in node:
+            r = _gfx_activity(w)
+            if r is not None:
+                return r
+    return None
+
+
+def observed_sclk(torch, fn, steps, warm_s=2.0, max_s=15.0):
+    """Shader clock read with `amd-smi metric -c` (run as a child process) while
+    the GPU replays a graph of `steps` calls of fn back to back; the GPU is kept
+    busy until amd-smi exits.  Returns the per-XCD clocks and their median, or
+    None when amd-smi is missing or fails.  The clock is power-managed, so it
+    is context for the roofline fraction, not a setting."""
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(stream)
+    g.replay()
+    torch.cuda.synchronize()
+    # the SMU's published metrics lag the load, so the GPU is kept busy for
+    # warm_s before amd-smi samples, and until it exits
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(4):
+            g.replay()
+        torch.cuda.synchronize()
+    proc = subprocess.Popen([exe, "metric", "-g", "0", "-c", "-u", "--json"], stdout=subprocess.PIPE,
+                            stderr=subprocess.DEVNULL)
+    t0 = time.perf_counter()
+    while proc.poll() is None and time.perf_counter() - t0 < max_s:
+        for _ in range(4):
+            g.replay()
+        torch.cuda.synchronize()
+    del g
+    try:
+        out, _ = proc.communicate(timeout=5.0)
+    except subprocess.TimeoutExpired:
+        proc.kill()
+        proc.communicate()
+        return None
+    if proc.returncode != 0:
+        return None
+    try:
+        doc = json.loads(out)
+    except ValueError:
+        return None
+    mhz = _gfx_clocks(doc)
+    if not mhz:
+        return None
+    return {"median_mhz": float(np.median(mhz)), "per_xcd_mhz": mhz, "gfx_activity_pct": _gfx_activity(doc),
+            "source": f"amd-smi metric -c -u, read after {warm_s:g} s of the timed graph replaying back to back"}
 
 
 def host_time_ms(fn, reps=3):
@@ -377,10 +471,11 @@ def main(argv=None):
     # timed region of exactly K steps); ms_per_step is the median replay
     timer.reps = HEADLINE_REPLAYS
     r = w24_i8_case(torch, ssg, perf, c, a.steps, a.warmup, timer, rotate=not a.warm)
-    t_eager = Timer(torch, graph=False, reps=HEADLINE_REPLAYS)(
-        lambda i: ssg.w24_gemm_i8(r["sets"][i % r["rotate_sets"]]["A"], r["sets"][i % r["rotate_sets"]]["vals"],
-                                  r["sets"][i % r["rotate_sets"]]["meta"], r["sets"][i % r["rotate_sets"]]["scale"],
-                                  out=r["sets"][i % r["rotate_sets"]]["C"]), a.steps, a.warmup)
+    step = lambda i: ssg.w24_gemm_i8(r["sets"][i % r["rotate_sets"]]["A"], r["sets"][i % r["rotate_sets"]]["vals"],
+                                     r["sets"][i % r["rotate_sets"]]["meta"], r["sets"][i % r["rotate_sets"]]["scale"],
+                                     out=r["sets"][i % r["rotate_sets"]]["C"])
+    t_eager = Timer(torch, graph=False, reps=HEADLINE_REPLAYS)(step, a.steps, a.warmup)
+    sclk = observed_sclk(torch, step, a.steps) if not a.eager else None
     nz, de = perf.w24_ops(M, N, K)
     t = r["t_sparse_ms"] / 1e3
     bytes_ = perf.w24_bytes(M, N, K, 1, 1, 4, scale=True)
@@ -414,6 +509,7 @@ def main(argv=None):
         "ms_per_step_p10": r["t_sparse_p10_ms"],
         "ms_per_step_p90": r["t_sparse_p90_ms"],
         "eager_ms_per_step": t_eager,
+        "sclk": sclk,
         "roofline": perf.roofline(achieved, perf.PEAK_HBM_GBS, "GB/s", "hbm", traffic),
         "cpu_baseline": None,
     }

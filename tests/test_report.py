@@ -73,3 +73,14 @@ def test_bound_report_matches_the_closed_forms():
     nz, _ = perf.w24_ops(4096, 3072, 1024)
     r = perf.bound_report(nz, perf.w24_bytes(4096, 3072, 1024, 2, 2, 2), 0.0103, perf.PEAK_F16_TFLOPS * 1e12)
     assert r["bound"] == "mfma" and abs(r["roofline_frac"] - 0.5) < 1e-3
+
+
+def test_gfx_clock_parser_reads_every_xcd_and_nothing_else():
+    import bench
+    doc = {"gpu_data": [{"gpu": 0, "clock": {
+        **{f"gfx_{i}": {"clk": {"value": 1400 + 10 * i, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"},
+                        "max_clk": {"value": 2400, "unit": "MHz"}, "clk_locked": "DISABLED"} for i in range(8)},
+        "mem_0": {"clk": {"value": 1900, "unit": "MHz"}},
+        "vclk_0": {"clk": {"value": 29, "unit": "MHz"}}}}]}
+    assert bench._gfx_clocks(doc) == [1400.0 + 10 * i for i in range(8)]
+    assert bench._gfx_clocks({"gpu_data": []}) == []
