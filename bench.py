@@ -753,7 +753,7 @@ def patterns(torch, ssg, perf, wl, timer, steps, warmup, emit):
 
 
 WORKLOADS = ("small", "vit_base_fc1", "bert_base_fc1", "bert_large_ffn", "vit_large", "vit_large_stack",
-             "bert_base_fc1_i8", "patterns")
+             "bert_base_fc1_i8", "patterns", "vit_large_shard8")
 
 
 def table(a, torch, ssg, perf, wl, timer):
@@ -834,6 +834,32 @@ def table(a, torch, ssg, perf, wl, timer):
                       speedup_vs_best_dense=min(r["t_dense_ms"], r["t_torch_ms"]) / r["t_sparse_ms"],
                       **perf.bound_report(nz, perf.w24_bytes(g["M"], g["N"], g["K"], 2, 2, 2), r["t_sparse_ms"],
                                           perf.PEAK_F16_TFLOPS * 1e12)))
+            torch.cuda.empty_cache()
+    if "vit_large_shard8" in want:
+        # one GPU's share of the ViT-L layer when the 4096 tokens are split over
+        # 8 GPUs (M = 512 rows each; the packed weights are replicated)
+        M8 = wl.VIT_LARGE_M // 8
+        for g in wl.vit_large_layers("f16", layers=1, M=M8):
+            r = w24_f16_case(torch, ssg, perf, g, steps, warmup, timer, rotate)
+            nz, de = perf.w24_ops(g["M"], g["N"], g["K"])
+            emit(dict(workload=g["name"].replace("vit_large_", "vit_large_shard8_") + "_w24_f16",
+                      shape=[g["M"], g["K"], g["N"]], **r,
+                      tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
+                      speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
+                      speedup_vs_best_dense=min(r["t_dense_ms"], r["t_torch_ms"]) / r["t_sparse_ms"],
+                      **perf.bound_report(nz, perf.w24_bytes(g["M"], g["N"], g["K"], 2, 2, 2), r["t_sparse_ms"],
+                                          perf.PEAK_F16_TFLOPS * 1e12)))
+            torch.cuda.empty_cache()
+        for g in wl.vit_large_layers("i8", layers=1, M=M8):
+            r = w24_i8_case(torch, ssg, perf, g, steps, warmup, timer, rotate)
+            r.pop("sets")
+            nz, de = perf.w24_ops(g["M"], g["N"], g["K"])
+            b = perf.w24_bytes(g["M"], g["N"], g["K"], 1, 1, 4, True)
+            emit(dict(workload=g["name"].replace("vit_large_", "vit_large_shard8_") + "_w24_i8",
+                      shape=[g["M"], g["K"], g["N"]], **r,
+                      tops_nonzero=nz / r["t_sparse_ms"] / 1e9, tops_dense_eq=de / r["t_sparse_ms"] / 1e9,
+                      speedup_vs_dense=r["t_dense_ms"] / r["t_sparse_ms"],
+                      **perf.bound_report(nz, b, r["t_sparse_ms"], perf.PEAK_I8_TOPS * 1e12)))
             torch.cuda.empty_cache()
     if "vit_large_stack" in want:
         f16 = vit_large_stack(torch, ssg, perf, wl, "f16", timer)

@@ -23,6 +23,7 @@ from .gen import (  # noqa: F401
     make_bert_base_fc1_tw_i8,
     make_bert_large_ffn_tw,
     vit_large_layers,
+    VIT_LARGE_M,
     prune24_magnitude,
     prune_tilewise,
     prune_blockwise,
