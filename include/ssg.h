@@ -210,6 +210,54 @@ int w24_gemm_i8_out(const int8_t *A, const int8_t *vals, const uint32_t *meta, c
                     const float *bias, void *C, int32_t out_type, int64_t M, int64_t N, int64_t K,
                     void *stream);
 
+/* ------------------------------------------------------------------------
+ * Split K, for GEMMs whose output tiles leave most of the chip idle (one
+ * GPU's share of a token-sharded layer, e.g. M = 512 rows).  The K loop of
+ * every output tile is cut into `splits` equal ranges run by separate
+ * workgroups; each writes its raw accumulators (fp32 for the fp16 kinds,
+ * int32 for the int8 kinds) to its [M][N] slice of the workspace, and a
+ * second kernel on the same stream sums the slices in split order and
+ * applies the kind's epilogue.  int8 results equal the unsplit calls' bit
+ * for bit (the int32 sum is the accumulator itself); fp16 results differ
+ * from theirs only in the fp32 summation order, within the same bound.  The
+ * pages' kernels split no reduction; this is a scheduling choice for
+ * MI355X's 256 CUs.
+ *
+ * kind: SSG_KIND_*.  splits: 1..64 and a divisor of the K stages (K/64 for
+ * the fp16 kinds, K/128 for the int8 kinds); splits == 1 runs the unsplit
+ * kernel and ignores ws.  ws: device memory of at least
+ * ssg_splitk_workspace_bytes(M, N, splits) bytes (ws_bytes says how many),
+ * 16-byte aligned, owned by the caller; its contents are ignored and
+ * overwritten, and nothing else may use it until this call's work on
+ * `stream` has completed.  Every other argument and rule as in the unsplit
+ * call of the same kind.  Nothing is allocated; errors as the unsplit calls
+ * (SSG_EINVAL for bad splits or a short or misaligned workspace).
+ * ------------------------------------------------------------------------ */
+enum { SSG_KIND_DENSE_F16 = 0, SSG_KIND_W24_F16 = 1, SSG_KIND_DENSE_I8 = 2, SSG_KIND_W24_I8 = 3 };
+
+/* Workspace bytes of a split call: splits * M * N * 4 (0 for splits <= 1 or
+ * negative sizes). */
+int64_t ssg_splitk_workspace_bytes(int64_t M, int64_t N, int32_t splits);
+
+/* The split count the library would take for a kind and shape: 1 (do not
+ * split) unless the output tiles fill at most half of the resident
+ * workgroup slots of a 256-CU MI355X; then the largest power of two <= 16
+ * whose split tiles still fit the slots once and leave every split at least
+ * 8 K stages.  Host-only; an invalid kind or shape gives 1. */
+int32_t ssg_splitk_suggest(int32_t kind, int64_t M, int64_t N, int64_t K);
+
+int dense_gemm_f16_splitk(const void *A, const void *Wt, void *C, int64_t M, int64_t N, int64_t K,
+                          int32_t splits, void *ws, int64_t ws_bytes, void *stream);
+int w24_gemm_f16_splitk(const void *A, const void *vals, const uint32_t *meta, void *C,
+                        int64_t M, int64_t N, int64_t K, int32_t splits, void *ws, int64_t ws_bytes,
+                        void *stream);
+int dense_gemm_i8_splitk(const int8_t *A, const int8_t *Wt, const float *scale, const float *bias,
+                         void *C, int32_t out_type, int64_t M, int64_t N, int64_t K, int32_t splits,
+                         void *ws, int64_t ws_bytes, void *stream);
+int w24_gemm_i8_splitk(const int8_t *A, const int8_t *vals, const uint32_t *meta, const float *scale,
+                       const float *bias, void *C, int32_t out_type, int64_t M, int64_t N, int64_t K,
+                       int32_t splits, void *ws, int64_t ws_bytes, void *stream);
+
 /* Tile-wise GEMM, fp16 in, fp32 accumulate, fp16 out.  At is A stored
  * K-major ([K][M], M contiguous) so that the rows picked by offset_k are
  * contiguous reads (the tile-wise slides transpose A to avoid uncoalesced

@@ -34,6 +34,16 @@ from ._lib import (  # noqa: F401
     w24_gemm_f16,
     w24_gemm_i8,
     w24_gemm_i8_out,
+    dense_gemm_f16_splitk,
+    w24_gemm_f16_splitk,
+    dense_gemm_i8_splitk,
+    w24_gemm_i8_splitk,
+    splitk_suggest,
+    splitk_workspace_bytes,
+    SSG_KIND_DENSE_F16,
+    SSG_KIND_W24_F16,
+    SSG_KIND_DENSE_I8,
+    SSG_KIND_W24_I8,
     SSG_OUT_I32,
     SSG_OUT_F32,
     SSG_OUT_F16,

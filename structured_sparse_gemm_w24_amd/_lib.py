@@ -40,7 +40,7 @@ _P = ct.c_void_p
 _I64 = ct.c_int64
 _I32 = ct.c_int32
 
-# name -> argument types (every function returns int)
+# name -> argument types (every function returns int, but ssg_splitk_workspace_bytes: int64)
 SIGNATURES = {
     "w24_pack_f16": [_P, _I64, _I64, _P, _P],
     "w24_pack_i8": [_P, _I64, _I64, _P, _P],
@@ -63,6 +63,11 @@ SIGNATURES = {
     "tw_gemm_f16_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I64, _I64, _I64, _P],
     "ssg_transpose_f16": [_P, _P, _I64, _I64, _P],
     "ssg_device_arch": [ct.c_char_p, _I64],
+    "dense_gemm_f16_splitk": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _I64, _P],
+    "w24_gemm_f16_splitk": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _I64, _P],
+    "dense_gemm_i8_splitk": [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _I64, _P],
+    "w24_gemm_i8_splitk": [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _I64, _P],
+    "ssg_splitk_suggest": [_I32, _I64, _I64, _I64],
 }
 
 
@@ -88,6 +93,8 @@ def load():
             lib.ssg_last_error.restype = ct.c_char_p
             lib.ssg_version.argtypes = []
             lib.ssg_version.restype = ct.c_char_p
+            lib.ssg_splitk_workspace_bytes.argtypes = [_I64, _I64, _I32]
+            lib.ssg_splitk_workspace_bytes.restype = ct.c_int64
             _LIB = lib
     return _LIB
 
@@ -300,20 +307,57 @@ def ssg_device_arch():
     return buf.value.decode()
 
 
-def dense_gemm_f16(A, Wt, out=None):
-    """C = A . Wt^T; A [M, K] fp16, Wt [N, K] fp16 -> C [M, N] fp16."""
+# GEMM kinds of the split-K calls (SSG_KIND_* in ssg.h).
+SSG_KIND_DENSE_F16, SSG_KIND_W24_F16, SSG_KIND_DENSE_I8, SSG_KIND_W24_I8 = 0, 1, 2, 3
+
+
+def splitk_suggest(kind, M, N, K):
+    """The library's K-split count for a GEMM kind and shape (1 = unsplit)."""
+    return int(load().ssg_splitk_suggest(kind, M, N, K))
+
+
+def splitk_workspace_bytes(M, N, splits):
+    return int(load().ssg_splitk_workspace_bytes(M, N, splits))
+
+
+def _splits(kind, M, N, K, splits):
+    """splits=None: the library's suggestion; otherwise the caller's count (1 = the
+    unsplit entry point)."""
+    return splitk_suggest(kind, M, N, K) if splits is None else int(splits)
+
+
+def _workspace(M, N, p, like, ws=None):
+    """Device workspace of a split call: the caller's (a uint8 tensor of at least
+    splitk_workspace_bytes(M, N, p) bytes), else one from torch's caching allocator
+    (stream-ordered reuse, so it may be released as soon as the launches are queued)."""
+    torch = _torch()
+    if ws is not None:
+        _dev(ws, torch.uint8, None, "workspace")
+        return ws
+    return torch.empty(max(16, splitk_workspace_bytes(M, N, p)), dtype=torch.uint8, device=like.device)
+
+
+def dense_gemm_f16(A, Wt, out=None, splits=None, workspace=None):
+    """C = A . Wt^T; A [M, K] fp16, Wt [N, K] fp16 -> C [M, N] fp16.  splits: K splits
+    (None: the library's choice for the shape; see dense_gemm_f16_splitk in ssg.h)."""
     torch = _torch()
     M, K = A.shape
     N = Wt.shape[0]
     _dev(A, torch.float16, (M, K), "A")
     _dev(Wt, torch.float16, (N, K), "Wt")
     C = _out(out, (M, N), torch.float16, A)
+    p = _splits(SSG_KIND_DENSE_F16, M, N, K, splits)
     with _on(A, Wt, C):
-        _check(load().dense_gemm_f16(_ptr(A), _ptr(Wt), _ptr(C), M, N, K, _stream(A)))
+        if p == 1:
+            _check(load().dense_gemm_f16(_ptr(A), _ptr(Wt), _ptr(C), M, N, K, _stream(A)))
+        else:
+            ws = _workspace(M, N, p, A, workspace)
+            _check(load().dense_gemm_f16_splitk(_ptr(A), _ptr(Wt), _ptr(C), M, N, K, p, _ptr(ws), ws.numel(),
+                                                _stream(A)))
     return C
 
 
-def dense_gemm_i8(A, Wt, scale=None, out=None):
+def dense_gemm_i8(A, Wt, scale=None, out=None, splits=None, workspace=None):
     """int8 dense GEMM; scale None -> int32 C, else fp32 C = float(acc) * scale[n]."""
     torch = _torch()
     M, K = A.shape
@@ -323,8 +367,15 @@ def dense_gemm_i8(A, Wt, scale=None, out=None):
     if scale is not None:
         _dev(scale, torch.float32, (N,), "scale")
     C = _out(out, (M, N), torch.int32 if scale is None else torch.float32, A)
+    p = _splits(SSG_KIND_DENSE_I8, M, N, K, splits)
     with _on(A, Wt, scale, C):
-        _check(load().dense_gemm_i8(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(C), M, N, K, _stream(A)))
+        if p == 1:
+            _check(load().dense_gemm_i8(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(C), M, N, K, _stream(A)))
+        else:
+            ws = _workspace(M, N, p, A, workspace)
+            code = SSG_OUT_I32 if scale is None else SSG_OUT_F32
+            _check(load().dense_gemm_i8_splitk(_ptr(A), _ptr(Wt), _ptr(scale), None, _ptr(C), code, M, N, K, p,
+                                               _ptr(ws), ws.numel(), _stream(A)))
     return C
 
 
@@ -349,7 +400,7 @@ def _epilogue_args(N, scale, bias):
         _dev(bias, torch.float32, (N,), "bias")
 
 
-def dense_gemm_i8_out(A, Wt, scale, bias=None, out_type="f16", out=None):
+def dense_gemm_i8_out(A, Wt, scale, bias=None, out_type="f16", out=None, splits=None, workspace=None):
     """int8 dense GEMM with the selectable epilogue: y = float(acc) * scale[n] (+ bias[n]),
     stored as out_type ("f32", "f16", "i8"; "i32" = raw accumulators, no scale or bias)."""
     torch = _torch()
@@ -360,13 +411,19 @@ def dense_gemm_i8_out(A, Wt, scale, bias=None, out_type="f16", out=None):
     code, dt = _out_kind(out_type)
     _epilogue_args(N, scale, bias)
     C = _out(out, (M, N), dt, A)
+    p = _splits(SSG_KIND_DENSE_I8, M, N, K, splits)
     with _on(A, Wt, scale, bias, C):
-        _check(load().dense_gemm_i8_out(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(bias), _ptr(C), code, M, N, K,
-                                        _stream(A)))
+        if p == 1:
+            _check(load().dense_gemm_i8_out(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(bias), _ptr(C), code, M, N, K,
+                                            _stream(A)))
+        else:
+            ws = _workspace(M, N, p, A, workspace)
+            _check(load().dense_gemm_i8_splitk(_ptr(A), _ptr(Wt), _ptr(scale), _ptr(bias), _ptr(C), code, M, N, K,
+                                               p, _ptr(ws), ws.numel(), _stream(A)))
     return C
 
 
-def w24_gemm_i8_out(A, vals, meta, scale, bias=None, out_type="f16", out=None):
+def w24_gemm_i8_out(A, vals, meta, scale, bias=None, out_type="f16", out=None, splits=None, workspace=None):
     """2:4 int8 GEMM with the selectable epilogue (see dense_gemm_i8_out)."""
     torch = _torch()
     M, K = A.shape
@@ -377,14 +434,21 @@ def w24_gemm_i8_out(A, vals, meta, scale, bias=None, out_type="f16", out=None):
     code, dt = _out_kind(out_type)
     _epilogue_args(N, scale, bias)
     C = _out(out, (M, N), dt, A)
+    p = _splits(SSG_KIND_W24_I8, M, N, K, splits)
     with _on(A, vals, meta, scale, bias, C):
-        _check(load().w24_gemm_i8_out(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), _ptr(bias), _ptr(C), code,
-                                      M, N, K, _stream(A)))
+        if p == 1:
+            _check(load().w24_gemm_i8_out(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), _ptr(bias), _ptr(C), code,
+                                          M, N, K, _stream(A)))
+        else:
+            ws = _workspace(M, N, p, A, workspace)
+            _check(load().w24_gemm_i8_splitk(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), _ptr(bias), _ptr(C),
+                                             code, M, N, K, p, _ptr(ws), ws.numel(), _stream(A)))
     return C
 
 
-def w24_gemm_f16(A, vals, meta, out=None):
-    """2:4 GEMM; A [M, K] fp16, vals [N, K/2] fp16, meta [N, K/32] int32 (uint32 bits)."""
+def w24_gemm_f16(A, vals, meta, out=None, splits=None, workspace=None):
+    """2:4 GEMM; A [M, K] fp16, vals [N, K/2] fp16, meta [N, K/32] int32 (uint32 bits).
+    splits: K splits (None: the library's choice for the shape)."""
     torch = _torch()
     M, K = A.shape
     N = vals.shape[0]
@@ -392,12 +456,19 @@ def w24_gemm_f16(A, vals, meta, out=None):
     _dev(vals, torch.float16, (N, K // 2), "vals")
     _dev(meta, torch.int32, (N, -(-K // 32)), "meta")
     C = _out(out, (M, N), torch.float16, A)
+    p = _splits(SSG_KIND_W24_F16, M, N, K, splits)
     with _on(A, vals, meta, C):
-        _check(load().w24_gemm_f16(_ptr(A), _ptr(vals), _ptr(meta), _ptr(C), M, N, K, _stream(A)))
+        if p == 1:
+            _check(load().w24_gemm_f16(_ptr(A), _ptr(vals), _ptr(meta), _ptr(C), M, N, K, _stream(A)))
+        else:
+            ws = _workspace(M, N, p, A, workspace)
+            _check(load().w24_gemm_f16_splitk(_ptr(A), _ptr(vals), _ptr(meta), _ptr(C), M, N, K, p, _ptr(ws),
+                                              ws.numel(), _stream(A)))
     return C
 
 
-def w24_gemm_i8(A, vals, meta, scale=None, out=None):
+def w24_gemm_i8(A, vals, meta, scale=None, out=None, splits=None, workspace=None):
+    """2:4 int8 GEMM; scale None -> int32 C, else fp32 C = float(acc) * scale[n]."""
     torch = _torch()
     M, K = A.shape
     N = vals.shape[0]
@@ -407,9 +478,38 @@ def w24_gemm_i8(A, vals, meta, scale=None, out=None):
     if scale is not None:
         _dev(scale, torch.float32, (N,), "scale")
     C = _out(out, (M, N), torch.int32 if scale is None else torch.float32, A)
+    p = _splits(SSG_KIND_W24_I8, M, N, K, splits)
     with _on(A, vals, meta, scale, C):
-        _check(load().w24_gemm_i8(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), _ptr(C), M, N, K, _stream(A)))
+        if p == 1:
+            _check(load().w24_gemm_i8(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), _ptr(C), M, N, K, _stream(A)))
+        else:
+            ws = _workspace(M, N, p, A, workspace)
+            code = SSG_OUT_I32 if scale is None else SSG_OUT_F32
+            _check(load().w24_gemm_i8_splitk(_ptr(A), _ptr(vals), _ptr(meta), _ptr(scale), None, _ptr(C), code,
+                                             M, N, K, p, _ptr(ws), ws.numel(), _stream(A)))
     return C
+
+
+def dense_gemm_f16_splitk(A, Wt, splits, workspace=None, out=None):
+    """dense_gemm_f16 with K split `splits` ways (1 = unsplit); workspace: optional uint8
+    device tensor of at least splitk_workspace_bytes(M, N, splits) bytes."""
+    return dense_gemm_f16(A, Wt, out=out, splits=splits, workspace=workspace)
+
+
+def w24_gemm_f16_splitk(A, vals, meta, splits, workspace=None, out=None):
+    """w24_gemm_f16 with K split `splits` ways (see dense_gemm_f16_splitk)."""
+    return w24_gemm_f16(A, vals, meta, out=out, splits=splits, workspace=workspace)
+
+
+def dense_gemm_i8_splitk(A, Wt, scale, bias=None, out_type="f16", splits=1, workspace=None, out=None):
+    """dense_gemm_i8_out with K split `splits` ways (int8 results equal the unsplit call's)."""
+    return dense_gemm_i8_out(A, Wt, scale, bias, out_type=out_type, out=out, splits=splits, workspace=workspace)
+
+
+def w24_gemm_i8_splitk(A, vals, meta, scale, bias=None, out_type="f16", splits=1, workspace=None, out=None):
+    """w24_gemm_i8_out with K split `splits` ways (int8 results equal the unsplit call's)."""
+    return w24_gemm_i8_out(A, vals, meta, scale, bias, out_type=out_type, out=out, splits=splits,
+                           workspace=workspace)
 
 
 def tw_gemm_f16(At, packed: TwPacked, out=None):

@@ -32,8 +32,8 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibili
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra"]
 
 HOST_SOURCES = ["status.cpp", "pack.cpp"]
-HIP_SOURCES = ["api.hip", "kernels/gemm.hip", "kernels/tw_gemm.hip", "kernels/tw_gemm_i8.hip",
-               "kernels/transpose.hip"]
+HIP_SOURCES = ["api.hip", "kernels/gemm.hip", "kernels/splitk.hip", "kernels/tw_gemm.hip",
+               "kernels/tw_gemm_i8.hip", "kernels/transpose.hip"]
 
 
 def _obj(src):

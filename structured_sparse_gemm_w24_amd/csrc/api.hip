@@ -158,6 +158,86 @@ SSG_API int w24_gemm_i8_out(const int8_t *A, const int8_t *vals, const uint32_t 
 
 namespace {
 
+// Split K: check the split arguments, run the partial launch and the reduce
+// launch on the caller's stream (kinds as in kernels/launch.h).
+int split_run(const char *fn, int kind, const void *A, const void *W, const uint32_t *meta, const float *scale,
+              const float *bias, void *C, int out, int64_t M, int64_t N, int64_t K, int32_t splits, void *ws,
+              int64_t ws_bytes, void *stream) {
+    const bool i8 = kind == 2 || kind == 3;
+    int rc = check_gemm(fn, A, W, C, M, N, K, i8 ? 128 : 64, 64);
+    if (rc) return rc;
+    if (kind == 1 || kind == 3)
+        if (M > 0 && (!meta || !ssg::aligned16(meta))) return ssg::fail(SSG_EINVAL, "%s: meta null or misaligned", fn);
+    if (i8 && (rc = check_i8_epilogue(fn, scale, bias, out))) return rc;
+    const int stages = ssg::gemm_k_stages(kind, int(K));
+    if (splits < 1 || splits > 64 || stages % splits)
+        return ssg::fail(SSG_EINVAL, "%s: splits=%d must be in 1..64 and divide the %d K stages", fn, int(splits),
+                         stages);
+    if (M == 0) return (ssg::clear_error(), SSG_OK);
+    if (splits > 1) {
+        if (!ws || !ssg::aligned16(ws)) return ssg::fail(SSG_EINVAL, "%s: workspace null or not 16-byte aligned", fn);
+        const int64_t need = int64_t(splits) * M * N * 4;
+        if (ws_bytes < need)
+            return ssg::fail(SSG_EINVAL, "%s: workspace of %lld bytes, %lld needed", fn, (long long)ws_bytes,
+                             (long long)need);
+    }
+    if ((rc = check_device())) return rc;
+    const hipStream_t st = hipStream_t(stream);
+    if (splits == 1) {
+        switch (kind) {
+            case 0: return launched(ssg::launch_dense_f16(A, W, C, int(M), int(N), int(K), st), fn);
+            case 1: return launched(ssg::launch_w24_f16(A, W, meta, C, int(M), int(N), int(K), st), fn);
+            case 2:
+                return launched(ssg::launch_dense_i8(A, W, scale, bias, C, out, int(M), int(N), int(K), st), fn);
+            default:
+                return launched(ssg::launch_w24_i8(A, W, meta, scale, bias, C, out, int(M), int(N), int(K), st), fn);
+        }
+    }
+    rc = launched(ssg::launch_gemm_partials(kind, A, W, meta, ws, int(M), int(N), int(K), int(splits), st), fn);
+    if (rc) return rc;
+    return launched(ssg::launch_splitk_reduce(ws, int(splits), i8, scale, bias, C, out, int(M), int(N), st), fn);
+}
+
+}  // namespace
+
+SSG_API int64_t ssg_splitk_workspace_bytes(int64_t M, int64_t N, int32_t splits) {
+    if (splits <= 1 || M <= 0 || N <= 0) return 0;
+    return int64_t(splits) * M * N * 4;
+}
+
+SSG_API int32_t ssg_splitk_suggest(int32_t kind, int64_t M, int64_t N, int64_t K) {
+    if (kind < 0 || kind > 3 || !fits_int(M) || !fits_int(N) || !fits_int(K)) return 1;
+    return ssg::suggest_splits(int(kind), int(M), int(N), int(K));
+}
+
+SSG_API int dense_gemm_f16_splitk(const void *A, const void *Wt, void *C, int64_t M, int64_t N, int64_t K,
+                                  int32_t splits, void *ws, int64_t ws_bytes, void *stream) {
+    return split_run("dense_gemm_f16_splitk", 0, A, Wt, nullptr, nullptr, nullptr, C, 0, M, N, K, splits, ws,
+                     ws_bytes, stream);
+}
+
+SSG_API int w24_gemm_f16_splitk(const void *A, const void *vals, const uint32_t *meta, void *C, int64_t M, int64_t N,
+                                int64_t K, int32_t splits, void *ws, int64_t ws_bytes, void *stream) {
+    return split_run("w24_gemm_f16_splitk", 1, A, vals, meta, nullptr, nullptr, C, 0, M, N, K, splits, ws, ws_bytes,
+                     stream);
+}
+
+SSG_API int dense_gemm_i8_splitk(const int8_t *A, const int8_t *Wt, const float *scale, const float *bias, void *C,
+                                 int32_t out_type, int64_t M, int64_t N, int64_t K, int32_t splits, void *ws,
+                                 int64_t ws_bytes, void *stream) {
+    return split_run("dense_gemm_i8_splitk", 2, A, Wt, nullptr, scale, bias, C, out_type, M, N, K, splits, ws,
+                     ws_bytes, stream);
+}
+
+SSG_API int w24_gemm_i8_splitk(const int8_t *A, const int8_t *vals, const uint32_t *meta, const float *scale,
+                               const float *bias, void *C, int32_t out_type, int64_t M, int64_t N, int64_t K,
+                               int32_t splits, void *ws, int64_t ws_bytes, void *stream) {
+    return split_run("w24_gemm_i8_splitk", 3, A, vals, meta, scale, bias, C, out_type, M, N, K, splits, ws, ws_bytes,
+                     stream);
+}
+
+namespace {
+
 int tw_run(const char *fn, const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
            const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr, const int32_t *tile_order, int32_t T,
            int32_t G, int32_t t_first, int32_t t_count, int32_t flags, void *C, int64_t M, int64_t N, int64_t K,

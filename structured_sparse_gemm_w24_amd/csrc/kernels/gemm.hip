@@ -67,8 +67,10 @@ namespace ssg {
 enum Kind { DENSE_F16 = 0, W24_F16 = 1, DENSE_I8 = 2, W24_I8 = 3 };
 // EPI_F16: fp16 kinds.  int8 kinds: EPI_I32 raw accumulators; the others
 // compute y = float(acc) * scale[n] (+ bias[n]), each step rounded to nearest
-// even, then store y as fp32, fp16 or saturated int8.
-enum Epi { EPI_F16 = 0, EPI_I32 = 1, EPI_F32_SCALE = 2, EPI_F16_SCALE = 3, EPI_I8_SCALE = 4 };
+// even, then store y as fp32, fp16 or saturated int8.  EPI_PART (split K, any
+// kind): the raw accumulators (fp32 or int32) of K-split blockIdx.y go to its
+// [M][N] slice of the workspace passed as C; a second kernel sums the slices.
+enum Epi { EPI_F16 = 0, EPI_I32 = 1, EPI_F32_SCALE = 2, EPI_F16_SCALE = 3, EPI_I8_SCALE = 4, EPI_PART = 5 };
 
 template <int KIND>
 struct KindTraits;
@@ -215,7 +217,7 @@ template <int KIND, int EPI, class CF>
 __global__ void __launch_bounds__(CF::WM *CF::WN * 64)
 gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const uint32_t *__restrict__ meta,
             const float *__restrict__ scale, const float *__restrict__ bias, void *__restrict__ C, int M, int N,
-            int K) {
+            int K, int stages) {
     using KT = KindTraits<KIND>;
     using LY = Layout<KIND, CF>;
     using Acc = typename AccOf<KIND>::T;
@@ -254,7 +256,14 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     const int64_t a_row = int64_t(K) * SA;                  // bytes per A row
     const int64_t w_row = KT::kSparse ? a_row / 2 : a_row;  // bytes per W row
     const int64_t m_row = K / 32;                            // meta words per row
-    const int S = int(a_row / 128);
+    // S = K stages of this workgroup (128 bytes of an A row each): all of them,
+    // or, with K split over gridDim.y, split blockIdx.y's equal share.  The
+    // mask is a value-range hint (the host's 4 GiB operand limit keeps S below
+    // 2^19): with S known to be small the compiler keeps the stage address
+    // arithmetic narrow, which holds the 128 x 256 tiles within the 256
+    // registers that two workgroups per CU allow (260 without it).
+    const int S = stages & 0xffffff;
+    const int ks0 = int(blockIdx.y) * S;
 
     // ---- direct-to-LDS sources: instruction j of this wave fills the wave's
     // j-th KiB of the A (or W) stage; lane -> (row, position) -> global chunk.
@@ -298,7 +307,7 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     const __amdgpu_buffer_rsrc_t bufM = buffer_of(meta_b, KT::kSparse ? uint32_t(int64_t(N) * m_row * 4) : 0u);
     auto issue = [&](int s) {
         uint8_t *base = smem + (s % NB) * STAGE;
-        const int sg = (s + rot < S) ? s + rot : s + rot - S;  // global K stage
+        const int sg = ks0 + ((s + rot < S) ? s + rot : s + rot - S);  // global K stage
 #pragma unroll
         for (int j = 0; j < LY::LA; ++j) dma16(bufA, oa[j] + uint32_t(sg * 128), base + (j * LY::NW + wave) * 1024);
 #pragma unroll
@@ -416,6 +425,12 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
         if constexpr (EPI == EPI_F16) {
             o.x = pack_half2_rne(v[4 * q + 0], v[4 * q + 1]);
             o.y = pack_half2_rne(v[4 * q + 2], v[4 * q + 3]);
+        } else if constexpr (EPI == EPI_PART) {
+            // (whole 4-vectors are bit-cast: a bit-cast of a single element of
+            // the 16-wide accumulator vector yielded element 0 for every lane)
+            using E4 = typename std::conditional<KT::kI8, intx4, floatx4>::type;
+            const E4 t = E4{v[4 * q + 0], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+            o = __builtin_bit_cast(u32x4, t);
         } else if constexpr (EPI == EPI_I32) {
             o.x = uint32_t(v[4 * q + 0]);
             o.y = uint32_t(v[4 * q + 1]);
@@ -460,6 +475,7 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     constexpr int RPI = kWave / CPR;        // token rows per store instruction
     static_assert(RPI * CPR == kWave, "row segment must tile a wave");
     __syncthreads();  // every wave is done reading the stage buffers
+    uint8_t *const Cb = reinterpret_cast<uint8_t *>(C) + (EPI == EPI_PART ? int64_t(blockIdx.y) * M * N * OB : 0);
     uint8_t *ew = smem + wave * EPASS * EWAVE;
     const int nw = n0 + wn * TN * 32;  // first channel of the wave
 #pragma unroll
@@ -487,7 +503,7 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
                 const int m = m0 + wm * TM * 32 + (tp + e) * 32 + row;
                 const int n = nw + ch * (16 / OB);
                 const u32x4 v = *reinterpret_cast<const u32x4 *>(ew + e * EWAVE + row * EROW + ch * 16);
-                if (m < M && n < N) store16<CF::NTS>(reinterpret_cast<uint8_t *>(C) + (int64_t(m) * N + n) * OB, v);
+                if (m < M && n < N) store16<CF::NTS>(Cb + (int64_t(m) * N + n) * OB, v);
             }
         }
         if (tp + EPASS < TM) __syncthreads();
@@ -496,12 +512,13 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
 
 template <int KIND, int EPI, class CF>
 static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, const float *scale,
-                         const float *bias, void *C, int M, int N, int K, hipStream_t st) {
+                         const float *bias, void *C, int M, int N, int K, hipStream_t st, int splits = 1) {
     using LY = Layout<KIND, CF>;
     const int nb = ((M + LY::BM - 1) / LY::BM) * ((N + LY::BN - 1) / LY::BN);
-    hipLaunchKernelGGL((gemm_kernel<KIND, EPI, CF>), dim3(nb), dim3(LY::NT), 0, st,
+    const int stages = K * (KindTraits<KIND>::kI8 ? 1 : 2) / 128 / splits;
+    hipLaunchKernelGGL((gemm_kernel<KIND, EPI, CF>), dim3(nb, splits), dim3(LY::NT), 0, st,
                        static_cast<const uint8_t *>(A), static_cast<const uint8_t *>(Wv), meta, scale, bias, C, M, N,
-                       K);
+                       K, stages);
     return hipGetLastError();
 }
 
@@ -564,17 +581,17 @@ static Shape pick_i8(int M, int N, int K, bool dense) {
 
 template <int KIND, int EPI, bool NTS, bool DENSE>
 static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const uint32_t *meta, const float *scale,
-                               const float *bias, void *C, int M, int N, int K, hipStream_t st) {
+                               const float *bias, void *C, int M, int N, int K, hipStream_t st, int splits = 1) {
     if (sh == SHAPE_BIG) {
-        if constexpr (DENSE) return launch<KIND, EPI, CfgBigDense<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
-        else return launch<KIND, EPI, CfgBig<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
+        if constexpr (DENSE) return launch<KIND, EPI, CfgBigDense<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
+        else return launch<KIND, EPI, CfgBig<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     }
-    if (sh == SHAPE_MID) return launch<KIND, EPI, CfgMid<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st);
+    if (sh == SHAPE_MID) return launch<KIND, EPI, CfgMid<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     if constexpr (KindTraits<KIND>::kI8)  // (only the int8 kinds pick Small2)
         if (sh == SHAPE_SMALL2)
             return launch<KIND, EPI, CfgSmall2<NTS, KindTraits<KIND>::kSparse>>(A, Wv, meta, scale, bias, C, M, N, K,
-                                                                                st);
-    return launch<KIND, EPI, CfgSmall<NTS, KindTraits<KIND>::kSparse>>(A, Wv, meta, scale, bias, C, M, N, K, st);
+                                                                                st, splits);
+    return launch<KIND, EPI, CfgSmall<NTS, KindTraits<KIND>::kSparse>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
 }
 
 hipError_t launch_dense_f16(const void *A, const void *Wt, void *C, int M, int N, int K, hipStream_t st) {
@@ -617,6 +634,56 @@ hipError_t launch_dense_i8(const void *A, const void *Wt, const float *scale, co
 hipError_t launch_w24_i8(const void *A, const void *vals, const uint32_t *meta, const float *scale, const float *bias,
                          void *C, int out, int M, int N, int K, hipStream_t st) {
     return launch_i8<W24_I8, false>(A, vals, meta, scale, bias, C, out, M, N, K, st);
+}
+
+}  // namespace ssg
+
+namespace ssg {
+
+// ---- split K.  The partial launches run the tile choice of the unsplit
+// kinds with gridDim.y = splits and the EPI_PART epilogue (plain stores: the
+// reduce launch reads the partials back right away).
+hipError_t launch_gemm_partials(int kind, const void *A, const void *W, const uint32_t *meta, void *ws, int M,
+                                int N, int K, int splits, hipStream_t st) {
+    switch (kind) {
+        case DENSE_F16:
+            return launch_shape<DENSE_F16, EPI_PART, false, true>(pick_f16(M, N), A, W, nullptr, nullptr, nullptr, ws,
+                                                                   M, N, K, st, splits);
+        case W24_F16:
+            return launch_shape<W24_F16, EPI_PART, false, false>(pick_f16(M, N), A, W, meta, nullptr, nullptr, ws, M,
+                                                                  N, K, st, splits);
+        case DENSE_I8:
+            return launch_shape<DENSE_I8, EPI_PART, false, true>(pick_i8(M, N, K, true), A, W, nullptr, nullptr,
+                                                                  nullptr, ws, M, N, K, st, splits);
+        default:
+            return launch_shape<W24_I8, EPI_PART, false, false>(pick_i8(M, N, K, false), A, W, meta, nullptr, nullptr,
+                                                                 ws, M, N, K, st, splits);
+    }
+}
+
+// Splitting K pays when the output tiles leave most workgroup slots of the
+// chip idle (one GPU's share of a token-sharded layer: M = 512): the K loop of
+// each tile is a chain of dependent stage loads, so more independent chains
+// run in the same time.  Resident workgroups per CU follow the tiles' LDS
+// (160 KiB per CU): Big 1; Mid 2; Small 2 (dense fp16 / int8: 1, three
+// 32 KiB stages); Small2 3 (dense int8: 2).  Splits double while the split
+// tiles still fit the slots once and every split keeps at least 8 stages.
+int suggest_splits(int kind, int M, int N, int K) {
+    constexpr int kCUs = 256;
+    if (M <= 0 || N <= 0 || K <= 0) return 1;
+    const bool i8 = kind == DENSE_I8 || kind == W24_I8;
+    const bool dense = kind == DENSE_F16 || kind == DENSE_I8;
+    const Shape sh = i8 ? pick_i8(M, N, K, dense) : pick_f16(M, N);
+    int bm = 128, bn = 128, occ = dense ? 1 : 2;
+    if (sh == SHAPE_BIG) bm = 256, bn = 256, occ = 1;
+    else if (sh == SHAPE_MID) bn = 256, occ = 2;
+    else if (sh == SHAPE_SMALL2) occ = dense ? 2 : 3;
+    const long t = tiles(M, N, bm, bn), slots = long(kCUs) * occ;
+    const int S = gemm_k_stages(kind, K);
+    if (2 * t > slots) return 1;
+    int p = 1;
+    while (p < 16 && t * 2 * p <= slots && S % (2 * p) == 0 && S / (2 * p) >= 8) p *= 2;
+    return p;
 }
 
 }  // namespace ssg

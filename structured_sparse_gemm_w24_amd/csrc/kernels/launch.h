@@ -33,4 +33,18 @@ hipError_t launch_tw_i8(const void *At, const void *vals, const int32_t *offset_
                         void *C, int out, int M, int N, hipStream_t st);
 hipError_t launch_transpose_f16(const void *A, void *At, int M, int K, hipStream_t st);
 
+// Split K: kind is a GEMM kind (0 dense fp16, 1 2:4 fp16, 2 dense int8, 3 2:4
+// int8).  The split launch writes split s's raw accumulators (fp32 / int32)
+// to slice s of ws ([splits][M][N], 4 bytes each); the reduce launch sums the
+// slices in split order and applies the kind's epilogue (out: OUT_* for int8).
+hipError_t launch_gemm_partials(int kind, const void *A, const void *W, const uint32_t *meta, void *ws, int M,
+                                int N, int K, int splits, hipStream_t st);
+hipError_t launch_splitk_reduce(const void *ws, int splits, bool i8, const float *scale, const float *bias,
+                                void *C, int out, int M, int N, hipStream_t st);
+// K splits worth taking for a kind and shape (1 = do not split); a host-only
+// rule from the tile choice, the resident workgroups per CU and the K stages.
+int suggest_splits(int kind, int M, int N, int K);
+// K stages (one per 128 bytes of an A row) for a kind and K.
+inline int gemm_k_stages(int kind, int K) { return (kind == 2 || kind == 3) ? K / 128 : K / 64; }
+
 }  // namespace ssg

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "ssg.h")
 def declared_functions():
     names = []
     for line in open(HEADER):
-        m = re.match(r"^\s*(?:int|const char \*)\s*(\w+)\s*\(", line)
+        m = re.match(r"^\s*(?:int|int32_t|int64_t|const char \*)\s*(\w+)\s*\(", line)
         if m:
             names.append(m.group(1))
     return names
@@ -83,6 +83,19 @@ def has_device(lib):
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 3, 16, _p(16), 8, 32, 64, None), "T=3"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 16, _p(16), 12, 32, 64, None), "multiple of 8"),
     (lambda r: r.ssg_transpose_f16(_p(16), _p(16), 12, 16, None), "multiples of 8"),
+    (lambda r: r.w24_gemm_f16_splitk(*[_p(16)] * 4, 8, 64, 128, 3, _p(16), 1 << 20, None), "splits=3"),
+    (lambda r: r.w24_gemm_f16_splitk(*[_p(16)] * 4, 8, 64, 128, 0, _p(16), 1 << 20, None), "splits=0"),
+    (lambda r: r.dense_gemm_f16_splitk(*[_p(16)] * 3, 8, 64, 128, 128, _p(16), 1 << 20, None), "splits=128"),
+    (lambda r: r.w24_gemm_f16_splitk(*[_p(16)] * 4, 8, 64, 128, 2, None, 1 << 20, None), "workspace null"),
+    (lambda r: r.w24_gemm_f16_splitk(*[_p(16)] * 4, 8, 64, 128, 2, _p(20), 1 << 20, None), "16-byte aligned"),
+    (lambda r: r.w24_gemm_f16_splitk(*[_p(16)] * 4, 8, 64, 128, 2, _p(16), 4095, None), "4096 needed"),
+    (lambda r: r.w24_gemm_i8_splitk(*[_p(16)] * 5, _p(16), 9, 8, 64, 256, 2, _p(16), 1 << 20, None),
+     "unknown out_type"),
+    (lambda r: r.dense_gemm_i8_splitk(*[_p(16)] * 2, None, None, _p(16), 1, 8, 64, 256, 2, _p(16), 1 << 20, None),
+     "needs scale"),
+    (lambda r: r.w24_gemm_i8_splitk(*[_p(16)] * 5, _p(16), 1, 8, 64, 256, 4, _p(16), 1 << 20, None), "splits=4"),
+    (lambda r: r.w24_gemm_i8_splitk(_p(16), _p(16), None, _p(16), None, _p(16), 1, 8, 64, 256, 2, _p(16), 1 << 20,
+                                    None), "meta"),
 ])
 def test_invalid_arguments_rejected_on_host(lib, call, msg):
     raw = _raw(lib)
@@ -152,3 +165,29 @@ def test_concurrent_packs_and_thread_local_errors(lib):
             assert rc == 2 and "nonzeros" in msg
         else:
             assert msg == ""  # the last call on this thread (a successful pack) cleared it
+
+
+def test_splitk_host_helpers(lib):
+    raw = _raw(lib)
+    assert raw.ssg_splitk_workspace_bytes(512, 1024, 8) == 8 * 512 * 1024 * 4
+    assert raw.ssg_splitk_workspace_bytes(512, 1024, 1) == 0
+    assert raw.ssg_splitk_workspace_bytes(-1, 1024, 8) == 0
+    # one GPU's share of ViT-L fc2 (M = 512): 32 tiles on 256 CUs -> split
+    assert lib.splitk_suggest(lib.SSG_KIND_W24_F16, 512, 1024, 4096) > 1
+    assert lib.splitk_suggest(lib.SSG_KIND_W24_I8, 512, 1024, 4096) > 1
+    # the ViT-Base fc1 shape fills the chip several times over -> no split
+    for kind in range(4):
+        assert lib.splitk_suggest(kind, 12608, 3072, 768) == 1
+    # every suggestion divides the K stages and leaves >= 8 per split
+    for kind in range(4):
+        for M, N, K in ((512, 1024, 4096), (512, 3072, 1024), (64, 256, 8192), (1, 64, 2048)):
+            p = lib.splitk_suggest(kind, M, N, K)
+            stages = K // (128 if kind >= 2 else 64)
+            assert p >= 1 and stages % p == 0 and (p == 1 or stages // p >= 8), (kind, M, N, K, p)
+    assert lib.splitk_suggest(7, 512, 1024, 4096) == 1
+    assert lib.splitk_suggest(1, 0, 1024, 4096) == 1
+
+
+def test_splitk_zero_rows_is_ok_without_touching_the_device(lib):
+    raw = _raw(lib)
+    assert raw.w24_gemm_f16_splitk(None, None, None, None, 0, 64, 128, 2, None, 0, None) == 0

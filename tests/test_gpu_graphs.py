@@ -164,3 +164,23 @@ def test_graph_tw_i8(lib, gpu):
     sc = _dev(wl.f32_scales(rng, N))
     _graph_replays(lambda s: {"At": _dev(np.ascontiguousarray(_i8(s, (M, K)).T))},
                    lambda x, out=None: lib.tw_gemm_i8(x["At"], p, sc, out_type="f16", out=out))
+
+
+@pytest.mark.parametrize("kind", ["f16", "i8"])
+def test_graph_splitk(lib, gpu, kind):
+    """Split-K path (partial launch + reduce launch, workspace from torch's allocator
+    inside the capture)."""
+    M, K, N = 256, 4096, 256
+    rng = np.random.default_rng(109)
+    if kind == "f16":
+        W = wl.prune24_magnitude(wl.f16_normal(rng, (K, N), 0.02))
+        vals, meta = lib.w24_pack_f16(W)
+        v, m = _dev(vals), _dev(meta.view(np.int32))
+        _graph_replays(lambda s: {"A": _dev(_f16(s, (M, K)))},
+                       lambda x, out=None: lib.w24_gemm_f16(x["A"], v, m, out=out, splits=8))
+    else:
+        W = wl.prune24_magnitude(wl.i8_weights(rng, (K, N)))
+        vals, meta = lib.w24_pack_i8(W)
+        v, m, sc = _dev(vals), _dev(meta.view(np.int32)), _dev(wl.f32_scales(rng, N))
+        _graph_replays(lambda s: {"A": _dev(_i8(s, (M, K)))},
+                       lambda x, out=None: lib.w24_gemm_i8(x["A"], v, m, sc, out=out, splits=4))

@@ -22,7 +22,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KDIR = os.path.join(ROOT, "structured_sparse_gemm_w24_amd", "csrc", "kernels")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ("gemm.hip", "tw_gemm.hip", "tw_gemm_i8.hip", "transpose.hip")
+SOURCES = ("gemm.hip", "splitk.hip", "tw_gemm.hip", "tw_gemm_i8.hip", "transpose.hip")
 
 LDS_PER_CU = 160 * 1024
 VGPRS_PER_SIMD_LANE = 512
@@ -65,6 +65,7 @@ def test_every_kernel_was_found(kernels):
     assert sum("gemm_kernel" in k for k in kernels) >= 20
     assert any("tw_gemm_kernel" in k for k in kernels)
     assert any("tw_gemm_i8_kernel" in k for k in kernels)
+    assert any("splitk_reduce_kernel" in k for k in kernels)
     assert all("wg" in v for v in kernels.values()), [k for k, v in kernels.items() if "wg" not in v]
 
 
