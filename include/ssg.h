@@ -239,11 +239,12 @@ enum { SSG_KIND_DENSE_F16 = 0, SSG_KIND_W24_F16 = 1, SSG_KIND_DENSE_I8 = 2, SSG_
  * negative sizes). */
 int64_t ssg_splitk_workspace_bytes(int64_t M, int64_t N, int32_t splits);
 
-/* The split count the library would take for a kind and shape: 1 (do not
- * split) unless the output tiles fill at most half of the resident
- * workgroup slots of a 256-CU MI355X; then the largest power of two <= 16
- * whose split tiles still fit the slots once and leave every split at least
- * 8 K stages.  Host-only; an invalid kind or shape gives 1. */
+/* The split count the library would take for a kind and shape (measured on
+ * MI355X): 1 (do not split) when K has fewer than 32 stages or the output
+ * tiles number more than 128 (fp16 kinds) / 64 (int8 kinds); otherwise the
+ * largest power of two <= 16 with tiles x splits <= 256 (one workgroup per
+ * CU) and at least 8 K stages per split.  Host-only; an invalid kind or
+ * shape gives 1. */
 int32_t ssg_splitk_suggest(int32_t kind, int64_t M, int64_t N, int64_t K);
 
 int dense_gemm_f16_splitk(const void *A, const void *Wt, void *C, int64_t M, int64_t N, int64_t K,

@@ -661,28 +661,30 @@ hipError_t launch_gemm_partials(int kind, const void *A, const void *W, const ui
     }
 }
 
-// Splitting K pays when the output tiles leave most workgroup slots of the
-// chip idle (one GPU's share of a token-sharded layer: M = 512): the K loop of
-// each tile is a chain of dependent stage loads, so more independent chains
-// run in the same time.  Resident workgroups per CU follow the tiles' LDS
-// (160 KiB per CU): Big 1; Mid 2; Small 2 (dense fp16 / int8: 1, three
-// 32 KiB stages); Small2 3 (dense int8: 2).  Splits double while the split
-// tiles still fit the slots once and every split keeps at least 8 stages.
+// Splitting K pays when a GEMM has few output tiles and a long K loop (one
+// GPU's share of a token-sharded layer, e.g. 512 x 4096 x 1024): each tile's
+// K loop is a chain of dependent stage loads, and cutting it into ranges run
+// side by side shortens the chain, at the price of a second launch and the
+// partials' round trip through memory (8 * M * N bytes per split).  Measured
+// on MI355X with graph-timed replays (fp16 2:4, 512 x 4096 x 1024: 31.0 us
+// unsplit, 16.0 us with 8 splits; 512 x 8192 x 1024: 56.3 -> 21.6 us; int8
+// 2:4, 512 x 4096 x 1024: 18.7 -> 14.8 us with 4 splits), the split loses
+// whenever K has fewer than 32 stages (K = 1024: 10.7 -> 11.9 us and worse)
+// or the tiles already number more than 128 (fp16) / 64 (int8).  Within
+// those bounds the splits double while tiles x splits stays within one
+// workgroup per CU and every split keeps at least 8 stages.
 int suggest_splits(int kind, int M, int N, int K) {
     constexpr int kCUs = 256;
     if (M <= 0 || N <= 0 || K <= 0) return 1;
     const bool i8 = kind == DENSE_I8 || kind == W24_I8;
     const bool dense = kind == DENSE_F16 || kind == DENSE_I8;
     const Shape sh = i8 ? pick_i8(M, N, K, dense) : pick_f16(M, N);
-    int bm = 128, bn = 128, occ = dense ? 1 : 2;
-    if (sh == SHAPE_BIG) bm = 256, bn = 256, occ = 1;
-    else if (sh == SHAPE_MID) bn = 256, occ = 2;
-    else if (sh == SHAPE_SMALL2) occ = dense ? 2 : 3;
-    const long t = tiles(M, N, bm, bn), slots = long(kCUs) * occ;
+    const int bm = sh == SHAPE_BIG ? 256 : 128, bn = (sh == SHAPE_BIG || sh == SHAPE_MID) ? 256 : 128;
+    const long t = tiles(M, N, bm, bn);
     const int S = gemm_k_stages(kind, K);
-    if (2 * t > slots) return 1;
+    if (S < 32 || t > (i8 ? 64 : 128)) return 1;
     int p = 1;
-    while (p < 16 && t * 2 * p <= slots && S % (2 * p) == 0 && S / (2 * p) >= 8) p *= 2;
+    while (p < 16 && t * 2 * p <= kCUs && S % (2 * p) == 0 && S / (2 * p) >= 8) p *= 2;
     return p;
 }
 
