@@ -424,6 +424,8 @@ def main(argv=None):
                     help="table mode: comma list from " + ",".join(WORKLOADS) +
                          " or vit_large:<qkv|proj|fc1|fc2> for one layer-0 GEMM (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip the shader-clock reading (2 s of extra replays; for profiled runs)")
     ap.add_argument("--no-tw-extras", action="store_true",
                     help="table mode: time only the grouped tile-wise kernel (not the fused, row-major-A "
                          "and multi-stream variants)")
@@ -475,7 +477,7 @@ def main(argv=None):
                                      r["sets"][i % r["rotate_sets"]]["meta"], r["sets"][i % r["rotate_sets"]]["scale"],
                                      out=r["sets"][i % r["rotate_sets"]]["C"])
     t_eager = Timer(torch, graph=False, reps=HEADLINE_REPLAYS)(step, a.steps, a.warmup)
-    sclk = observed_sclk(torch, step, a.steps) if not a.eager else None
+    sclk = observed_sclk(torch, step, a.steps) if not (a.eager or a.no_sclk) else None
     nz, de = perf.w24_ops(M, N, K)
     t = r["t_sparse_ms"] / 1e3
     bytes_ = perf.w24_bytes(M, N, K, 1, 1, 4, scale=True)
@@ -585,8 +587,9 @@ def summarize_profile(a):
         out.append(f"target '{a.kernel}': {d.size} dispatches, mean {d.mean():.1f} us, median {np.median(d):.1f} us")
         w, st = max(0, a.profile_warmup), max(1, a.profile_steps)
         groups = [d[:w]] + [d[i:i + st] for i in range(w, d.size, st)]
-        out.append(f"  per-group median us (warm-up {w}, then groups of {st}): " +
-                   " ".join(f"{np.median(g):.1f}" for g in groups if g.size))
+        shown = [g for g in groups if g.size][:40]
+        out.append(f"  per-group median us (warm-up {w}, then groups of {st}; first {len(shown)} of "
+                   f"{sum(1 for g in groups if g.size)}): " + " ".join(f"{np.median(g):.1f}" for g in shown))
     if a.bench_log and os.path.exists(a.bench_log):
         lines = [ln for ln in open(a.bench_log) if ln.startswith("{")]
         for ln in lines:
