@@ -256,7 +256,9 @@ def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, with_f16
     st = timer.stats(sp, steps, warmup)
     t_de = timer(de, steps, warmup)
     out = dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"], t_dense_ms=t_de,
-               rotate_sets=R, t_pack_host_ms=t_pack, sets=sets)
+               rotate_sets=R, t_pack_host_ms=t_pack, sets=sets,
+               k_splits=ssg.splitk_suggest(ssg.SSG_KIND_W24_I8, M, N, K),
+               k_splits_dense=ssg.splitk_suggest(ssg.SSG_KIND_DENSE_I8, M, N, K))
     if with_f16_dense:
         # the same shape through the fp16 dense kernel (int8 values are exact in fp16)
         for d in sets:
@@ -329,7 +331,8 @@ def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
     st = timer.stats(sp, steps, warmup)
     return dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
                 t_dense_ms=timer(de, steps, warmup), t_torch_ms=timer(tm, steps, warmup), rotate_sets=R,
-                t_pack_host_ms=t_pack)
+                t_pack_host_ms=t_pack, k_splits=ssg.splitk_suggest(ssg.SSG_KIND_W24_F16, M, N, K),
+                k_splits_dense=ssg.splitk_suggest(ssg.SSG_KIND_DENSE_F16, M, N, K))
 
 
 def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, extras=True):
