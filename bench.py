@@ -21,6 +21,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import shutil
 import subprocess
 import sys
@@ -42,12 +43,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text):
+    """C++ source without comments and with whitespace collapsed: edits to
+    comments or layout do not change a kernel, so they keep its hash."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash(main="gemm.hip"):
-    """Hash of a kernel source and the shared header (traffic counters are only
-    reused while this matches)."""
+    """Hash of a kernel source and the shared header, code only (traffic
+    counters are only reused while this matches)."""
     h = hashlib.sha256()
     for f in (main, "common.h"):
-        h.update(open(os.path.join(ROOT, "structured_sparse_gemm_w24_amd", "csrc", "kernels", f), "rb").read())
+        src = open(os.path.join(ROOT, "structured_sparse_gemm_w24_amd", "csrc", "kernels", f)).read()
+        h.update(_code_only(src).encode())
     return h.hexdigest()[:16]
 
 

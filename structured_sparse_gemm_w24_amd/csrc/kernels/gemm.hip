@@ -40,7 +40,12 @@
 //     lane (fp16 kinds: fp16 rounded to nearest even; int8 kinds: raw int32,
 //     or y = float(acc) * scale[n] (+ bias[n]) written as fp32, as fp16
 //     rounded to nearest even, or as int8 rounded to nearest even and
-//     saturated to [-128, 127]).
+//     saturated to [-128, 127]);
+//   * a tile starts its K loop at stage 0 or, for the sparse 128 x 128 tiles,
+//     at a stage rotated by its tile id (measured per tile shape, see ROT);
+//   * split K (gridDim.y > 1, EPI_PART): workgroup (tile, y) runs K-stage range
+//     y and writes its raw accumulators to slice y of a workspace, which
+//     splitk.hip sums and finishes with the kind's epilogue.
 //
 // Instruction operand layouts (64-lane wave, h = lane / 32, r = lane % 32):
 //   dense f16 32x32x16 : row-op lane holds k = 8h .. 8h+7 of its row r

@@ -84,3 +84,11 @@ def test_gfx_clock_parser_reads_every_xcd_and_nothing_else():
         "vclk_0": {"clk": {"value": 29, "unit": "MHz"}}}}]}
     assert bench._gfx_clocks(doc) == [1400.0 + 10 * i for i in range(8)]
     assert bench._gfx_clocks({"gpu_data": []}) == []
+
+
+def test_kernel_hash_ignores_comments_and_layout():
+    import bench
+    a = "int f(int x) {\n  return x + 1;  // add one\n}\n/* note */\n"
+    b = "/* header\n   text */ int f(int x) { return x + 1; }"
+    c = "int f(int x) { return x + 2; }"
+    assert bench._code_only(a) == bench._code_only(b) != bench._code_only(c)
