@@ -244,6 +244,95 @@ def rotation(bytes_per_set):
     return max(2, int(np.ceil(2 * CACHE_BYTES / max(1, bytes_per_set))))
 
 
+# ---------------------------------------------------------------- vendor 2:4 baseline
+_VENDOR = []
+
+
+def vendor_lib():
+    """AMD's hipSPARSELt through libssg_vendor.so (built beside libssg when the
+    hipSPARSELt headers are installed), or None.  Bench only: the product never
+    loads it."""
+    if not _VENDOR:
+        import ctypes as ct
+        path = os.path.join(ROOT, "structured_sparse_gemm_w24_amd", "libssg_vendor.so")
+        v = None
+        if os.path.exists(path):
+            v = ct.CDLL(path)
+            v.vsl_create.restype = ct.c_void_p
+            v.vsl_create.argtypes = [ct.c_int] * 5 + [ct.c_float] + [ct.c_void_p] * 4
+            v.vsl_run.restype = ct.c_int
+            v.vsl_run.argtypes = [ct.c_void_p] * 4
+            v.vsl_destroy.argtypes = [ct.c_void_p]
+            v.vsl_last_error.restype = ct.c_char_p
+        _VENDOR.append(v)
+    return _VENDOR[0]
+
+
+def vendor_w24_time(torch, kind, Wp, sets, M, N, K, C_ours, steps, warmup, timer):
+    """Times hipSPARSELt's 2:4 GEMM on the same operands: kind 0 fp16 in / fp16
+    out, kind 1 int8 in / fp16 out.  The vendor output is alpha * product with
+    a scalar alpha: 1 for fp16, 2^-12 for int8 (the raw accumulators exceed
+    the fp16 range), where the int8 kernel beside it applies a per-channel
+    scale vector.  C_ours is the unscaled product.  Both operand orientations are
+    planned (algorithm search on each) and the faster is reported.  The weight
+    is compressed once; A and C rotate over `sets` like the other kernels'.
+    Every plan's first result is checked against alpha * C_ours (C_ours: this
+    library's unscaled product for sets[0]) before it is timed.  Returns {} when the library is absent."""
+    v = vendor_lib()
+    if v is None:
+        return {}
+    dev = torch.device("cuda")
+    R = len(sets)
+    W_t = torch.from_numpy(np.ascontiguousarray(Wp)).to(dev)
+    best, notes = None, []
+    alpha = 1.0 if kind == 0 else 2.0 ** -12
+    ref = C_ours.float() * alpha
+    for rowmajor in (0, 1):
+        W_o = W_t if rowmajor == 0 else W_t.t().contiguous()
+        stream = torch.cuda.current_stream().cuda_stream
+        plan = v.vsl_create(kind, M, N, K, rowmajor, alpha, W_o.data_ptr(), sets[0]["A"].data_ptr(),
+                            sets[0]["C"].data_ptr(), stream)
+        if not plan:
+            notes.append(f"orientation {rowmajor}: {v.vsl_last_error().decode()}")
+            continue
+        try:
+            Cv = torch.empty(M * N, dtype=torch.float16, device=dev)
+            if v.vsl_run(plan, sets[0]["A"].data_ptr(), Cv.data_ptr(), stream) != 0:
+                notes.append(f"orientation {rowmajor}: {v.vsl_last_error().decode()}")
+                continue
+            torch.cuda.synchronize()
+            got = (Cv.view(M, N) if rowmajor == 0 else Cv.view(N, M).t()).float()
+            err = float((got - ref).abs().max() / ref.abs().max().clamp_min(1e-30))
+            if not err < 1e-2:
+                notes.append(f"orientation {rowmajor}: result differs (max rel err {err:.3g})")
+                continue
+
+            def fn(i, plan=plan):
+                d = sets[i % R]
+                rc = v.vsl_run(plan, d["A"].data_ptr(), d["C"].data_ptr(), torch.cuda.current_stream().cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(v.vsl_last_error().decode())
+
+            mode = "graph"
+            try:
+                t = timer(fn, steps, warmup)
+            except RuntimeError as e:
+                torch.cuda.synchronize()
+                mode = "eager"
+                notes.append(f"orientation {rowmajor}: graph capture failed ({e}); timed eagerly")
+                t = Timer(torch, graph=False, reps=timer.reps)(fn, steps, warmup)
+            if best is None or t < best[0]:
+                best = (t, rowmajor, mode, err)
+        finally:
+            torch.cuda.synchronize()
+            v.vsl_destroy(plan)
+    out = {"vendor_notes": notes} if notes else {}
+    if best is not None:
+        out.update(t_vendor_sparse_ms=best[0], vendor_orientation=["col-major", "row-major"][best[1]],
+                   vendor_timing=best[2], vendor_max_rel_err=best[3])
+    return out
+
+
 # ---------------------------------------------------------------- workloads
 def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, with_f16_dense=False):
     dev = torch.device("cuda")
@@ -282,7 +371,7 @@ def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, with_f16
     return out
 
 
-def w24_i8_out_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate=True):
+def w24_i8_out_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate=True, vendor=False):
     """2:4 and dense int8 GEMMs with the lower-traffic epilogue (fp16 or int8 output)."""
     dev = torch.device("cuda")
     M, K, N = c["M"], c["K"], c["N"]
@@ -300,8 +389,13 @@ def w24_i8_out_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate=
     de = lambda i: ssg.dense_gemm_i8_out(sets[i % R]["A"], sets[i % R]["Wt"], sets[i % R]["scale"],
                                          out_type=out_type, out=sets[i % R]["C"])
     st = timer.stats(sp, steps, warmup)
-    return dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
-                t_dense_ms=timer(de, steps, warmup), rotate_sets=R, out_bytes=ob)
+    out = dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
+               t_dense_ms=timer(de, steps, warmup), rotate_sets=R, out_bytes=ob)
+    if vendor and out_type == "f16":
+        # the vendor call applies no channel scale: its check is against the raw accumulators
+        acc = ssg.w24_gemm_i8_out(sets[0]["A"], sets[0]["vals"], sets[0]["meta"], None, out_type="i32")
+        out.update(vendor_w24_time(torch, 1, c["Wp"], sets, M, N, K, acc, steps, warmup, timer))
+    return out
 
 
 def tw_i8_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate=True):
@@ -326,7 +420,7 @@ def tw_i8_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate=True)
                 t_dense_ms=timer(de, steps, warmup), rotate_sets=R, ops=perf.tw_ops(M, nnz))
 
 
-def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
+def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, vendor=False):
     dev = torch.device("cuda")
     M, K, N = c["M"], c["K"], c["N"]
     t_pack, (vals, meta) = host_time_ms(lambda: ssg.w24_pack_f16(c["Wp"]))
@@ -339,10 +433,14 @@ def w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True):
     de = lambda i: ssg.dense_gemm_f16(sets[i % R]["A"], sets[i % R]["Wt"], out=sets[i % R]["C"])
     tm = lambda i: torch.matmul(sets[i % R]["A"], sets[i % R]["Wt"].T)
     st = timer.stats(sp, steps, warmup)
-    return dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
-                t_dense_ms=timer(de, steps, warmup), t_torch_ms=timer(tm, steps, warmup), rotate_sets=R,
-                t_pack_host_ms=t_pack, k_splits=ssg.splitk_suggest(ssg.SSG_KIND_W24_F16, M, N, K),
-                k_splits_dense=ssg.splitk_suggest(ssg.SSG_KIND_DENSE_F16, M, N, K))
+    out = dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
+               t_dense_ms=timer(de, steps, warmup), t_torch_ms=timer(tm, steps, warmup), rotate_sets=R,
+               t_pack_host_ms=t_pack, k_splits=ssg.splitk_suggest(ssg.SSG_KIND_W24_F16, M, N, K),
+               k_splits_dense=ssg.splitk_suggest(ssg.SSG_KIND_DENSE_F16, M, N, K))
+    if vendor:
+        sp(0)
+        out.update(vendor_w24_time(torch, 0, c["Wp"], sets, M, N, K, sets[0]["C"].clone(), steps, warmup, timer))
+    return out
 
 
 def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, extras=True):
@@ -442,6 +540,8 @@ def main(argv=None):
     ap.add_argument("--no-tw-extras", action="store_true",
                     help="table mode: time only the grouped tile-wise kernel (not the fused, row-major-A "
                          "and multi-stream variants)")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="table mode: skip the vendor 2:4 library (hipSPARSELt) beside the 2:4 kernels")
     ap.add_argument("--warm", action="store_true", help="one input set (cache-resident) instead of rotating")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a replayed HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -778,12 +878,16 @@ def table(a, torch, ssg, perf, wl, timer):
     want = set(a.workloads.split(",")) if a.workloads else set(WORKLOADS)
     timer.reps = 5
 
+    vendor = not a.no_vendor
+
     def emit(d):
+        if "t_vendor_sparse_ms" in d:
+            d["speedup_vs_vendor_sparse"] = d["t_vendor_sparse_ms"] / d["t_sparse_ms"]
         print(json.dumps(d), flush=True)
 
     if "small" in want:
         c = wl.make_small_w24_f16()
-        r = w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate)
+        r = w24_f16_case(torch, ssg, perf, c, steps, warmup, timer, rotate, vendor=vendor)
         nz, de = perf.w24_ops(c["M"], c["N"], c["K"])
         emit(dict(workload=c["name"] + "_w24_f16", shape=[c["M"], c["K"], c["N"]], **r,
                   tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
@@ -804,7 +908,7 @@ def table(a, torch, ssg, perf, wl, timer):
                   **perf.bound_report(nz, b, r["t_sparse_ms"], perf.PEAK_I8_TOPS * 1e12)))
         torch.cuda.empty_cache()
         for out_type in ("f16", "i8"):
-            r = w24_i8_out_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate)
+            r = w24_i8_out_case(torch, ssg, perf, c, out_type, steps, warmup, timer, rotate, vendor=vendor)
             b = perf.w24_bytes(c["M"], c["N"], c["K"], 1, 1, r["out_bytes"], True)
             emit(dict(workload=f"vit_base_fc1_w24_i8_{out_type}_out", shape=[c["M"], c["K"], c["N"]], **r,
                       tops_nonzero=nz / r["t_sparse_ms"] / 1e9, tops_dense_eq=de / r["t_sparse_ms"] / 1e9,
@@ -842,7 +946,7 @@ def table(a, torch, ssg, perf, wl, timer):
         for g in wl.vit_large_layers("f16", layers=1):
             if only5 and g["name"].rsplit("_", 1)[1] not in only5:
                 continue
-            r = w24_f16_case(torch, ssg, perf, g, steps, warmup, timer, rotate)
+            r = w24_f16_case(torch, ssg, perf, g, steps, warmup, timer, rotate, vendor=vendor)
             nz, de = perf.w24_ops(g["M"], g["N"], g["K"])
             emit(dict(workload=g["name"] + "_w24_f16", shape=[g["M"], g["K"], g["N"]], **r,
                       tflops_nonzero=nz / r["t_sparse_ms"] / 1e9, tflops_dense_eq=de / r["t_sparse_ms"] / 1e9,
@@ -856,7 +960,7 @@ def table(a, torch, ssg, perf, wl, timer):
         # 8 GPUs (M = 512 rows each; the packed weights are replicated)
         M8 = wl.VIT_LARGE_M // 8
         for g in wl.vit_large_layers("f16", layers=1, M=M8):
-            r = w24_f16_case(torch, ssg, perf, g, steps, warmup, timer, rotate)
+            r = w24_f16_case(torch, ssg, perf, g, steps, warmup, timer, rotate, vendor=vendor)
             nz, de = perf.w24_ops(g["M"], g["N"], g["K"])
             emit(dict(workload=g["name"].replace("vit_large_", "vit_large_shard8_") + "_w24_f16",
                       shape=[g["M"], g["K"], g["N"]], **r,

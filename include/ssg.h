@@ -240,11 +240,11 @@ enum { SSG_KIND_DENSE_F16 = 0, SSG_KIND_W24_F16 = 1, SSG_KIND_DENSE_I8 = 2, SSG_
 int64_t ssg_splitk_workspace_bytes(int64_t M, int64_t N, int32_t splits);
 
 /* The split count the library would take for a kind and shape (measured on
- * MI355X): 1 (do not split) when K has fewer than 32 stages or the output
- * tiles number more than 128 (fp16 kinds) / 64 (int8 kinds); otherwise the
- * largest power of two <= 16 with tiles x splits <= 256 (one workgroup per
- * CU) and at least 8 K stages per split.  Host-only; an invalid kind or
- * shape gives 1. */
+ * MI355X): 1 (do not split) when K has fewer than 64 stages (64 K elements
+ * per stage for the fp16 kinds, 128 for int8) or the output tiles of the
+ * library's tile choice number more than 128; otherwise the largest power of
+ * two <= 16 with tiles x splits <= 256 (one workgroup per CU) and at least 8
+ * K stages per split.  Host-only; an invalid kind or shape gives 1. */
 int32_t ssg_splitk_suggest(int32_t kind, int64_t M, int64_t N, int64_t K);
 
 int dense_gemm_f16_splitk(const void *A, const void *Wt, void *C, int64_t M, int64_t N, int64_t K,

@@ -66,7 +66,25 @@ def build(jobs=8, save_temps=False, verbose=False):
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp,
           *[_obj(s) for s in HOST_SOURCES + HIP_SOURCES]])
     os.replace(tmp, LIB)
+    build_vendor()
     return LIB
+
+
+VENDOR_LIB = os.path.join(PKG, "libssg_vendor.so")
+VENDOR_HEADER = "/opt/rocm/include/hipsparselt/hipsparselt.h"
+
+
+def build_vendor():
+    """The bench's vendor 2:4 baseline (hipSPARSELt), when its headers are
+    installed; a separate library that libssg never loads."""
+    if not os.path.exists(VENDOR_HEADER):
+        return None
+    tmp = VENDOR_LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=" + ARCH, "-O2", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+          "-Wno-unused-command-line-argument", os.path.join(CSRC, "vendor", "hipsparselt_ref.cpp"),
+          "-o", tmp, "-lhipsparselt"])
+    os.replace(tmp, VENDOR_LIB)
+    return VENDOR_LIB
 
 
 def main(argv=None):

@@ -41,8 +41,9 @@
 //     or y = float(acc) * scale[n] (+ bias[n]) written as fp32, as fp16
 //     rounded to nearest even, or as int8 rounded to nearest even and
 //     saturated to [-128, 127]);
-//   * a tile starts its K loop at stage 0 or, for the sparse 128 x 128 tiles,
-//     at a stage rotated by its tile id (measured per tile shape, see ROT);
+//   * a tile starts its K loop at stage 0 or, for the sparse tiles of 128 x 128
+//     and smaller, at a stage rotated by its tile id (measured per tile
+//     shape, see ROT);
 //   * split K (gridDim.y > 1, EPI_PART): workgroup (tile, y) runs K-stage range
 //     y and writes its raw accumulators to slice y of a workspace, which
 //     splitk.hip sums and finishes with the kind's epilogue.
@@ -209,13 +210,26 @@ struct Layout {
     static constexpr int M_STAGE = BN * MW * 4;
     static constexpr int STAGE = A_STAGE + W_STAGE + M_STAGE;
     // direct-to-LDS instructions per wave per stage (each moves 1 KiB, or
-    // 256 bytes for the 4-byte meta loads)
+    // 256 bytes for the 4-byte meta loads).  A 64-channel fp16 tile has 2
+    // meta chunks of 256 bytes for 4 waves: then waves w and w + MCH load the
+    // same chunk into the same LDS bytes (identical data), so that every wave
+    // issues the same number of loads per stage and one counter value means
+    // "stage complete" for all of them.
+    static constexpr int MCH = M_STAGE / 256;
     static constexpr int LA = A_STAGE / 1024 / NW;
     static constexpr int LW = W_STAGE / 1024 / NW;
-    static constexpr int LM = M_STAGE / 256 / NW;
+    static constexpr int LM = MCH >= NW ? MCH / NW : (MCH > 0 ? 1 : 0);
     static constexpr int L = LA + LW + LM;
-    static_assert(LA * NW * 1024 == A_STAGE && LW * NW * 1024 == W_STAGE && LM * NW * 256 == M_STAGE,
+    static_assert(LA * NW * 1024 == A_STAGE && LW * NW * 1024 == W_STAGE && MCH * 256 == M_STAGE &&
+                      (MCH == 0 || MCH % NW == 0 || NW % MCH == 0),
                   "stage does not split evenly over the waves");
+    // meta chunk of this wave's j-th meta load (no modulo unless chunks are
+    // shared: on the 128 x 256 int8 tiles it cost the registers that keep
+    // two workgroups per CU)
+    static __device__ __forceinline__ int mchunk(int j, int wave) {
+        if constexpr (MCH >= NW) return j * NW + wave;
+        else return wave % (MCH > 0 ? MCH : 1);
+    }
 };
 
 template <int KIND, int EPI, class CF>
@@ -291,7 +305,7 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     uint32_t om[LY::LM > 0 ? LY::LM : 1];
 #pragma unroll
     for (int j = 0; j < LY::LM; ++j) {
-        const int word = (j * LY::NW + wave) * 64 + lane;  // row-major [BN][MW]
+        const int word = LY::mchunk(j, wave) * 64 + lane;  // row-major [BN][MW]
         const int row = word / (MW > 0 ? MW : 1), w = word % (MW > 0 ? MW : 1);
         om[j] = (uint32_t(min(n0 + row, N - 1)) * uint32_t(m_row) + w) * 4;
     }
@@ -320,7 +334,7 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
             dma16(bufW, ow[j] + uint32_t(sg * WB), base + A_STAGE + (j * LY::NW + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < LY::LM; ++j)
-            dma4(bufM, om[j] + uint32_t(sg * MW * 4), base + A_STAGE + W_STAGE + (j * LY::NW + wave) * 256);
+            dma4(bufM, om[j] + uint32_t(sg * MW * 4), base + A_STAGE + W_STAGE + LY::mchunk(j, wave) * 256);
     };
 
     // Fragments of one k-step (one matrix instruction deep) for the wave's
@@ -537,7 +551,20 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 //          outputs (N = 1024) that would leave CUs idle with big tiles;
 //   Small2 128 x 128, 4 waves, 2 stages (three int8 workgroups per CU) --
 //          short-K int8 GEMMs whose Mid tiles would fill the chip more than
-//          twice or less than once, and the dense int8 GEMMs at short K.
+//          twice or less than once, and the dense int8 GEMMs at short K;
+//   T64    64 x 64 and T64N 64 x 128, 4 waves of 32 x 32 / 32 x 64, 3 stages
+//          -- GEMMs with at most 128 tiles of 128 x 128 (half the CUs), e.g.
+//          one GPU's share of a token-sharded layer (M = 512).  With so few
+//          tiles each workgroup's K loop runs alone on its CU, limited by
+//          what its four waves can pull into LDS per stage; smaller tiles
+//          put more CUs to work and each moves less (int8 2:4 512 x 1024 x
+//          1024: 9.2 us on 128 x 128, 5.8 on 64 x 64; 512 x 4096 x 1024:
+//          19.6 -> 12.6 us; fp16 2:4 512 x 1024 x 1024: 10.7 us -> 9.0 on
+//          64 x 128).  A deeper ring (4-6 stages) on 128 x 128 gained nothing
+//          there.  The fp16 kinds keep 64 x 128 once 64 x 64 tiles would
+//          outnumber the CUs (dense fp16 512 x 1024 x 3072: 10.1 us on
+//          64 x 128, 11.1 on 64 x 64); int8, with half as many K stages,
+//          takes 64 x 64 throughout.
 // K-loop start (ROT), measured with both variants timed in one process over
 // alternating rounds, on input sets rotated through more than twice the
 // 256 MB Infinity Cache: every dense kind and the sparse Big and Mid tiles run
@@ -545,7 +572,7 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 // 4096x2048x4096), while the sparse 128 x 128 tiles run 4-10 % faster rotated
 // (fp16 ViT-L fc2 42.1 vs 46.2 us, int8 4096x8192x1024 43.7 vs 47.7 us; the
 // short-K int8 one is within noise either way).  So ROT = sparse kind on a
-// 128 x 128 tile.
+// 128 x 128 tile, and on the 64-row tiles below (not measured apart there).
 template <bool NTS>
 using CfgBig = Cfg<4, 2, 2, 4, 3, 8, NTS, false>;
 template <bool NTS>
@@ -556,13 +583,30 @@ template <bool NTS, bool ROT>
 using CfgSmall = Cfg<2, 2, 2, 2, 3, 8, NTS, ROT>;
 template <bool NTS, bool ROT>
 using CfgSmall2 = Cfg<2, 2, 2, 2, 2, 8, NTS, ROT>;
+template <bool NTS, bool ROT>
+using CfgT64 = Cfg<2, 2, 1, 1, 3, 8, NTS, ROT>;
+template <bool NTS, bool ROT>
+using CfgT64N = Cfg<2, 2, 1, 2, 3, 8, NTS, ROT>;
 
-enum Shape { SHAPE_BIG, SHAPE_MID, SHAPE_SMALL, SHAPE_SMALL2 };
+enum Shape { SHAPE_BIG, SHAPE_MID, SHAPE_SMALL, SHAPE_SMALL2, SHAPE_T64, SHAPE_T64N };
 
 static long tiles(int M, int N, int bm, int bn) { return long((M + bm - 1) / bm) * long((N + bn - 1) / bn); }
 
-// f16 kinds: big tiles when they still give >= 3/4 of a tile per CU.
-static Shape pick_f16(int M, int N) { return tiles(M, N, 256, 256) >= 192 ? SHAPE_BIG : SHAPE_SMALL; }
+// tile rows x columns of a shape
+static void tile_dims(Shape sh, int &bm, int &bn) {
+    bm = sh == SHAPE_BIG ? 256 : (sh == SHAPE_T64 || sh == SHAPE_T64N) ? 64 : 128;
+    bn = (sh == SHAPE_BIG || sh == SHAPE_MID) ? 256 : sh == SHAPE_T64 ? 64 : 128;
+}
+
+// few output tiles: at most half the CUs would get a 128 x 128 tile
+static bool few_tiles(int M, int N) { return tiles(M, N, 128, 128) <= 128; }
+
+// f16 kinds: big tiles when they still give >= 3/4 of a tile per CU; 64-row
+// tiles for few-tile GEMMs.
+static Shape pick_f16(int M, int N) {
+    if (few_tiles(M, N)) return tiles(M, N, 64, 64) <= 256 ? SHAPE_T64 : SHAPE_T64N;
+    return tiles(M, N, 256, 256) >= 192 ? SHAPE_BIG : SHAPE_SMALL;
+}
 
 // int8 kinds.  Short K (<= 1024): the per-tile prologue and the output
 // stream weigh most, so the choice follows how evenly the tiles fill the
@@ -573,6 +617,7 @@ static Shape pick_f16(int M, int N) { return tiles(M, N, 256, 256) >= 192 ? SHAP
 // takes Small2 unless Big tiles fill the chip one to two times (ViT-L fc1).
 // Long K: as the f16 kinds.
 static Shape pick_i8(int M, int N, int K, bool dense) {
+    if (few_tiles(M, N)) return SHAPE_T64;
     if (K <= 1024) {
         if (dense) {
             const long big = tiles(M, N, 256, 256);
@@ -592,6 +637,11 @@ static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const ui
         else return launch<KIND, EPI, CfgBig<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     }
     if (sh == SHAPE_MID) return launch<KIND, EPI, CfgMid<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
+    constexpr bool ROT = KindTraits<KIND>::kSparse;
+    if (sh == SHAPE_T64) return launch<KIND, EPI, CfgT64<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
+    if constexpr (!KindTraits<KIND>::kI8)  // (only the fp16 kinds pick T64N)
+        if (sh == SHAPE_T64N)
+            return launch<KIND, EPI, CfgT64N<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     if constexpr (KindTraits<KIND>::kI8)  // (only the int8 kinds pick Small2)
         if (sh == SHAPE_SMALL2)
             return launch<KIND, EPI, CfgSmall2<NTS, KindTraits<KIND>::kSparse>>(A, Wv, meta, scale, bias, C, M, N, K,
@@ -670,24 +720,28 @@ hipError_t launch_gemm_partials(int kind, const void *A, const void *W, const ui
 // GPU's share of a token-sharded layer, e.g. 512 x 4096 x 1024): each tile's
 // K loop is a chain of dependent stage loads, and cutting it into ranges run
 // side by side shortens the chain, at the price of a second launch and the
-// partials' round trip through memory (8 * M * N bytes per split).  Measured
-// on MI355X with graph-timed replays (fp16 2:4, 512 x 4096 x 1024: 31.0 us
-// unsplit, 16.0 us with 8 splits; 512 x 8192 x 1024: 56.3 -> 21.6 us; int8
-// 2:4, 512 x 4096 x 1024: 18.7 -> 14.8 us with 4 splits), the split loses
-// whenever K has fewer than 32 stages (K = 1024: 10.7 -> 11.9 us and worse)
-// or the tiles already number more than 128 (fp16) / 64 (int8).  Within
-// those bounds the splits double while tiles x splits stays within one
-// workgroup per CU and every split keeps at least 8 stages.
+// partials' round trip through memory (8 * M * N bytes per split).  Few-tile
+// GEMMs already run on 64-row tiles (more workgroups, shorter chains per
+// stage), so the split only pays from 64 K stages on.  Measured on MI355X
+// with graph-timed replays on those tiles: fp16 2:4 512 x 4096 x 1024 (64
+// stages, 128 tiles) 20.6 us unsplit, 15.6 with 2 splits; 128 x 4096 x 4096
+// 20.2 -> 16.3; int8 2:4 512 x 8192 x 1024 21.1 -> 15.6; but with 32 stages
+// (int8 512 x 4096 x 1024, fp16 256 x 2048 x 2048) 2 splits are no faster,
+// and with more than 128 tiles every split loses (fp16 1024 x 4096 x 1024:
+// 21.9 -> 26.5 us).  Within those bounds the splits double while tiles x
+// splits stays within one workgroup per CU and every split keeps at least 8
+// stages.
 int suggest_splits(int kind, int M, int N, int K) {
     constexpr int kCUs = 256;
     if (M <= 0 || N <= 0 || K <= 0) return 1;
     const bool i8 = kind == DENSE_I8 || kind == W24_I8;
     const bool dense = kind == DENSE_F16 || kind == DENSE_I8;
     const Shape sh = i8 ? pick_i8(M, N, K, dense) : pick_f16(M, N);
-    const int bm = sh == SHAPE_BIG ? 256 : 128, bn = (sh == SHAPE_BIG || sh == SHAPE_MID) ? 256 : 128;
+    int bm, bn;
+    tile_dims(sh, bm, bn);
     const long t = tiles(M, N, bm, bn);
     const int S = gemm_k_stages(kind, K);
-    if (S < 32 || t > (i8 ? 64 : 128)) return 1;
+    if (S < 64 || t > 128) return 1;
     int p = 1;
     while (p < 16 && t * 2 * p <= kCUs && S % (2 * p) == 0 && S / (2 * p) >= 8) p *= 2;
     return p;

@@ -172,9 +172,15 @@ def test_splitk_host_helpers(lib):
     assert raw.ssg_splitk_workspace_bytes(512, 1024, 8) == 8 * 512 * 1024 * 4
     assert raw.ssg_splitk_workspace_bytes(512, 1024, 1) == 0
     assert raw.ssg_splitk_workspace_bytes(-1, 1024, 8) == 0
-    # one GPU's share of ViT-L fc2 (M = 512): 32 tiles on 256 CUs -> split
-    assert lib.splitk_suggest(lib.SSG_KIND_W24_F16, 512, 1024, 4096) > 1
-    assert lib.splitk_suggest(lib.SSG_KIND_W24_I8, 512, 1024, 4096) > 1
+    # one GPU's share of ViT-L fc2 (M = 512): 128 tiles of 64 x 64 on 256 CUs;
+    # fp16 has 64 K stages -> split, int8 32 -> none; int8 at K = 8192 -> split
+    assert lib.splitk_suggest(lib.SSG_KIND_W24_F16, 512, 1024, 4096) == 2
+    assert lib.splitk_suggest(lib.SSG_KIND_W24_I8, 512, 1024, 4096) == 1
+    assert lib.splitk_suggest(lib.SSG_KIND_W24_I8, 512, 1024, 8192) == 2
+    # 64 x 64 tiles for 128 x 4096 -> 2 x 64 = 128 tiles, 64 stages -> 2 splits
+    assert lib.splitk_suggest(lib.SSG_KIND_W24_F16, 128, 4096, 4096) == 2
+    # more than 128 tiles -> no split (1024 x 1024 output: 256 tiles of 64 x 64)
+    assert lib.splitk_suggest(lib.SSG_KIND_W24_F16, 1024, 1024, 4096) == 1
     # the ViT-Base fc1 shape fills the chip several times over -> no split
     for kind in range(4):
         assert lib.splitk_suggest(kind, 12608, 3072, 768) == 1
