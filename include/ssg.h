@@ -247,6 +247,16 @@ int64_t ssg_splitk_workspace_bytes(int64_t M, int64_t N, int32_t splits);
  * K stages per split.  Host-only; an invalid kind or shape gives 1. */
 int32_t ssg_splitk_suggest(int32_t kind, int64_t M, int64_t N, int64_t K);
 
+/* The output tile the GEMM calls of a kind use for a shape (measured choice,
+ * see the tile notes of the GEMM kernels): rows * 1024 + columns, rows and
+ * columns each one of 64, 128, 256.  256 x 256 once such tiles give about a
+ * tile per CU; 64 x 64 (64 x 128 for the fp16 kinds when 64 x 64 tiles would
+ * outnumber the 256 CUs) when the output has at most 128 tiles of 128 x 128
+ * (192 for the int8 kinds with K <= 1024);
+ * otherwise 128 x 128 or 128 x 256.  Host-only; 0 for an invalid kind or
+ * shape. */
+int32_t ssg_tile_choice(int32_t kind, int64_t M, int64_t N, int64_t K);
+
 int dense_gemm_f16_splitk(const void *A, const void *Wt, void *C, int64_t M, int64_t N, int64_t K,
                           int32_t splits, void *ws, int64_t ws_bytes, void *stream);
 int w24_gemm_f16_splitk(const void *A, const void *vals, const uint32_t *meta, void *C,

@@ -39,6 +39,7 @@ from ._lib import (  # noqa: F401
     dense_gemm_i8_splitk,
     w24_gemm_i8_splitk,
     splitk_suggest,
+    tile_choice,
     splitk_workspace_bytes,
     SSG_KIND_DENSE_F16,
     SSG_KIND_W24_F16,

@@ -68,6 +68,7 @@ SIGNATURES = {
     "dense_gemm_i8_splitk": [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _I64, _P],
     "w24_gemm_i8_splitk": [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _I64, _P],
     "ssg_splitk_suggest": [_I32, _I64, _I64, _I64],
+    "ssg_tile_choice": [_I32, _I64, _I64, _I64],
 }
 
 
@@ -314,6 +315,12 @@ SSG_KIND_DENSE_F16, SSG_KIND_W24_F16, SSG_KIND_DENSE_I8, SSG_KIND_W24_I8 = 0, 1,
 def splitk_suggest(kind, M, N, K):
     """The library's K-split count for a GEMM kind and shape (1 = unsplit)."""
     return int(load().ssg_splitk_suggest(kind, M, N, K))
+
+
+def tile_choice(kind, M, N, K):
+    """(rows, columns) of the output tile the library's GEMMs use for a kind and shape."""
+    v = int(load().ssg_tile_choice(kind, M, N, K))
+    return v // 1024, v % 1024
 
 
 def splitk_workspace_bytes(M, N, splits):

@@ -210,6 +210,13 @@ SSG_API int32_t ssg_splitk_suggest(int32_t kind, int64_t M, int64_t N, int64_t K
     return ssg::suggest_splits(int(kind), int(M), int(N), int(K));
 }
 
+SSG_API int32_t ssg_tile_choice(int32_t kind, int64_t M, int64_t N, int64_t K) {
+    if (kind < 0 || kind > 3 || M <= 0 || N <= 0 || K <= 0 || !fits_int(M) || !fits_int(N) || !fits_int(K)) return 0;
+    int bm = 0, bn = 0;
+    ssg::tile_choice(int(kind), int(M), int(N), int(K), &bm, &bn);
+    return bm * 1024 + bn;
+}
+
 SSG_API int dense_gemm_f16_splitk(const void *A, const void *Wt, void *C, int64_t M, int64_t N, int64_t K,
                                   int32_t splits, void *ws, int64_t ws_bytes, void *stream) {
     return split_run("dense_gemm_f16_splitk", 0, A, Wt, nullptr, nullptr, nullptr, C, 0, M, N, K, splits, ws,

@@ -553,7 +553,8 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 //          short-K int8 GEMMs whose Mid tiles would fill the chip more than
 //          twice or less than once, and the dense int8 GEMMs at short K;
 //   T64    64 x 64 and T64N 64 x 128, 4 waves of 32 x 32 / 32 x 64, 3 stages
-//          -- GEMMs with at most 128 tiles of 128 x 128 (half the CUs), e.g.
+//          -- GEMMs with at most 128 tiles of 128 x 128 (half the CUs; int8
+//          with K <= 1024: 192), e.g.
 //          one GPU's share of a token-sharded layer (M = 512).  With so few
 //          tiles each workgroup's K loop runs alone on its CU, limited by
 //          what its four waves can pull into LDS per stage; smaller tiles
@@ -598,8 +599,8 @@ static void tile_dims(Shape sh, int &bm, int &bn) {
     bn = (sh == SHAPE_BIG || sh == SHAPE_MID) ? 256 : sh == SHAPE_T64 ? 64 : 128;
 }
 
-// few output tiles: at most half the CUs would get a 128 x 128 tile
-static bool few_tiles(int M, int N) { return tiles(M, N, 128, 128) <= 128; }
+// few output tiles: at most `limit` tiles of 128 x 128 (128 = half the CUs)
+static bool few_tiles(int M, int N, long limit = 128) { return tiles(M, N, 128, 128) <= limit; }
 
 // f16 kinds: big tiles when they still give >= 3/4 of a tile per CU; 64-row
 // tiles for few-tile GEMMs.
@@ -617,7 +618,10 @@ static Shape pick_f16(int M, int N) {
 // takes Small2 unless Big tiles fill the chip one to two times (ViT-L fc1).
 // Long K: as the f16 kinds.
 static Shape pick_i8(int M, int N, int K, bool dense) {
-    if (few_tiles(M, N)) return SHAPE_T64;
+    // (short K: up to 192 tiles; 1024 x 1024 x 3072 2:4 9.9 -> 9.1 us, dense
+    // 9.9 -> 8.1; at 256 tiles within 5 %, and with K = 4096 at 192 tiles the
+    // 128-row tiles stay ahead, 20.4 vs 24.7 us)
+    if (few_tiles(M, N, K <= 1024 ? 192 : 128)) return SHAPE_T64;
     if (K <= 1024) {
         if (dense) {
             const long big = tiles(M, N, 256, 256);
@@ -731,6 +735,13 @@ hipError_t launch_gemm_partials(int kind, const void *A, const void *W, const ui
 // 21.9 -> 26.5 us).  Within those bounds the splits double while tiles x
 // splits stays within one workgroup per CU and every split keeps at least 8
 // stages.
+// Tile rows x columns the launchers pick for a kind and shape.
+void tile_choice(int kind, int M, int N, int K, int *bm, int *bn) {
+    const bool i8 = kind == DENSE_I8 || kind == W24_I8;
+    const bool dense = kind == DENSE_F16 || kind == DENSE_I8;
+    tile_dims(i8 ? pick_i8(M, N, K, dense) : pick_f16(M, N), *bm, *bn);
+}
+
 int suggest_splits(int kind, int M, int N, int K) {
     constexpr int kCUs = 256;
     if (M <= 0 || N <= 0 || K <= 0) return 1;

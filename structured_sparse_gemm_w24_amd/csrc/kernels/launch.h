@@ -44,6 +44,8 @@ hipError_t launch_splitk_reduce(const void *ws, int splits, bool i8, const float
 // K splits worth taking for a kind and shape (1 = do not split); a host-only
 // rule from the tile choice, the resident workgroups per CU and the K stages.
 int suggest_splits(int kind, int M, int N, int K);
+// tile rows x columns the GEMM launchers pick for a kind (0-3) and shape
+void tile_choice(int kind, int M, int N, int K, int *bm, int *bn);
 // K stages (one per 128 bytes of an A row) for a kind and K.
 inline int gemm_k_stages(int kind, int K) { return (kind == 2 || kind == 3) ? K / 128 : K / 64; }
 

@@ -194,6 +194,26 @@ def test_splitk_host_helpers(lib):
     assert lib.splitk_suggest(1, 0, 1024, 4096) == 1
 
 
+def test_tile_choice_host_query(lib):
+    F16, D16, I8, D8 = lib.SSG_KIND_W24_F16, lib.SSG_KIND_DENSE_F16, lib.SSG_KIND_W24_I8, lib.SSG_KIND_DENSE_I8
+    # the headline shape (ViT-Base fc1, int8): 2376 tiles of 128 x 128
+    assert lib.tile_choice(I8, 12608, 3072, 768) == (128, 128)
+    assert lib.tile_choice(D8, 12608, 3072, 768) == (128, 128)
+    # ViT-L fc1 (fp16): 256 x 256 tiles fill the chip
+    assert lib.tile_choice(F16, 4096, 4096, 1024) == (256, 256)
+    # one GPU's share of ViT-L (M = 512): 64-row tiles
+    for kind in (F16, D16, I8, D8):
+        assert lib.tile_choice(kind, 512, 1024, 1024) == (64, 64)
+    assert lib.tile_choice(F16, 512, 4096, 1024) == (64, 128)  # 64 x 64 tiles would number 512
+    assert lib.tile_choice(I8, 512, 4096, 1024) == (64, 64)
+    # 192 tiles of 128 x 128: int8 at short K takes 64 x 64, fp16 and long-K int8 do not
+    assert lib.tile_choice(I8, 1024, 3072, 1024) == (64, 64)
+    assert lib.tile_choice(F16, 1024, 3072, 1024) == (128, 128)
+    assert lib.tile_choice(I8, 1024, 3072, 4096) == (128, 128)
+    assert lib.tile_choice(7, 512, 1024, 1024) == (0, 0)
+    assert lib.tile_choice(F16, 0, 1024, 1024) == (0, 0)
+
+
 def test_splitk_zero_rows_is_ok_without_touching_the_device(lib):
     raw = _raw(lib)
     assert raw.w24_gemm_f16_splitk(None, None, None, None, 0, 64, 128, 2, None, 0, None) == 0
