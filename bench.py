@@ -487,10 +487,12 @@ def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, extras=True)
 
 
 # ---------------------------------------------------------------- cpu baseline
-def cpu_baseline(c, perf, budget_s=12.0, one_core_rows=1024):
+def cpu_baseline(c, perf, budget_s=12.0, one_core_rows=1024, gpu_out=None):
     """The oracle as it stands, on the host cores, over a bounded number of full
     repetitions; then on one core over the first `one_core_rows` token rows
-    (median of 3), the same GEMM restricted to a slice of A."""
+    (median of 3), the same GEMM restricted to a slice of A.  gpu_out (host
+    copy of a timed launch's output) is compared with the first repetition's
+    result bit for bit."""
     import oracle
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
@@ -498,9 +500,11 @@ def cpu_baseline(c, perf, budget_s=12.0, one_core_rows=1024):
     except Exception:
         threadpool_limits = None
         threads = os.cpu_count() or 1
-    reps, t0 = 0, time.perf_counter()
+    reps, t0, ref = 0, time.perf_counter(), None
     while True:
-        oracle.ref_gemm_i8(c["A"], c["Wp"], c["scale"])
+        C_ref = oracle.ref_gemm_i8(c["A"], c["Wp"], c["scale"])
+        if ref is None:
+            ref = C_ref
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 200:
@@ -509,6 +513,12 @@ def cpu_baseline(c, perf, budget_s=12.0, one_core_rows=1024):
     out = {"value": nz * reps / el / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
            "sample": f"full {c['M']}x{c['K']}x{c['N']} int8 GEMM + epilogue (numpy float64 BLAS), "
                      f"{reps} repetition(s), {el:.1f} s; host {platform.processor() or platform.machine()}"}
+    if gpu_out is not None:
+        diff = np.abs(gpu_out.astype(np.float64) - ref.astype(np.float64))
+        out["parity"] = {"what": "output of a timed launch vs the oracle's first repetition, every element",
+                         "elements": int(ref.size), "bit_exact": bool(np.array_equal(gpu_out.view(np.uint32),
+                                                                                      ref.view(np.uint32))),
+                         "max_abs_diff": float(np.nanmax(diff)) if diff.size else 0.0}
     if threadpool_limits is not None:
         rows = min(one_core_rows, c["M"])
         A = np.ascontiguousarray(c["A"][:rows])
@@ -628,11 +638,18 @@ def main(argv=None):
         "roofline": perf.roofline(achieved, perf.PEAK_HBM_GBS, "GB/s", "hbm", traffic),
         "cpu_baseline": None,
     }
+    # one more launch of the timed step on set 0 (the dense timing shares the
+    # output buffers), copied out for the oracle's check
+    C_gpu = None
+    if not a.no_cpu:
+        step(0)
+        torch.cuda.synchronize()
+        C_gpu = r["sets"][0]["C"].cpu().numpy()
     del r
     torch.cuda.empty_cache()
     if not a.no_cpu:
         log("timing the CPU oracle ...")
-        line["cpu_baseline"] = cpu_baseline(c, perf)
+        line["cpu_baseline"] = cpu_baseline(c, perf, gpu_out=C_gpu)
     print(json.dumps(line), flush=True)
     return 0
 

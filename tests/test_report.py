@@ -92,3 +92,24 @@ def test_kernel_hash_ignores_comments_and_layout():
     b = "/* header\n   text */ int f(int x) { return x + 1; }"
     c = "int f(int x) { return x + 2; }"
     assert bench._code_only(a) == bench._code_only(b) != bench._code_only(c)
+
+
+def test_cpu_baseline_parity_field():
+    """The headline's oracle leg compares a GPU output with the oracle bit for
+    bit; a single changed element must flip the verdict."""
+    import numpy as np
+
+    import bench
+    import oracle
+    import workloads as wl
+    case = wl.random_24_i8(np.random.default_rng(5), 64, 256, 128)
+    c = dict(case, M=64, K=256, N=128)
+    good = oracle.ref_gemm_i8(case["A"], case["Wp"], case["scale"])
+    out = bench.cpu_baseline(c, perf, budget_s=0.01, gpu_out=good.copy())
+    assert out["parity"]["bit_exact"] and out["parity"]["max_abs_diff"] == 0.0
+    assert out["parity"]["elements"] == 64 * 128
+    bad = good.copy()
+    bad[3, 7] = np.nextafter(bad[3, 7], np.float32(np.inf))
+    out = bench.cpu_baseline(c, perf, budget_s=0.01, gpu_out=bad)
+    assert not out["parity"]["bit_exact"] and out["parity"]["max_abs_diff"] > 0
+    assert "parity" not in bench.cpu_baseline(c, perf, budget_s=0.01)
