@@ -217,3 +217,21 @@ def test_tile_choice_host_query(lib):
 def test_splitk_zero_rows_is_ok_without_touching_the_device(lib):
     raw = _raw(lib)
     assert raw.w24_gemm_f16_splitk(None, None, None, None, 0, 64, 128, 2, None, 0, None) == 0
+
+
+def test_vendor_baseline_is_outside_the_product():
+    """The bench's hipSPARSELt baseline lives in its own library: libssg does not
+    link hipSPARSELt and the package never names the vendor library."""
+    import glob
+    import subprocess
+    import structured_sparse_gemm_w24_amd as ssg
+    pkg = os.path.dirname(ssg.__file__)
+    dyn = subprocess.run(["readelf", "-d", os.path.join(pkg, "libssg.so")], capture_output=True, text=True)
+    assert dyn.returncode == 0 and "NEEDED" in dyn.stdout
+    assert "hipsparselt" not in dyn.stdout.lower()
+    for path in glob.glob(os.path.join(pkg, "*.py")) + glob.glob(os.path.join(pkg, "csrc", "*.*")) + \
+            glob.glob(os.path.join(pkg, "csrc", "kernels", "*.*")):
+        if path.endswith("build.py"):
+            continue  # the build step is what builds the separate bench library
+        text = open(path, errors="replace").read()
+        assert "libssg_vendor" not in text and "hipsparselt" not in text.lower(), path

@@ -146,3 +146,38 @@ def test_split_k_on_64x64_tiles(lib, gpu):
     vals, meta = lib.w24_pack_f16(case["Wp"])
     C = H(lib.w24_gemm_f16(T(case["A"]), T(vals), T(meta.view(np.int32))))
     _check_f16(C, case["A"], case["Wp"], "w24 f16 split on 64x64")
+
+
+# Shapes on both sides of each tile-rule boundary: (kind, M, K, N, tile).
+F16_BOUNDARY = [(1024, 128, 1024, (64, 64)),     # 256 tiles of 64 x 64
+                (1032, 128, 1024, (64, 128)),    # 272 would be too many
+                (1024, 128, 2048, (64, 128)),    # 128 tiles of 128 x 128
+                (1032, 128, 2048, (128, 128))]   # 144: not few any more
+I8_BOUNDARY = [(1536, 256, 2048, (64, 64)),      # short K: 192 tiles of 128 x 128
+               (1544, 256, 2048, (128, 128)),    # 208
+               (1024, 1152, 2048, (64, 64)),     # long K: 128
+               (1032, 1152, 2048, (128, 128))]   # 144
+
+
+@pytest.mark.parametrize("M,K,N,tile", F16_BOUNDARY)
+def test_f16_tile_rule_boundaries(lib, gpu, M, K, N, tile):
+    case = wl.random_24_f16(np.random.default_rng(M * 7 + N), M, K, N)
+    assert lib.tile_choice(lib.SSG_KIND_W24_F16, M, N, K) == tile
+    assert lib.tile_choice(lib.SSG_KIND_DENSE_F16, M, N, K) == tile
+    vals, meta = lib.w24_pack_f16(case["Wp"])
+    C = H(lib.w24_gemm_f16(T(case["A"]), T(vals), T(meta.view(np.int32))))
+    _check_f16(C, case["A"], case["Wp"], f"w24 f16 {M}x{K}x{N}")
+    C = H(lib.dense_gemm_f16(T(case["A"]), T(case["W"].T)))
+    _check_f16(C, case["A"], case["W"], f"dense f16 {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M,K,N,tile", I8_BOUNDARY)
+def test_i8_tile_rule_boundaries(lib, gpu, M, K, N, tile):
+    case = wl.random_24_i8(np.random.default_rng(M * 5 + K), M, K, N)
+    assert lib.tile_choice(lib.SSG_KIND_W24_I8, M, N, K) == tile
+    assert lib.tile_choice(lib.SSG_KIND_DENSE_I8, M, N, K) == tile
+    vals, meta = lib.w24_pack_i8(case["Wp"])
+    C = H(lib.w24_gemm_i8(T(case["A"]), T(vals), T(meta.view(np.int32)), T(case["scale"])))
+    assert np.array_equal(C.view(np.uint32), oracle.ref_gemm_i8(case["A"], case["Wp"], case["scale"]).view(np.uint32))
+    C = H(lib.dense_gemm_i8(T(case["A"]), T(case["W"].T), T(case["scale"])))
+    assert np.array_equal(C.view(np.uint32), oracle.ref_gemm_i8(case["A"], case["W"], case["scale"]).view(np.uint32))
