@@ -257,7 +257,12 @@ def vendor_lib():
         path = os.path.join(ROOT, "structured_sparse_gemm_w24_amd", "libssg_vendor.so")
         v = None
         if os.path.exists(path):
-            v = ct.CDLL(path)
+            try:
+                v = ct.CDLL(path)
+            except OSError as e:
+                log(f"vendor baseline not loaded: {e}")
+                _VENDOR.append(None)
+                return None
             v.vsl_create.restype = ct.c_void_p
             v.vsl_create.argtypes = [ct.c_int] * 5 + [ct.c_float] + [ct.c_void_p] * 4
             v.vsl_run.restype = ct.c_int

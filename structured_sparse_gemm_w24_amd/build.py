@@ -76,13 +76,19 @@ VENDOR_HEADER = "/opt/rocm/include/hipsparselt/hipsparselt.h"
 
 def build_vendor():
     """The bench's vendor 2:4 baseline (hipSPARSELt), when its headers are
-    installed; a separate library that libssg never loads."""
+    installed; a separate library that libssg never loads.  A failure here is
+    reported and leaves the product build alone (the bench then skips the
+    vendor columns)."""
     if not os.path.exists(VENDOR_HEADER):
         return None
     tmp = VENDOR_LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=" + ARCH, "-O2", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
-          "-Wno-unused-command-line-argument", os.path.join(CSRC, "vendor", "hipsparselt_ref.cpp"),
-          "-o", tmp, "-lhipsparselt"])
+    try:
+        _run([HIPCC, "--offload-arch=" + ARCH, "-O2", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+              "-Wno-unused-command-line-argument", os.path.join(CSRC, "vendor", "hipsparselt_ref.cpp"),
+              "-o", tmp, "-lhipsparselt"])
+    except RuntimeError as e:
+        print(f"note: vendor baseline library not built ({str(e).splitlines()[0]})", file=sys.stderr)
+        return None
     os.replace(tmp, VENDOR_LIB)
     return VENDOR_LIB
 
