@@ -249,10 +249,12 @@ int32_t ssg_splitk_suggest(int32_t kind, int64_t M, int64_t N, int64_t K);
 
 /* The output tile the GEMM calls of a kind use for a shape (measured choice,
  * see the tile notes of the GEMM kernels): rows * 1024 + columns, rows and
- * columns each one of 64, 128, 256.  256 x 256 once such tiles give about a
- * tile per CU; 64 x 64 (64 x 128 for the fp16 kinds when 64 x 64 tiles would
- * outnumber the 256 CUs) when the output has at most 128 tiles of 128 x 128
- * (192 for the int8 kinds with K <= 1024);
+ * columns each one of 32, 64, 128, 256.  256 x 256 once such tiles give about
+ * a tile per CU; when the output has at most 128 tiles of 128 x 128 (192 for
+ * the int8 kinds with K <= 1024): 32 x 32 if those number at most 512 and K
+ * has fewer than 64 stages (64 K elements per stage for fp16, 128 for int8),
+ * else 64 x 64 (64 x 128 for the fp16 kinds when 64 x 64 tiles would
+ * outnumber the 256 CUs);
  * otherwise 128 x 128 or 128 x 256.  Host-only; 0 for an invalid kind or
  * shape. */
 int32_t ssg_tile_choice(int32_t kind, int64_t M, int64_t N, int64_t K);

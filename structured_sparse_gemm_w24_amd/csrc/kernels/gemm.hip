@@ -565,7 +565,12 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 //          there.  The fp16 kinds keep 64 x 128 once 64 x 64 tiles would
 //          outnumber the CUs (dense fp16 512 x 1024 x 3072: 10.1 us on
 //          64 x 128, 11.1 on 64 x 64); int8, with half as many K stages,
-//          takes 64 x 64 throughout.
+//          takes 64 x 64 throughout;
+//   T32    32 x 32, one wave, 3 stages -- the smallest GEMMs (at most 512
+//          such tiles and fewer than 64 K stages): fp16 2:4 256 x 512 x 512
+//          5.2 -> 4.4 us, 384 x 1024 x 1024 7.3 -> 6.4; int8 2:4 128 x 4096
+//          x 4096 12.3 -> 10.5 (against 64-row tiles, same sweep); at 1024
+//          tiles (1024 x 1024 outputs) the 64-row tiles are ahead again.
 // K-loop start (ROT), measured with both variants timed in one process over
 // alternating rounds, on input sets rotated through more than twice the
 // 256 MB Infinity Cache: every dense kind and the sparse Big and Mid tiles run
@@ -588,24 +593,35 @@ template <bool NTS, bool ROT>
 using CfgT64 = Cfg<2, 2, 1, 1, 3, 8, NTS, ROT>;
 template <bool NTS, bool ROT>
 using CfgT64N = Cfg<2, 2, 1, 2, 3, 8, NTS, ROT>;
+template <bool NTS, bool ROT>
+using CfgT32 = Cfg<1, 1, 1, 1, 3, 8, NTS, ROT>;
 
-enum Shape { SHAPE_BIG, SHAPE_MID, SHAPE_SMALL, SHAPE_SMALL2, SHAPE_T64, SHAPE_T64N };
+enum Shape { SHAPE_BIG, SHAPE_MID, SHAPE_SMALL, SHAPE_SMALL2, SHAPE_T64, SHAPE_T64N, SHAPE_T32 };
 
 static long tiles(int M, int N, int bm, int bn) { return long((M + bm - 1) / bm) * long((N + bn - 1) / bn); }
 
 // tile rows x columns of a shape
 static void tile_dims(Shape sh, int &bm, int &bn) {
-    bm = sh == SHAPE_BIG ? 256 : (sh == SHAPE_T64 || sh == SHAPE_T64N) ? 64 : 128;
-    bn = (sh == SHAPE_BIG || sh == SHAPE_MID) ? 256 : sh == SHAPE_T64 ? 64 : 128;
+    bm = sh == SHAPE_BIG ? 256 : (sh == SHAPE_T64 || sh == SHAPE_T64N) ? 64 : sh == SHAPE_T32 ? 32 : 128;
+    bn = (sh == SHAPE_BIG || sh == SHAPE_MID) ? 256 : sh == SHAPE_T64 ? 64 : sh == SHAPE_T32 ? 32 : 128;
 }
 
 // few output tiles: at most `limit` tiles of 128 x 128 (128 = half the CUs)
 static bool few_tiles(int M, int N, long limit = 128) { return tiles(M, N, 128, 128) <= limit; }
 
+// The smallest GEMMs (at most 512 tiles of 32 x 32, fewer than 64 K stages):
+// one-wave 32 x 32 tiles.  Past 64 K stages such shapes split K on 64 x 64
+// tiles instead, which is faster there (fp16 2:4 512 x 4096 x 1024: 15.6 us
+// split vs 21.7 on 32 x 32).
+static bool tiny(int M, int N, int stages) { return stages < 64 && tiles(M, N, 32, 32) <= 512; }
+
 // f16 kinds: big tiles when they still give >= 3/4 of a tile per CU; 64-row
 // tiles for few-tile GEMMs.
-static Shape pick_f16(int M, int N) {
-    if (few_tiles(M, N)) return tiles(M, N, 64, 64) <= 256 ? SHAPE_T64 : SHAPE_T64N;
+static Shape pick_f16(int M, int N, int K) {
+    if (few_tiles(M, N)) {
+        if (tiny(M, N, K / 64)) return SHAPE_T32;
+        return tiles(M, N, 64, 64) <= 256 ? SHAPE_T64 : SHAPE_T64N;
+    }
     return tiles(M, N, 256, 256) >= 192 ? SHAPE_BIG : SHAPE_SMALL;
 }
 
@@ -621,7 +637,7 @@ static Shape pick_i8(int M, int N, int K, bool dense) {
     // (short K: up to 192 tiles; 1024 x 1024 x 3072 2:4 9.9 -> 9.1 us, dense
     // 9.9 -> 8.1; at 256 tiles within 5 %, and with K = 4096 at 192 tiles the
     // 128-row tiles stay ahead, 20.4 vs 24.7 us)
-    if (few_tiles(M, N, K <= 1024 ? 192 : 128)) return SHAPE_T64;
+    if (few_tiles(M, N, K <= 1024 ? 192 : 128)) return tiny(M, N, K / 128) ? SHAPE_T32 : SHAPE_T64;
     if (K <= 1024) {
         if (dense) {
             const long big = tiles(M, N, 256, 256);
@@ -643,6 +659,7 @@ static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const ui
     if (sh == SHAPE_MID) return launch<KIND, EPI, CfgMid<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     constexpr bool ROT = KindTraits<KIND>::kSparse;
     if (sh == SHAPE_T64) return launch<KIND, EPI, CfgT64<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
+    if (sh == SHAPE_T32) return launch<KIND, EPI, CfgT32<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     if constexpr (!KindTraits<KIND>::kI8)  // (only the fp16 kinds pick T64N)
         if (sh == SHAPE_T64N)
             return launch<KIND, EPI, CfgT64N<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
@@ -654,13 +671,13 @@ static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const ui
 }
 
 hipError_t launch_dense_f16(const void *A, const void *Wt, void *C, int M, int N, int K, hipStream_t st) {
-    return launch_shape<DENSE_F16, EPI_F16, true, true>(pick_f16(M, N), A, Wt, nullptr, nullptr, nullptr, C, M, N, K,
+    return launch_shape<DENSE_F16, EPI_F16, true, true>(pick_f16(M, N, K), A, Wt, nullptr, nullptr, nullptr, C, M, N, K,
                                                          st);
 }
 
 hipError_t launch_w24_f16(const void *A, const void *vals, const uint32_t *meta, void *C, int M, int N, int K,
                           hipStream_t st) {
-    return launch_shape<W24_F16, EPI_F16, true, false>(pick_f16(M, N), A, vals, meta, nullptr, nullptr, C, M, N, K,
+    return launch_shape<W24_F16, EPI_F16, true, false>(pick_f16(M, N, K), A, vals, meta, nullptr, nullptr, C, M, N, K,
                                                         st);
 }
 
@@ -706,10 +723,10 @@ hipError_t launch_gemm_partials(int kind, const void *A, const void *W, const ui
                                 int N, int K, int splits, hipStream_t st) {
     switch (kind) {
         case DENSE_F16:
-            return launch_shape<DENSE_F16, EPI_PART, false, true>(pick_f16(M, N), A, W, nullptr, nullptr, nullptr, ws,
+            return launch_shape<DENSE_F16, EPI_PART, false, true>(pick_f16(M, N, K), A, W, nullptr, nullptr, nullptr, ws,
                                                                    M, N, K, st, splits);
         case W24_F16:
-            return launch_shape<W24_F16, EPI_PART, false, false>(pick_f16(M, N), A, W, meta, nullptr, nullptr, ws, M,
+            return launch_shape<W24_F16, EPI_PART, false, false>(pick_f16(M, N, K), A, W, meta, nullptr, nullptr, ws, M,
                                                                   N, K, st, splits);
         case DENSE_I8:
             return launch_shape<DENSE_I8, EPI_PART, false, true>(pick_i8(M, N, K, true), A, W, nullptr, nullptr,
@@ -739,7 +756,7 @@ hipError_t launch_gemm_partials(int kind, const void *A, const void *W, const ui
 void tile_choice(int kind, int M, int N, int K, int *bm, int *bn) {
     const bool i8 = kind == DENSE_I8 || kind == W24_I8;
     const bool dense = kind == DENSE_F16 || kind == DENSE_I8;
-    tile_dims(i8 ? pick_i8(M, N, K, dense) : pick_f16(M, N), *bm, *bn);
+    tile_dims(i8 ? pick_i8(M, N, K, dense) : pick_f16(M, N, K), *bm, *bn);
 }
 
 int suggest_splits(int kind, int M, int N, int K) {
@@ -747,7 +764,7 @@ int suggest_splits(int kind, int M, int N, int K) {
     if (M <= 0 || N <= 0 || K <= 0) return 1;
     const bool i8 = kind == DENSE_I8 || kind == W24_I8;
     const bool dense = kind == DENSE_F16 || kind == DENSE_I8;
-    const Shape sh = i8 ? pick_i8(M, N, K, dense) : pick_f16(M, N);
+    const Shape sh = i8 ? pick_i8(M, N, K, dense) : pick_f16(M, N, K);
     int bm, bn;
     tile_dims(sh, bm, bn);
     const long t = tiles(M, N, bm, bn);

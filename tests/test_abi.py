@@ -201,9 +201,16 @@ def test_tile_choice_host_query(lib):
     assert lib.tile_choice(D8, 12608, 3072, 768) == (128, 128)
     # ViT-L fc1 (fp16): 256 x 256 tiles fill the chip
     assert lib.tile_choice(F16, 4096, 4096, 1024) == (256, 256)
-    # one GPU's share of ViT-L (M = 512): 64-row tiles
+    # one GPU's share of ViT-L (M = 512): proj on one-wave 32 x 32 tiles (512 of
+    # them, 16 / 8 K stages), the wider layers on 64-row tiles
     for kind in (F16, D16, I8, D8):
-        assert lib.tile_choice(kind, 512, 1024, 1024) == (64, 64)
+        assert lib.tile_choice(kind, 512, 1024, 1024) == (32, 32)
+        assert lib.tile_choice(kind, 520, 1024, 1024) == (64, 64)  # 544 tiles of 32 x 32
+    # 64 or more K stages: 64 x 64 tiles (and split K) instead of 32 x 32
+    assert lib.tile_choice(F16, 512, 1024, 4096) == (64, 64)
+    assert lib.tile_choice(F16, 512, 1024, 4032) == (32, 32)
+    assert lib.tile_choice(I8, 512, 1024, 4096) == (32, 32)  # 32 stages of 128
+    assert lib.tile_choice(I8, 512, 1024, 8192) == (64, 64)
     assert lib.tile_choice(F16, 512, 4096, 1024) == (64, 128)  # 64 x 64 tiles would number 512
     assert lib.tile_choice(I8, 512, 4096, 1024) == (64, 64)
     # 192 tiles of 128 x 128: int8 at short K takes 64 x 64, fp16 and long-K int8 do not

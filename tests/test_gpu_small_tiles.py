@@ -1,10 +1,11 @@
-"""The 64-row tiles (64 x 64 and 64 x 128) that GEMMs with few output tiles
-take, vs the oracle, through the C ABI.
+"""The small tiles (64 x 64, 64 x 128 and one-wave 32 x 32) that GEMMs with
+few output tiles take, vs the oracle, through the C ABI.
 
 Each case first asserts, through the library's host-side tile query, that
 its shape reaches the tile it is meant to cover, so that a change of the
 tile rules cannot leave a path untested.  Covered: the fp16 2:4 64 x 64 tile,
-where two waves load each meta chunk of a stage; 64 x 128 fp16 tiles; ragged
+where two waves load each meta chunk of a stage; 64 x 128 fp16 tiles; 32 x 32
+tiles; ragged
 token counts (M not a multiple of 64); every int8 output kind bit-exact; the
 dense kinds; and split K on 64 x 64 tiles.  Bars as in the other parity
 tests: int8 bit-exact, fp16 within the strict per-element bound and
@@ -38,10 +39,11 @@ def _check_f16(C, A, Wp, what):
 
 
 # (M, K, N, tile the fp16 kinds take)
-F16_CASES = [(200, 512, 256, (64, 64)),     # 4 x 4 tiles, last tile row 8 rows deep
+F16_CASES = [(600, 512, 1024, (64, 64)),    # 10 x 16 tiles, last tile row 24 rows deep
              (1000, 256, 2048, (64, 128)),  # 64 x 64 tiles would number 512
-             (64, 2048, 128, (64, 64)),     # one tile row, long K
-             (1, 128, 64, (64, 64))]        # a single token
+             (64, 4096, 128, (64, 64)),     # one tile row, 64 K stages
+             (200, 512, 256, (32, 32)),     # 7 x 8 tiles, last tile row 8 rows deep
+             (1, 128, 64, (32, 32))]        # a single token
 
 
 @pytest.mark.parametrize("M,K,N,tile", F16_CASES)
@@ -66,12 +68,12 @@ def test_w24_f16_small_tiles_exact(lib, gpu, M, K, N, tile):
 def test_w24_f16_64x64_one_hot(lib, gpu):
     """Each output column copies one activation column: a meta chunk loaded for
     the wrong channel rows, or missing from the stage, selects the wrong k."""
-    M, K, N = 96, 1024, 192
-    assert lib.tile_choice(lib.SSG_KIND_W24_F16, M, N, K) == (64, 64)
-    case = wl.one_hot_24(np.random.default_rng(11), M, K, N)
-    vals, meta = lib.w24_pack_f16(case["Wp"])
-    C = H(lib.w24_gemm_f16(T(case["A"]), T(vals), T(meta.view(np.int32)), splits=1))
-    assert np.array_equal(C.view(np.uint16), case["A"][:, case["k_of_n"]].view(np.uint16))
+    for M, K, N, tile in ((600, 512, 1024, (64, 64)), (96, 1024, 192, (32, 32))):
+        assert lib.tile_choice(lib.SSG_KIND_W24_F16, M, N, K) == tile
+        case = wl.one_hot_24(np.random.default_rng(11), M, K, N)
+        vals, meta = lib.w24_pack_f16(case["Wp"])
+        C = H(lib.w24_gemm_f16(T(case["A"]), T(vals), T(meta.view(np.int32)), splits=1))
+        assert np.array_equal(C.view(np.uint16), case["A"][:, case["k_of_n"]].view(np.uint16)), tile
 
 
 @pytest.mark.parametrize("M,K,N,tile", F16_CASES[:2])
@@ -83,9 +85,9 @@ def test_dense_f16_small_tiles(lib, gpu, M, K, N, tile):
 
 
 @pytest.mark.parametrize("out", ["i32", "f32", "f16", "i8"])
-@pytest.mark.parametrize("M,K,N", [(200, 1024, 320), (1000, 256, 2048)])
-def test_w24_i8_small_tiles_bit_exact(lib, gpu, out, M, K, N):
-    assert lib.tile_choice(lib.SSG_KIND_W24_I8, M, N, K) == (64, 64)
+@pytest.mark.parametrize("M,K,N,tile", [(200, 1024, 320, (32, 32)), (1000, 256, 2048, (64, 64))])
+def test_w24_i8_small_tiles_bit_exact(lib, gpu, out, M, K, N, tile):
+    assert lib.tile_choice(lib.SSG_KIND_W24_I8, M, N, K) == tile
     rng = np.random.default_rng(M + N)
     case = wl.random_24_i8(rng, M, K, N)
     bias = None if out == "i32" else rng.normal(0, 4, N).astype(np.float32)
@@ -99,9 +101,9 @@ def test_w24_i8_small_tiles_bit_exact(lib, gpu, out, M, K, N):
 
 
 @pytest.mark.parametrize("out", ["i32", "f32", "i8"])
-def test_dense_i8_small_tiles_bit_exact(lib, gpu, out):
-    M, K, N = 136, 768, 448
-    assert lib.tile_choice(lib.SSG_KIND_DENSE_I8, M, N, K) == (64, 64)
+@pytest.mark.parametrize("M,K,N,tile", [(136, 768, 448, (32, 32)), (600, 768, 1024, (64, 64))])
+def test_dense_i8_small_tiles_bit_exact(lib, gpu, out, M, K, N, tile):
+    assert lib.tile_choice(lib.SSG_KIND_DENSE_I8, M, N, K) == tile
     rng = np.random.default_rng(17)
     case = wl.random_24_i8(rng, M, K, N)
     scale = None if out == "i32" else case["scale"]
@@ -149,11 +151,19 @@ def test_split_k_on_64x64_tiles(lib, gpu):
 
 
 # Shapes on both sides of each tile-rule boundary: (kind, M, K, N, tile).
-F16_BOUNDARY = [(1024, 128, 1024, (64, 64)),     # 256 tiles of 64 x 64
+F16_BOUNDARY = [(512, 128, 1024, (32, 32)),      # 512 tiles of 32 x 32
+                (520, 128, 1024, (64, 64)),      # 544
+                (512, 4032, 1024, (32, 32)),     # 63 K stages
+                (512, 4096, 1024, (64, 64)),     # 64: split K on 64 x 64 instead
+                (1024, 128, 1024, (64, 64)),     # 256 tiles of 64 x 64
                 (1032, 128, 1024, (64, 128)),    # 272 would be too many
                 (1024, 128, 2048, (64, 128)),    # 128 tiles of 128 x 128
                 (1032, 128, 2048, (128, 128))]   # 144: not few any more
-I8_BOUNDARY = [(1536, 256, 2048, (64, 64)),      # short K: 192 tiles of 128 x 128
+I8_BOUNDARY = [(512, 128, 1024, (32, 32)),       # 512 tiles of 32 x 32
+               (520, 128, 1024, (64, 64)),       # 544
+               (128, 8064, 256, (32, 32)),       # 63 K stages
+               (128, 8192, 256, (64, 64)),       # 64
+               (1536, 256, 2048, (64, 64)),      # short K: 192 tiles of 128 x 128
                (1544, 256, 2048, (128, 128)),    # 208
                (1024, 1152, 2048, (64, 64)),     # long K: 128
                (1032, 1152, 2048, (128, 128))]   # 144

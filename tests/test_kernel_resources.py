@@ -10,7 +10,6 @@ SIMDs), and no kernel may spill to scratch.  A few extra registers in a
 kernel near a boundary halve its occupancy without any other symptom.
 """
 
-import math
 import os
 import re
 import shutil
@@ -76,9 +75,12 @@ def test_no_kernel_spills_to_scratch(kernels):
 def test_registers_never_limit_occupancy_below_lds(kernels):
     bad = {}
     for name, v in kernels.items():
-        waves_per_simd = math.ceil(v["wg"] // 64 / SIMDS_PER_CU)
+        waves = v["wg"] // 64
         alloc = -(-v["vgpr"] // VGPR_GRANULE) * VGPR_GRANULE
-        by_regs = (VGPRS_PER_SIMD_LANE // alloc) // waves_per_simd
+        # waves the register file holds per CU, in whole workgroups (a workgroup
+        # of 4 or more waves spreads over the 4 SIMDs; one-wave workgroups fill
+        # them one by one)
+        by_regs = SIMDS_PER_CU * (VGPRS_PER_SIMD_LANE // alloc) // waves
         by_lds = LDS_PER_CU // v["lds"] if v["lds"] else 8
         if by_regs < min(by_lds, 8):
             bad[name] = dict(v, workgroups_by_registers=by_regs, workgroups_by_lds=by_lds)
