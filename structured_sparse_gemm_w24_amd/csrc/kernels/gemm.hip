@@ -566,7 +566,7 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 //          outnumber the CUs (dense fp16 512 x 1024 x 3072: 10.1 us on
 //          64 x 128, 11.1 on 64 x 64); int8, with half as many K stages,
 //          takes 64 x 64 throughout;
-//   T32    32 x 32, one wave, 3 stages -- the smallest GEMMs (at most 512
+//   T32    32 x 32, one wave, 4 stages -- the smallest GEMMs (at most 512
 //          such tiles and fewer than 64 K stages): fp16 2:4 256 x 512 x 512
 //          5.2 -> 4.4 us, 384 x 1024 x 1024 7.3 -> 6.4; int8 2:4 128 x 4096
 //          x 4096 12.3 -> 10.5 (against 64-row tiles, same sweep); at 1024
@@ -578,7 +578,11 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 // 4096x2048x4096), while the sparse 128 x 128 tiles run 4-10 % faster rotated
 // (fp16 ViT-L fc2 42.1 vs 46.2 us, int8 4096x8192x1024 43.7 vs 47.7 us; the
 // short-K int8 one is within noise either way).  So ROT = sparse kind on a
-// 128 x 128 tile, and on the 64-row tiles below (not measured apart there).
+// 128 x 128 tile, and on the sparse 64 x 128 tile (fp16 2:4 512 x 1024 x 4096
+// 9.8 vs 10.2 us); the 64 x 64 and 32 x 32 tiles run faster from stage 0 (int8
+// 2:4 512 x 1024 x 3072 6.6 vs 6.9 us on 64 x 64; 32 x 32 with a 4-stage ring:
+// fp16 2:4 512 x 1024 x 1024 5.7 vs 6.5 us, int8 2:4 512 x 4096 x 1024 9.1 vs
+// 10.6 us against the rotated 3-stage form).
 template <bool NTS>
 using CfgBig = Cfg<4, 2, 2, 4, 3, 8, NTS, false>;
 template <bool NTS>
@@ -589,12 +593,12 @@ template <bool NTS, bool ROT>
 using CfgSmall = Cfg<2, 2, 2, 2, 3, 8, NTS, ROT>;
 template <bool NTS, bool ROT>
 using CfgSmall2 = Cfg<2, 2, 2, 2, 2, 8, NTS, ROT>;
-template <bool NTS, bool ROT>
-using CfgT64 = Cfg<2, 2, 1, 1, 3, 8, NTS, ROT>;
+template <bool NTS>
+using CfgT64 = Cfg<2, 2, 1, 1, 3, 8, NTS, false>;
 template <bool NTS, bool ROT>
 using CfgT64N = Cfg<2, 2, 1, 2, 3, 8, NTS, ROT>;
-template <bool NTS, bool ROT>
-using CfgT32 = Cfg<1, 1, 1, 1, 3, 8, NTS, ROT>;
+template <bool NTS>
+using CfgT32 = Cfg<1, 1, 1, 1, 4, 8, NTS, false>;
 
 enum Shape { SHAPE_BIG, SHAPE_MID, SHAPE_SMALL, SHAPE_SMALL2, SHAPE_T64, SHAPE_T64N, SHAPE_T32 };
 
@@ -658,8 +662,8 @@ static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const ui
     }
     if (sh == SHAPE_MID) return launch<KIND, EPI, CfgMid<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     constexpr bool ROT = KindTraits<KIND>::kSparse;
-    if (sh == SHAPE_T64) return launch<KIND, EPI, CfgT64<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
-    if (sh == SHAPE_T32) return launch<KIND, EPI, CfgT32<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
+    if (sh == SHAPE_T64) return launch<KIND, EPI, CfgT64<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
+    if (sh == SHAPE_T32) return launch<KIND, EPI, CfgT32<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     if constexpr (!KindTraits<KIND>::kI8)  // (only the fp16 kinds pick T64N)
         if (sh == SHAPE_T64N)
             return launch<KIND, EPI, CfgT64N<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
