@@ -41,8 +41,8 @@
 //     or y = float(acc) * scale[n] (+ bias[n]) written as fp32, as fp16
 //     rounded to nearest even, or as int8 rounded to nearest even and
 //     saturated to [-128, 127]);
-//   * a tile starts its K loop at stage 0 or, for the sparse tiles of 128 x 128
-//     and smaller, at a stage rotated by its tile id (measured per tile
+//   * a tile starts its K loop at stage 0 or, for the sparse 128 x 128 and
+//     64 x 128 tiles, at a stage rotated by its tile id (measured per tile
 //     shape, see ROT);
 //   * split K (gridDim.y > 1, EPI_PART): workgroup (tile, y) runs K-stage range
 //     y and writes its raw accumulators to slice y of a workspace, which
@@ -554,8 +554,8 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 //          twice or less than once, and the dense int8 GEMMs at short K;
 //   T64    64 x 64 and T64N 64 x 128, 4 waves of 32 x 32 / 32 x 64, 3 stages
 //          -- GEMMs with at most 128 tiles of 128 x 128 (half the CUs; int8
-//          with K <= 1024: 192), e.g.
-//          one GPU's share of a token-sharded layer (M = 512).  With so few
+//          with K <= 1024: 192), e.g. one GPU's share of a token-sharded
+//          layer (M = 512).  With so few
 //          tiles each workgroup's K loop runs alone on its CU, limited by
 //          what its four waves can pull into LDS per stage; smaller tiles
 //          put more CUs to work and each moves less (int8 2:4 512 x 1024 x
@@ -567,10 +567,12 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 //          64 x 128, 11.1 on 64 x 64); int8, with half as many K stages,
 //          takes 64 x 64 throughout;
 //   T32    32 x 32, one wave, 4 stages -- the smallest GEMMs (at most 512
-//          such tiles and fewer than 64 K stages): fp16 2:4 256 x 512 x 512
-//          5.2 -> 4.4 us, 384 x 1024 x 1024 7.3 -> 6.4; int8 2:4 128 x 4096
-//          x 4096 12.3 -> 10.5 (against 64-row tiles, same sweep); at 1024
-//          tiles (1024 x 1024 outputs) the 64-row tiles are ahead again.
+//          such tiles and fewer than 64 K stages).  Against 64-row tiles in
+//          one sweep (its first, 3-stage rotated form): fp16 2:4 256 x 512 x
+//          512 5.2 -> 4.4 us, 384 x 1024 x 1024 7.3 -> 6.4; int8 2:4 128 x
+//          4096 x 4096 12.3 -> 10.5; at 1024 tiles (1024 x 1024 outputs) the
+//          64-row tiles are ahead again.  The 4-stage ring from stage 0
+//          (ROT below) took 256 x 512 x 512 to 3.8 us.
 // K-loop start (ROT), measured with both variants timed in one process over
 // alternating rounds, on input sets rotated through more than twice the
 // 256 MB Infinity Cache: every dense kind and the sparse Big and Mid tiles run
@@ -741,6 +743,13 @@ hipError_t launch_gemm_partials(int kind, const void *A, const void *W, const ui
     }
 }
 
+// Tile rows x columns the launchers pick for a kind and shape.
+void tile_choice(int kind, int M, int N, int K, int *bm, int *bn) {
+    const bool i8 = kind == DENSE_I8 || kind == W24_I8;
+    const bool dense = kind == DENSE_F16 || kind == DENSE_I8;
+    tile_dims(i8 ? pick_i8(M, N, K, dense) : pick_f16(M, N, K), *bm, *bn);
+}
+
 // Splitting K pays when a GEMM has few output tiles and a long K loop (one
 // GPU's share of a token-sharded layer, e.g. 512 x 4096 x 1024): each tile's
 // K loop is a chain of dependent stage loads, and cutting it into ranges run
@@ -756,13 +765,6 @@ hipError_t launch_gemm_partials(int kind, const void *A, const void *W, const ui
 // 21.9 -> 26.5 us).  Within those bounds the splits double while tiles x
 // splits stays within one workgroup per CU and every split keeps at least 8
 // stages.
-// Tile rows x columns the launchers pick for a kind and shape.
-void tile_choice(int kind, int M, int N, int K, int *bm, int *bn) {
-    const bool i8 = kind == DENSE_I8 || kind == W24_I8;
-    const bool dense = kind == DENSE_F16 || kind == DENSE_I8;
-    tile_dims(i8 ? pick_i8(M, N, K, dense) : pick_f16(M, N, K), *bm, *bn);
-}
-
 int suggest_splits(int kind, int M, int N, int K) {
     constexpr int kCUs = 256;
     if (M <= 0 || N <= 0 || K <= 0) return 1;
