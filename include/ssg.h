@@ -242,9 +242,14 @@ int64_t ssg_splitk_workspace_bytes(int64_t M, int64_t N, int32_t splits);
 /* The split count the library would take for a kind and shape (measured on
  * MI355X): 1 (do not split) when K has fewer than 64 stages (64 K elements
  * per stage for the fp16 kinds, 128 for int8) or the output tiles of the
- * library's tile choice number more than 128; otherwise the largest power of
- * two <= 16 with tiles x splits <= 256 (one workgroup per CU) and at least 8
- * K stages per split.  Host-only; an invalid kind or shape gives 1. */
+ * library's tile choice number more than 128.  Otherwise, for the fp16
+ * kinds, 8 when 128 x 128 tiles x 8 splits reach 256 workgroups (M >= 128,
+ * >= 8 stages per split), else 4 when 64 x 128 tiles x 4 do; failing both,
+ * and for the int8 kinds, the largest power of two <= 16 with tiles x splits
+ * <= 256 (one workgroup per CU) and at least 8 K stages per split.  A split
+ * launch of the fp16 kinds uses those bigger tiles when called with that
+ * split count (8 or 4) and the same conditions hold, otherwise the unsplit
+ * call's tile.  Host-only; an invalid kind or shape gives 1. */
 int32_t ssg_splitk_suggest(int32_t kind, int64_t M, int64_t N, int64_t K);
 
 /* The output tile the GEMM calls of a kind use for a shape (measured choice,

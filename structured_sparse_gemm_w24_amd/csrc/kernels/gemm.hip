@@ -730,15 +730,31 @@ namespace ssg {
 // ---- split K.  The partial launches run the tile choice of the unsplit
 // kinds with gridDim.y = splits and the EPI_PART epilogue (plain stores: the
 // reduce launch reads the partials back right away).
+// The tile of a split launch of the fp16 kinds.  Split launches read each
+// weight once per tile row, cold from HBM, so where the split reaches one
+// workgroup per CU with bigger tiles, those win (graph-timed, a fresh weight
+// per call): fp16 2:4 512 x 4096 x 1024 16.9 us as 128 x 128 x 8 splits, 16.3
+// as 64 x 128 x 4, 18.4 as 64 x 64 x 2; 512 x 8192 x 1024 21.9 / 23.2 / 30.6.
+// A function of the shape and the split count alone, so an explicit split
+// count gets a fixed tile too.
+static Shape split_shape_f16(int M, int N, int K, int splits) {
+    const Shape sh = pick_f16(M, N, K);
+    if (sh != SHAPE_T64 && sh != SHAPE_T64N && sh != SHAPE_T32) return sh;
+    const int S = K / 64;
+    if (splits == 8 && M >= 128 && tiles(M, N, 128, 128) * 8 >= 256 && S / 8 >= 8) return SHAPE_SMALL;
+    if (splits == 4 && tiles(M, N, 64, 128) * 4 >= 256 && S / 4 >= 8) return SHAPE_T64N;
+    return sh;
+}
+
 hipError_t launch_gemm_partials(int kind, const void *A, const void *W, const uint32_t *meta, void *ws, int M,
                                 int N, int K, int splits, hipStream_t st) {
     switch (kind) {
         case DENSE_F16:
-            return launch_shape<DENSE_F16, EPI_PART, false, true>(pick_f16(M, N, K), A, W, nullptr, nullptr, nullptr, ws,
-                                                                   M, N, K, st, splits);
+            return launch_shape<DENSE_F16, EPI_PART, false, true>(split_shape_f16(M, N, K, splits), A, W, nullptr,
+                                                                   nullptr, nullptr, ws, M, N, K, st, splits);
         case W24_F16:
-            return launch_shape<W24_F16, EPI_PART, false, false>(pick_f16(M, N, K), A, W, meta, nullptr, nullptr, ws, M,
-                                                                  N, K, st, splits);
+            return launch_shape<W24_F16, EPI_PART, false, false>(split_shape_f16(M, N, K, splits), A, W, meta, nullptr,
+                                                                  nullptr, ws, M, N, K, st, splits);
         case DENSE_I8:
             return launch_shape<DENSE_I8, EPI_PART, false, true>(pick_i8(M, N, K, true), A, W, nullptr, nullptr,
                                                                   nullptr, ws, M, N, K, st, splits);
@@ -781,6 +797,10 @@ int suggest_splits(int kind, int M, int N, int K) {
     const long t = tiles(M, N, bm, bn);
     const int S = gemm_k_stages(kind, K);
     if (S < 64 || t > 128) return 1;
+    if (!i8) {  // bigger tiles with more splits first (see split_shape_f16)
+        for (int q : {8, 4})
+            if (S % q == 0 && split_shape_f16(M, N, K, q) != sh) return q;
+    }
     int p = 1;
     while (p < 16 && t * 2 * p <= kCUs && S % (2 * p) == 0 && S / (2 * p) >= 8) p *= 2;
     return p;

@@ -172,13 +172,16 @@ def test_splitk_host_helpers(lib):
     assert raw.ssg_splitk_workspace_bytes(512, 1024, 8) == 8 * 512 * 1024 * 4
     assert raw.ssg_splitk_workspace_bytes(512, 1024, 1) == 0
     assert raw.ssg_splitk_workspace_bytes(-1, 1024, 8) == 0
-    # one GPU's share of ViT-L fc2 (M = 512): 128 tiles of 64 x 64 on 256 CUs;
-    # fp16 has 64 K stages -> split, int8 32 -> none; int8 at K = 8192 -> split
-    assert lib.splitk_suggest(lib.SSG_KIND_W24_F16, 512, 1024, 4096) == 2
+    # one GPU's share of ViT-L fc2 (M = 512): fp16 has 64 K stages -> split, on
+    # 128 x 128 tiles x 8 (256 workgroups); int8 32 -> none; int8 at K = 8192 -> split
+    assert lib.splitk_suggest(lib.SSG_KIND_W24_F16, 512, 1024, 4096) == 8
     assert lib.splitk_suggest(lib.SSG_KIND_W24_I8, 512, 1024, 4096) == 1
     assert lib.splitk_suggest(lib.SSG_KIND_W24_I8, 512, 1024, 8192) == 2
-    # 64 x 64 tiles for 128 x 4096 -> 2 x 64 = 128 tiles, 64 stages -> 2 splits
-    assert lib.splitk_suggest(lib.SSG_KIND_W24_F16, 128, 4096, 4096) == 2
+    # 128 x 4096 output: 32 tiles of 128 x 128 x 8 splits
+    assert lib.splitk_suggest(lib.SSG_KIND_W24_F16, 128, 4096, 4096) == 8
+    # 256 x 1024: 128 x 128 x 8 and 64 x 128 x 4 stay under 256 workgroups ->
+    # 64 x 64 tiles (64 of them) x 4
+    assert lib.splitk_suggest(lib.SSG_KIND_W24_F16, 256, 1024, 4096) == 4
     # more than 128 tiles -> no split (1024 x 1024 output: 256 tiles of 64 x 64)
     assert lib.splitk_suggest(lib.SSG_KIND_W24_F16, 1024, 1024, 4096) == 1
     # the ViT-Base fc1 shape fills the chip several times over -> no split

@@ -147,3 +147,16 @@ def test_splitk_workspace_reused_across_calls(lib, gpu):
                                            out_type="f32", splits=8, workspace=ws))
     for c, o in zip(cases, outs):
         assert np.array_equal(H(o).view(np.uint32), oracle.ref_gemm_i8(c["A"], c["Wp"], c["scale"]).view(np.uint32))
+
+
+@pytest.mark.parametrize("splits", [2, 4, 8])
+def test_f16_split_tiles_of_a_shard(lib, gpu, splits):
+    """One GPU's share of ViT-L fc2 (512 x 4096 x 1024) with each split count:
+    the split launch takes 64 x 64 (2), 64 x 128 (4) or 128 x 128 (8) tiles;
+    2:4 and dense fp16 within the bound."""
+    case = wl.random_24_f16(np.random.default_rng(60 + splits), 512, 4096, 1024)
+    vals, meta = lib.w24_pack_f16(case["Wp"])
+    C = H(lib.w24_gemm_f16_splitk(T(case["A"]), T(vals), T(meta.view(np.int32)), splits))
+    _check_f16(C, case["A"], case["Wp"], f"w24 f16 shard fc2 splits={splits}")
+    C = H(lib.dense_gemm_f16_splitk(T(case["A"]), T(case["W"].T), splits))
+    _check_f16(C, case["A"], case["W"], f"dense f16 shard fc2 splits={splits}")
