@@ -34,7 +34,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "effective TFLOPS/TOPS of sparse GEMM + speedup vs dense MFMA GEMM, same shape"
-HEADLINE_REPLAYS = 5  # graph replays of the K timed steps; the median is reported
+# Headline timing: after the W eager warm-up steps, the sparse and the dense
+# graphs (K launches each) replay alternately for HEADLINE_WARM_S seconds so
+# the power-managed shader clock settles at its sustained value, then
+# HEADLINE_ROUNDS rounds each time one sparse replay and one dense replay
+# (every replay a timed region of exactly K steps); medians are reported.
+HEADLINE_ROUNDS = 25
+HEADLINE_WARM_S = 1.5
 CACHE_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w24_gemm_i8_vit_base_fc1.txt")
 
@@ -228,6 +234,71 @@ def observed_sclk(torch, fn, steps, warm_s=2.0, max_s=15.0):
             "source": f"amd-smi metric -c -u, read after {warm_s:g} s of the timed graph replaying back to back"}
 
 
+def paired_replays(torch, fns, steps, warmup, warm_s, rounds):
+    """Times several step functions against each other under the same clock.
+
+    Each fn gets `warmup` eager calls, then one HIP graph of `steps` calls;
+    the graphs replay round-robin for warm_s seconds (untimed: the shader
+    clock is power-managed and drops from its idle value during the first
+    milliseconds of sustained load), then `rounds` timed rounds replay every
+    graph once, in order, with HIP events on the replaying stream around each
+    replay.  Returns per fn the median, p10 and p90 ms per step over the
+    rounds.  Alternating the kernels gives each the same clock history, so
+    their ratio does not depend on which was timed first."""
+    for i in range(warmup):
+        for fn in fns:
+            fn(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graphs = []
+    for fn in fns:
+        stream.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(steps):
+                    fn(i)
+        torch.cuda.current_stream().wait_stream(stream)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    warm_replays = 0
+    while time.perf_counter() - t0 < warm_s:
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        warm_replays += 1
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in graphs]
+    times = [[] for _ in graphs]
+    for _ in range(rounds):
+        for j, g in enumerate(graphs):
+            s, e = ev[j]
+            s.record()
+            g.replay()
+            e.record()
+            torch.cuda.synchronize()
+            times[j].append(s.elapsed_time(e) / steps)
+    del graphs
+    out = []
+    for t in times:
+        t = np.array(t)
+        out.append(dict(ms=float(np.median(t)), p10=float(np.percentile(t, 10)), p90=float(np.percentile(t, 90)),
+                        rounds=rounds, warm_replays=warm_replays))
+    return out
+
+
+def host_cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo, as lscpu reports it)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def host_time_ms(fn, reps=3):
     """Median wall time of a host call (the pack stage runs offline, outside the
     timed GPU region; it is reported beside it)."""
@@ -339,7 +410,9 @@ def vendor_w24_time(torch, kind, Wp, sets, M, N, K, C_ours, steps, warmup, timer
 
 
 # ---------------------------------------------------------------- workloads
-def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, with_f16_dense=False):
+def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, with_f16_dense=False, paired=None):
+    """2:4 and dense int8 GEMMs at c's shape.  paired = (warm_s, rounds): time
+    both with paired_replays (the headline) instead of the table timer."""
     dev = torch.device("cuda")
     M, K, N = c["M"], c["K"], c["N"]
     t_pack, (vals, meta) = host_time_ms(lambda: ssg.w24_pack_i8(c["Wp"]))
@@ -357,10 +430,17 @@ def w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, with_f16
                                    sets[i % R]["scale"], out=sets[i % R]["C"])
     de = lambda i: ssg.dense_gemm_i8(sets[i % R]["A"], sets[i % R]["Wt"], sets[i % R]["scale"],
                                      out=sets[i % R]["C"])
-    st = timer.stats(sp, steps, warmup)
-    t_de = timer(de, steps, warmup)
+    if paired is not None:
+        st, sd = paired_replays(torch, [sp, de], steps, warmup, *paired)
+        t_de = sd["ms"]
+        extra = dict(t_dense_p10_ms=sd["p10"], t_dense_p90_ms=sd["p90"], rounds=st["rounds"],
+                     warm_replays=st["warm_replays"])
+    else:
+        st = timer.stats(sp, steps, warmup)
+        t_de = timer(de, steps, warmup)
+        extra = {}
     out = dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"], t_dense_ms=t_de,
-               rotate_sets=R, t_pack_host_ms=t_pack, sets=sets,
+               rotate_sets=R, t_pack_host_ms=t_pack, sets=sets, sp=sp, **extra,
                k_splits=ssg.splitk_suggest(ssg.SSG_KIND_W24_I8, M, N, K),
                k_splits_dense=ssg.splitk_suggest(ssg.SSG_KIND_DENSE_I8, M, N, K))
     if with_f16_dense:
@@ -517,7 +597,8 @@ def cpu_baseline(c, perf, budget_s=12.0, one_core_rows=1024, gpu_out=None):
     nz, _ = perf.w24_ops(c["M"], c["N"], c["K"])
     out = {"value": nz * reps / el / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
            "sample": f"full {c['M']}x{c['K']}x{c['N']} int8 GEMM + epilogue (numpy float64 BLAS), "
-                     f"{reps} repetition(s), {el:.1f} s; host {platform.processor() or platform.machine()}"}
+                     f"{reps} repetition(s), {el:.1f} s; host CPU {host_cpu_model()}, {os.cpu_count()} "
+                     f"logical CPUs visible"}
     if gpu_out is not None:
         diff = np.abs(gpu_out.astype(np.float64) - ref.astype(np.float64))
         out["parity"] = {"what": "output of a timed launch vs the oracle's first repetition, every element",
@@ -597,14 +678,12 @@ def main(argv=None):
     c = wl.make_vit_base_fc1_i8()
     M, K, N = c["M"], c["K"], c["N"]
     log(f"workload vit_base_mlp_fc1 2:4 int8 {M}x{K}x{N}, steps {a.steps}, warmup {a.warmup}")
-    # the graph of K steps is replayed HEADLINE_REPLAYS times (each replay a
-    # timed region of exactly K steps); ms_per_step is the median replay
-    timer.reps = HEADLINE_REPLAYS
-    r = w24_i8_case(torch, ssg, perf, c, a.steps, a.warmup, timer, rotate=not a.warm)
-    step = lambda i: ssg.w24_gemm_i8(r["sets"][i % r["rotate_sets"]]["A"], r["sets"][i % r["rotate_sets"]]["vals"],
-                                     r["sets"][i % r["rotate_sets"]]["meta"], r["sets"][i % r["rotate_sets"]]["scale"],
-                                     out=r["sets"][i % r["rotate_sets"]]["C"])
-    t_eager = Timer(torch, graph=False, reps=HEADLINE_REPLAYS)(step, a.steps, a.warmup)
+    r = w24_i8_case(torch, ssg, perf, c, a.steps, a.warmup, timer, rotate=not a.warm,
+                    paired=(HEADLINE_WARM_S, HEADLINE_ROUNDS))
+    log(f"sparse {r['t_sparse_ms'] * 1e3:.1f} us/step (p10 {r['t_sparse_p10_ms'] * 1e3:.1f}, "
+        f"p90 {r['t_sparse_p90_ms'] * 1e3:.1f}), dense {r['t_dense_ms'] * 1e3:.1f} us/step")
+    step = r["sp"]
+    t_eager = Timer(torch, graph=False, reps=5)(step, a.steps, a.warmup)
     sclk = observed_sclk(torch, step, a.steps) if not (a.eager or a.no_sclk) else None
     nz, de = perf.w24_ops(M, N, K)
     t = r["t_sparse_ms"] / 1e3
@@ -633,11 +712,16 @@ def main(argv=None):
         "speedup_vs_dense": perf.speedup(r["t_dense_ms"], r["t_sparse_ms"]),
         "dense_i8_ms": r["t_dense_ms"],
         "pack_host_ms": r["t_pack_host_ms"],
-        "timing": f"HIP graph of the {a.steps} timed steps replayed on one stream, HIP events around each replay; "
-                  f"median of {HEADLINE_REPLAYS} replays (p10 / p90 beside)",
-        "replays": HEADLINE_REPLAYS,
+        "timing": f"{a.warmup} eager warm-up steps per kernel; HIP graphs of the {a.steps} steps of the sparse "
+                  f"and of the dense kernel replayed alternately for {HEADLINE_WARM_S:g} s (untimed, "
+                  f"{r['warm_replays']} pairs) so the power-managed clock settles; then {r['rounds']} rounds "
+                  f"of one sparse and one dense replay, HIP events on the replay stream around each "
+                  f"replay; ms_per_step = median sparse replay / {a.steps} (p10 / p90 beside)",
+        "rounds": r["rounds"],
         "ms_per_step_p10": r["t_sparse_p10_ms"],
         "ms_per_step_p90": r["t_sparse_p90_ms"],
+        "dense_i8_ms_p10": r["t_dense_p10_ms"],
+        "dense_i8_ms_p90": r["t_dense_p90_ms"],
         "eager_ms_per_step": t_eager,
         "sclk": sclk,
         "roofline": perf.roofline(achieved, perf.PEAK_HBM_GBS, "GB/s", "hbm", traffic),
@@ -834,14 +918,29 @@ def vit_large_stack(torch, ssg, perf, wl, dtype, timer, steps_gemm=20, passes=3,
                 by_shape=by_shape)
 
 
+def critical_density(sweep):
+    """Density at which a pattern's kernel matches the dense kernel: linear
+    interpolation between the two measured densities where the speedup
+    crosses 1 (sweep: (density, speedup) ascending in density), or None."""
+    crit = None
+    for (d0, s0), (d1, s1) in zip(sweep, sweep[1:]):
+        if s0 >= 1.0 > s1:
+            crit = d0 + (s0 - 1.0) * (d1 - d0) / (s0 - s1)
+    return crit
+
+
 def patterns(torch, ssg, perf, wl, timer, steps, warmup, emit):
-    """The pages' pattern comparison at the BERT-base FFN shape (M, K, N) =
-    (4096, 768, 3072), fp16, one input set (cache-warm): dense; 2:4; tile-wise
-    (G = 128) over a density sweep, with the critical density where it matches
-    dense; block-wise 64 x 64 (run by the tile-wise kernel with G = 64, since
-    a BW weight is a tile-wise weight of whole 64-row runs); element-wise
-    (unstructured) through torch's CSR sparse product in fp32, as the slides'
-    cuSparse baseline ran in fp32."""
+    """The pages' pattern comparison and critical-sparsity study (tile-wise
+    slides: pattern-comparison and critical-sparsity tables) at the BERT-base
+    FFN shape (M, K, N) = (4096, 768, 3072), fp16, one input set (cache-warm):
+    dense; 2:4; tile-wise with G = 128 and G = 64 and block-wise with 64 x 64
+    and 32 x 32 blocks (both run by the tile-wise kernel: a BW weight is a
+    tile-wise weight, G = b, of whole b-row runs), each over a density sweep
+    with the density where it matches dense; element-wise (unstructured)
+    through torch's CSR sparse product in fp32, as the slides' cuSparse
+    baseline ran in fp32.  Every pattern's first result is checked against
+    the dense kernel on the same pruned weight (a tested kernel of this
+    library) before it is timed."""
     rng = np.random.default_rng(0)
     M, K, N = 4096, 768, 3072
     A = wl.f16_normal(rng, (M, K))
@@ -853,41 +952,70 @@ def patterns(torch, ssg, perf, wl, timer, steps, warmup, emit):
     Wt = torch.from_numpy(np.ascontiguousarray(W.T)).to(dev)
     t_dense = timer(lambda i: ssg.dense_gemm_f16(A_d, Wt, out=C), steps, warmup)
     base = dict(shape=[M, K, N], t_dense_ms=t_dense, inputs="one set (cache-warm)")
-    vals, meta = ssg.w24_pack_f16(wl.prune24_magnitude(W))
+
+    def dense_ref(Wp):
+        """The dense kernel on the pruned weight, in float32."""
+        Wpt = torch.from_numpy(np.ascontiguousarray(Wp.T)).to(dev)
+        return ssg.dense_gemm_f16(A_d, Wpt).float()
+
+    def rel_err(got, ref):
+        return float((got.float() - ref).abs().max() / ref.abs().max().clamp_min(1e-30))
+
+    Wp24 = wl.prune24_magnitude(W)
+    vals, meta = ssg.w24_pack_f16(Wp24)
     v_d, m_d = torch.from_numpy(vals).to(dev), torch.from_numpy(meta.view(np.int32)).to(dev)
+    err = rel_err(ssg.w24_gemm_f16(A_d, v_d, m_d), dense_ref(Wp24))
     t = timer(lambda i: ssg.w24_gemm_f16(A_d, v_d, m_d, out=C), steps, warmup)
-    emit(dict(workload="patterns_2to4", density=0.5, t_ms=t, speedup_vs_dense=t_dense / t, **base))
-    sweep = []
-    for d in (0.1, 0.2, 0.3, 0.4, 0.5, 0.6, 0.7, 0.8, 0.9):
-        pk = ssg.tw_pack_f16(wl.prune_tilewise(W, 128, d), 128).to(dev)
-        t = timer(lambda i: ssg.tw_gemm_f16(At, pk, out=C), steps, warmup)
-        sweep.append((d, t_dense / t))
-        emit(dict(workload="patterns_tilewise_g128", density=d, t_ms=t, speedup_vs_dense=t_dense / t, **base))
-    crit = None
-    for (d0, s0), (d1, s1) in zip(sweep, sweep[1:]):
-        if s0 >= 1.0 > s1:
-            crit = d0 + (s0 - 1.0) * (d1 - d0) / (s0 - s1)
-    emit(dict(workload="patterns_tilewise_critical_density", critical_density=crit,
-              note="density at which the tile-wise kernel matches the dense kernel (linear interpolation)",
+    emit(dict(workload="patterns_2to4", density=0.5, t_ms=t, speedup_vs_dense=t_dense / t, check_rel_err=err,
               **base))
-    for d in (0.25, 0.5, 0.75):
-        pk = ssg.tw_pack_f16(wl.prune_blockwise(W, 64, d), 64).to(dev)
-        t = timer(lambda i: ssg.tw_gemm_f16(At, pk, out=C), steps, warmup)
-        emit(dict(workload="patterns_blockwise_64x64", density=d, t_ms=t, speedup_vs_dense=t_dense / t, **base))
+    fams = [("tilewise_g128", 128, lambda d: wl.prune_tilewise(W, 128, d), [0.1 * i for i in range(1, 10)]),
+            ("tilewise_g64", 64, lambda d: wl.prune_tilewise(W, 64, d), [0.1 * i for i in range(1, 10)]),
+            ("blockwise_64x64", 64, lambda d: wl.prune_blockwise(W, 64, d), [i / 12 for i in range(1, 12)]),
+            ("blockwise_32x32", 32, lambda d: wl.prune_blockwise(W, 32, d), [i / 12 for i in range(1, 12)])]
+    for name, G, prune, dens in fams:
+        sweep = []
+        for d in dens:
+            Wp = prune(d)
+            pk = ssg.tw_pack_f16(Wp, G).to(dev)
+            err = rel_err(ssg.tw_gemm_f16(At, pk), dense_ref(Wp))
+            if not err <= 1e-2:
+                raise RuntimeError(f"{name} d={d}: result differs from the dense kernel (rel err {err:.3g})")
+            t = timer(lambda i: ssg.tw_gemm_f16(At, pk, out=C), steps, warmup)
+            dens_eff = float(np.count_nonzero(Wp)) / Wp.size
+            sweep.append((dens_eff, t_dense / t))
+            emit(dict(workload=f"patterns_{name}", density=d, density_nonzero=dens_eff, t_ms=t,
+                      speedup_vs_dense=t_dense / t, check_rel_err=err, **base))
+        crit = critical_density(sweep)
+        emit(dict(workload=f"patterns_{name}_critical", critical_density=crit,
+                  critical_sparsity=None if crit is None else 1.0 - crit,
+                  note="nonzero density at which the pattern's kernel matches the dense kernel (linear "
+                       "interpolation over the sweep)", **base))
     A32 = A_d.float()
-    W32 = torch.from_numpy(W.astype(np.float32)).to(dev)
     At32 = A32.t().contiguous()
+    W32 = torch.from_numpy(W.astype(np.float32)).to(dev)
     t_dense32 = Timer(torch, graph=False)(lambda i: torch.matmul(A32, W32), steps, warmup)
-    for d in (0.37, 0.5):
+    sweep = []
+    for d in (0.01, 0.05, 0.2, 0.37, 0.5):
         Wp = wl.prune_elementwise(W, d)
         S = torch.from_numpy(np.ascontiguousarray(Wp.T.astype(np.float32))).to(dev).to_sparse_csr()
         try:
+            got = torch.sparse.mm(S, At32).t()
+            err = rel_err(got, dense_ref(Wp))
+            if not err <= 1e-2:
+                raise RuntimeError(f"element-wise d={d}: CSR result differs from the dense kernel "
+                                   f"(rel err {err:.3g})")
             t = Timer(torch, graph=False)(lambda i: torch.sparse.mm(S, At32), steps, warmup)
-            emit(dict(workload="patterns_elementwise_csr_fp32", density=d, t_ms=t,
+            sweep.append((d, t_dense / t))
+            emit(dict(workload="patterns_elementwise_csr_fp32", density=d, t_ms=t, check_rel_err=err,
                       speedup_vs_dense=t_dense / t, speedup_vs_dense_fp32=t_dense32 / t, t_dense_fp32_ms=t_dense32,
                       timing="eager (library call)", **base))
         except (RuntimeError, NotImplementedError) as e:
             emit(dict(workload="patterns_elementwise_csr_fp32", density=d, error=str(e)[:200], **base))
+    crit = critical_density(sweep)
+    emit(dict(workload="patterns_elementwise_csr_fp32_critical", critical_density=crit,
+              critical_sparsity=None if crit is None else 1.0 - crit,
+              note="None: slower than the dense kernel at every density measured" if crit is None else "",
+              **base))
 
 
 WORKLOADS = ("small", "vit_base_fc1", "bert_base_fc1", "bert_large_ffn", "vit_large", "vit_large_stack",
@@ -920,7 +1048,7 @@ def table(a, torch, ssg, perf, wl, timer):
     if "vit_base_fc1" in want:
         c = wl.make_vit_base_fc1_i8()
         r = w24_i8_case(torch, ssg, perf, c, steps, warmup, timer, rotate, with_f16_dense=True)
-        r.pop("sets")
+        r.pop("sets"), r.pop("sp")
         nz, de = perf.w24_ops(c["M"], c["N"], c["K"])
         b = perf.w24_bytes(c["M"], c["N"], c["K"], 1, 1, 4, True)
         emit(dict(workload=c["name"] + "_w24_i8", shape=[c["M"], c["K"], c["N"]], **r,
@@ -994,7 +1122,7 @@ def table(a, torch, ssg, perf, wl, timer):
             torch.cuda.empty_cache()
         for g in wl.vit_large_layers("i8", layers=1, M=M8):
             r = w24_i8_case(torch, ssg, perf, g, steps, warmup, timer, rotate)
-            r.pop("sets")
+            r.pop("sets"), r.pop("sp")
             nz, de = perf.w24_ops(g["M"], g["N"], g["K"])
             b = perf.w24_bytes(g["M"], g["N"], g["K"], 1, 1, 4, True)
             emit(dict(workload=g["name"].replace("vit_large_", "vit_large_shard8_") + "_w24_i8",

@@ -13,8 +13,14 @@ some order; the fp32 sum is rounded once to fp16):
 with u16 = 2^-11 (fp16 unit roundoff), eta16 = 2^-25 (half the fp16
 subnormal spacing), u32 = 2^-24 and S = |A| . |W_p|.  The factor 2 * n * u32
 bounds the error of n fp32 additions in any order even if the matrix unit
-does not round to nearest at every step.  It catches a single dropped or
-duplicated term, which the loose bound can hide.
+does not round to nearest at every step; n is the number of products one
+output sums (K for a dense GEMM, K/2 kept slots for 2:4, K_t of the output's
+tile for tile-wise).  Since S is n times the average |a w| of the sum, the
+bound catches a dropped or duplicated term larger than 2 n^2 u32 average
+terms plus the output rounding: 0.018 of an average term at n = 384 (which
+the loose bound can hide), half of one at n = 2048.  Smaller single terms can
+sit inside a valid summation error, which is why exact-integer cases
+(bit-exact whatever the summation order) pin the index paths.
 """
 
 from __future__ import annotations

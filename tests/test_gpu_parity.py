@@ -45,7 +45,15 @@ def run_w24_i8(lib, A, Wp, scale):
     return H(lib.w24_gemm_i8(T(A), T(vals), meta_t(meta), None if scale is None else T(scale)))
 
 
+def tw_terms(Wp, G):
+    """Products each output column sums in the tile-wise kernel: K_t of its
+    tile (the kernel walks only the tile's kept rows), one entry per column."""
+    packed = oracle.ref_tw_pack(Wp, G)
+    return np.repeat(np.maximum(np.diff(packed["k_ptr"]), 1), G).astype(np.float64)
+
+
 def check_f16(C, A, Wp, n_terms, what=""):
+    """n_terms: products summed per output (a number, or one per column)."""
     C_ref, _ = oracle.ref_gemm_f16(A, Wp)
     S = oracle.ref_abs_gemm(A, Wp)
     err = oracle.loose_err(C, C_ref)
@@ -201,6 +209,27 @@ def test_dense_f16(lib, gpu, M, K, N):
     check_f16_exact(H(lib.dense_gemm_f16(T(ex["A"]), T(ex["W"].T))), ex["A"], ex["W"], "dense exact")
 
 
+# The shapes where the dense fp16 kernel runs its 256 x 256 tile (two-stage
+# ring) and is the denominator of the fp16 speedups: ViT-Large fc1 and the
+# BERT-base FFN fc1 shape of the tile-wise workload.
+DENSE_BIG = [(4096, 1024, 4096), (4096, 768, 3072)]
+
+
+@pytest.mark.parametrize("M,K,N", DENSE_BIG)
+def test_dense_f16_big_tile(lib, gpu, M, K, N):
+    assert lib.tile_choice(lib.SSG_KIND_DENSE_F16, M, N, K) == (256, 256)
+    rng = np.random.default_rng(M + 5 * K + N)
+    A = wl.f16_normal(rng, (M, K))
+    W = wl.f16_normal(rng, (K, N), 0.02)
+    C = H(lib.dense_gemm_f16(T(A), T(W.T), splits=1))
+    check_f16(C, A, W, K, f"dense f16 256x256 tile {M}x{K}x{N}")
+    # exact integers: every fp32 partial sum is an exact integer (|C| <= 6K),
+    # so the single fp16 rounding equals the oracle's bit for bit
+    ex = wl.exact_int_24_f16(rng, M, K, N)
+    check_f16_exact(H(lib.dense_gemm_f16(T(ex["A"]), T(ex["W"].T), splits=1)), ex["A"], ex["W"],
+                    f"dense f16 256x256 tile exact {M}x{K}x{N}")
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 128, 64), (200, 768, 320), (129, 512, 64)])
 @pytest.mark.parametrize("scaled", [False, True])
 def test_dense_i8(lib, gpu, M, K, N, scaled):
@@ -312,8 +341,7 @@ def test_tw_random(lib, gpu, M, K, N, G, d):
     case = wl.random_tw_f16(np.random.default_rng(M + K + G), M, K, N, G, d)
     C = run_tw(lib, case["A"], case["Wp"], G)
     packed = oracle.ref_tw_pack(case["Wp"], G)
-    n_terms = int(max(np.diff(packed["k_ptr"]).max(), 1))
-    check_f16(C, case["A"], case["Wp"], n_terms, f"tw {M}x{K}x{N} G={G}")
+    check_f16(C, case["A"], case["Wp"], tw_terms(case["Wp"], G), f"tw {M}x{K}x{N} G={G}")
     # pruned columns are exact +0
     kept = np.zeros(N, bool)
     for t in range(packed["T"]):
@@ -346,14 +374,16 @@ def test_tw_all_zero_weight(lib, gpu):
 def test_tw_bert_base_fc1(lib, gpu):
     c = wl.make_bert_base_fc1_tw()
     C = run_tw(lib, c["A"], c["Wp"], c["G"])
-    check_f16(C, c["A"], c["Wp"], 512, c["name"])
+    check_f16(C, c["A"], c["Wp"], tw_terms(c["Wp"], c["G"]), c["name"])
 
 
 @pytest.mark.parametrize("which", ["fc1", "fc2"])
 def test_tw_bert_large_ffn(lib, gpu, which):
     c = wl.make_bert_large_ffn_tw()[which]
     C = run_tw(lib, c["A"], c["Wp"], c["G"])
-    check_f16(C, c["A"], c["Wp"], 1311, c["name"])
+    n = tw_terms(c["Wp"], c["G"])
+    assert n.max() == {"fc1": 328, "fc2": 1311}[which]  # K_t of the uniform 10 % tiles
+    check_f16(C, c["A"], c["Wp"], n, c["name"])
 
 
 def test_tw_indexed_oracle_agrees(lib, gpu):
@@ -365,16 +395,22 @@ def test_tw_indexed_oracle_agrees(lib, gpu):
 
 
 # ---------------------------------------------------------------- block-wise through the tile-wise kernel
+@pytest.mark.parametrize("b", [32, 64])
 @pytest.mark.parametrize("d", [0.25, 0.5, 1.0])
-def test_blockwise_via_tilewise_kernel(lib, gpu, d):
-    # a 64x64 block-pruned weight is a tile-wise weight (G = 64) of whole 64-row runs
-    rng = np.random.default_rng(50)
+def test_blockwise_via_tilewise_kernel(lib, gpu, b, d):
+    # a b x b block-pruned weight (the slides' 32x32 and 64x64 block-sparse
+    # patterns) is a tile-wise weight (G = b) of whole b-row runs
+    rng = np.random.default_rng(50 + b)
     A = wl.f16_normal(rng, (200, 512))
-    Wp = wl.prune_blockwise(wl.f16_normal(rng, (512, 256), 0.02), 64, d)
-    packed = lib.tw_pack_f16(Wp, 64)
-    assert (np.diff(packed.n_ptr) == 64).all() and (np.diff(packed.k_ptr) % 64 == 0).all()
-    C = run_tw(lib, A, Wp, 64)
-    check_f16(C, A, Wp, int(np.diff(packed.k_ptr).max()), f"BW d={d}")
+    Wp = wl.prune_blockwise(wl.f16_normal(rng, (512, 256), 0.02), b, d)
+    packed = lib.tw_pack_f16(Wp, b)
+    assert (np.diff(packed.n_ptr) == b).all() and (np.diff(packed.k_ptr) % b == 0).all()
+    C = run_tw(lib, A, Wp, b)
+    check_f16(C, A, Wp, tw_terms(Wp, b), f"BW {b}x{b} d={d}")
+    # exact integers: bit-exact
+    Ax = rng.integers(-3, 4, size=(200, 512)).astype(np.float16)
+    Wx = wl.prune_blockwise(rng.integers(-2, 3, size=(512, 256)).astype(np.float16), b, d)
+    check_f16_exact(run_tw(lib, Ax, Wx, b), Ax, Wx, f"BW {b}x{b} d={d} exact")
 
 
 # ---------------------------------------------------------------- int8 tile-wise
@@ -452,9 +488,14 @@ def test_tw_row_major_a(lib, gpu, M, K, N, G, d):
     packed, At = _tw_setup(lib, case["A"], case["Wp"], G)
     C = H(lib.tw_gemm_f16(At, packed))
     Cr = H(lib.tw_gemm_f16_ex(T(case["A"]), packed, a_rowmajor=True))
+    check_f16(Cr, case["A"], case["Wp"], tw_terms(case["Wp"], G), f"tw row-major A {M}x{K}x{N}")
     assert np.array_equal(Cr.view(np.uint16), C.view(np.uint16))
     Crt = H(lib.tw_gemm_f16_ex(T(case["A"]), packed, a_rowmajor=True, out_t=True))
     assert np.array_equal(Crt.T.view(np.uint16), C.view(np.uint16))
+    # exact integers through the row-major gather: bit-exact against the oracle
+    ex = wl.exact_int_tw_f16(np.random.default_rng(M + K), M, K, N, G, d)
+    px = lib.tw_pack_f16(ex["Wp"], G).to("cuda")
+    check_f16_exact(H(lib.tw_gemm_f16_ex(T(ex["A"]), px, a_rowmajor=True)), ex["A"], ex["Wp"], "tw row-major exact")
 
 
 def test_tw_chain_without_transpose(lib, gpu):
@@ -468,8 +509,8 @@ def test_tw_chain_without_transpose(lib, gpu):
     Ct1 = lib.tw_gemm_f16_ex(lib.ssg_transpose_f16(T(l1["A"])), p1, out_t=True)
     C2 = H(lib.tw_gemm_f16(Ct1, p2))
     A2 = H(Ct1).T.copy()  # layer 1's fp16 output, as the oracle's input of layer 2
-    check_f16(A2, l1["A"], l1["Wp"], K, "chain layer 1")
-    check_f16(C2, A2, W2, N1, "chain layer 2")
+    check_f16(A2, l1["A"], l1["Wp"], tw_terms(l1["Wp"], G), "chain layer 1")
+    check_f16(C2, A2, W2, tw_terms(W2, G), "chain layer 2")
 
 
 def test_tw_tile_ranges(lib, gpu):
@@ -477,6 +518,7 @@ def test_tw_tile_ranges(lib, gpu):
     case = wl.random_tw_f16(np.random.default_rng(31), 200, 512, 640, 128, [0.2, 0.5, 0.0, 0.8, 0.3])
     packed, At = _tw_setup(lib, case["A"], case["Wp"], 128)
     full = H(lib.tw_gemm_f16(At, packed))
+    check_f16(full, case["A"], case["Wp"], tw_terms(case["Wp"], 128), "tw tile ranges, grouped launch")
     C = torch.full((200, 640), float("nan"), dtype=torch.float16, device="cuda")
     lib.tw_gemm_f16_ex(At, packed, t_first=1, t_count=2, out=C)
     part = H(C)
@@ -490,7 +532,16 @@ def test_tw_tile_ranges(lib, gpu):
             assert np.isnan(win).all()  # tiles outside the range are not written
     lib.tw_gemm_f16_ex(At, packed, t_first=0, t_count=1, out=C)
     lib.tw_gemm_f16_ex(At, packed, t_first=3, t_count=2, out=C)
-    assert np.array_equal(H(C).view(np.uint16), full.view(np.uint16))
+    assembled = H(C)
+    check_f16(assembled, case["A"], case["Wp"], tw_terms(case["Wp"], 128), "tw tile ranges, assembled")
+    assert np.array_equal(assembled.view(np.uint16), full.view(np.uint16))
+    # exact integers, assembled from three ranges: bit-exact against the oracle
+    ex = wl.exact_int_tw_f16(np.random.default_rng(32), 200, 512, 640, 128, [0.2, 0.5, 0.0, 0.8, 0.3])
+    px, Atx = _tw_setup(lib, ex["A"], ex["Wp"], 128)
+    Cx = torch.full((200, 640), float("nan"), dtype=torch.float16, device="cuda")
+    for t0, tc in ((3, 2), (0, 1), (1, 2)):
+        lib.tw_gemm_f16_ex(Atx, px, t_first=t0, t_count=tc, out=Cx)
+    check_f16_exact(H(Cx), ex["A"], ex["Wp"], "tw tile ranges exact")
 
 
 def test_tw_multi_stream_schedule(lib, gpu):
@@ -500,7 +551,13 @@ def test_tw_multi_stream_schedule(lib, gpu):
     full = H(lib.tw_gemm_f16(At, packed))
     streams = [torch.cuda.Stream() for _ in range(4)]
     C = H(lib.tw_gemm_f16_streams(At, packed, streams))
+    check_f16(C, c["A"], c["Wp"], tw_terms(c["Wp"], c["G"]), "tw multi-stream schedule")
     assert np.array_equal(C.view(np.uint16), full.view(np.uint16))
+    # exact integers over the streams: bit-exact against the oracle
+    ex = wl.exact_int_tw_f16(np.random.default_rng(33), 512, 768, 1536, 128,
+                             np.linspace(0.05, 0.6, 12))
+    px, Atx = _tw_setup(lib, ex["A"], ex["Wp"], 128)
+    check_f16_exact(H(lib.tw_gemm_f16_streams(Atx, px, streams)), ex["A"], ex["Wp"], "tw streams exact")
 
 
 # ---------------------------------------------------------------- transpose, determinism, errors
@@ -646,9 +703,8 @@ def test_w24_i8_random_shapes(lib, gpu, M, K, N):
 @pytest.mark.parametrize("M,K,N,G,d", _random_shapes(103, 6, 8, 8, [16, 32, 64, 128]))
 def test_tw_random_shapes(lib, gpu, M, K, N, G, d):
     case = wl.random_tw_f16(np.random.default_rng(M + K + N), M, K, N, G, d)
-    packed = lib.tw_pack_f16(case["Wp"], G)
-    n_terms = int(max(np.diff(packed.k_ptr).max(), 1))
-    check_f16(run_tw(lib, case["A"], case["Wp"], G), case["A"], case["Wp"], n_terms, f"TW {M}x{K}x{N} G={G}")
+    check_f16(run_tw(lib, case["A"], case["Wp"], G), case["A"], case["Wp"], tw_terms(case["Wp"], G),
+              f"TW {M}x{K}x{N} G={G}")
 
 
 @pytest.mark.parametrize("M,K,N,G,d", _random_shapes(104, 4, 16, 16, [16, 64, 128]))
@@ -658,3 +714,21 @@ def test_tw_i8_random_shapes(lib, gpu, M, K, N, G, d):
     C = run_tw_i8(lib, case["A"], case["Wp"], G, case["scale"], None, "f32")
     ref = oracle.ref_gemm_i8_out(case["A"], case["Wp"], case["scale"], None, "f32")
     assert np.array_equal(C.view(np.uint32), ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------- the element-wise comparison baseline
+def test_elementwise_csr_baseline_matches_oracle(lib, gpu):
+    """The pattern study's element-wise leg (torch's CSR sparse product in fp32,
+    the slides' cuSparse stand-in) computes C = A . W_p: every fp16 x fp16
+    product is exact in fp32, so it meets the fp32 summation bound."""
+    import torch
+    rng = np.random.default_rng(60)
+    A = wl.f16_normal(rng, (256, 768))
+    Wp = wl.prune_elementwise(wl.f16_normal(rng, (768, 384), 0.02), 0.37)
+    S = torch.from_numpy(np.ascontiguousarray(Wp.T.astype(np.float32))).cuda().to_sparse_csr()
+    At32 = torch.from_numpy(np.ascontiguousarray(A.T.astype(np.float32))).cuda()
+    C = H(torch.sparse.mm(S, At32)).T
+    C_ref = oracle.ref_gemm_f64(A, Wp)
+    n = np.count_nonzero(Wp, axis=0).astype(np.float64)  # products per output column
+    bound = 2.0 * n * 2.0 ** -24 * oracle.ref_abs_gemm(A, Wp) + 2.0 ** -126
+    assert (np.abs(C.astype(np.float64) - C_ref) <= bound).all()

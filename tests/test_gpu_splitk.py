@@ -30,10 +30,13 @@ def H(t):
     return t.cpu().numpy()
 
 
-def _check_f16(C, A, Wp, what):
+def _check_f16(C, A, Wp, what, dense=False):
+    """Loose and strict bounds; the strict one counts the products each output
+    sums over all splits: K for the dense kinds, K/2 kept slots for 2:4."""
     C_ref, _ = oracle.ref_gemm_f16(A, Wp)
+    n_terms = Wp.shape[0] if dense else Wp.shape[0] // 2
     assert oracle.loose_err(C, C_ref) <= 1e-2, what
-    assert oracle.strict_ok_f16(C, C_ref, oracle.ref_abs_gemm(A, Wp), Wp.shape[0]), what
+    assert oracle.strict_ok_f16(C, C_ref, oracle.ref_abs_gemm(A, Wp), n_terms), what
 
 
 def _exact_f16(C, A, Wp, what):
@@ -57,7 +60,7 @@ def test_w24_f16_splitk_random(lib, gpu, splits):
 def test_dense_f16_splitk_random(lib, gpu, splits):
     case = wl.random_24_f16(np.random.default_rng(10 + splits), 300, 2048, 256)
     C = H(lib.dense_gemm_f16_splitk(T(case["A"]), T(case["W"].T), splits))
-    _check_f16(C, case["A"], case["W"], f"dense f16 splits={splits}")
+    _check_f16(C, case["A"], case["W"], f"dense f16 splits={splits}", dense=True)
 
 
 @pytest.mark.parametrize("splits", [2, 5])  # K = 640: 10 K stages
@@ -159,4 +162,18 @@ def test_f16_split_tiles_of_a_shard(lib, gpu, splits):
     C = H(lib.w24_gemm_f16_splitk(T(case["A"]), T(vals), T(meta.view(np.int32)), splits))
     _check_f16(C, case["A"], case["Wp"], f"w24 f16 shard fc2 splits={splits}")
     C = H(lib.dense_gemm_f16_splitk(T(case["A"]), T(case["W"].T), splits))
-    _check_f16(C, case["A"], case["W"], f"dense f16 shard fc2 splits={splits}")
+    _check_f16(C, case["A"], case["W"], f"dense f16 shard fc2 splits={splits}", dense=True)
+
+
+@pytest.mark.parametrize("splits", [2, 4, 8])
+def test_f16_split_tiles_of_a_shard_exact(lib, gpu, splits):
+    """The same split forms (64 x 64 x 2, 64 x 128 x 4, 128 x 128 x 8) on
+    exact-integer inputs: every fp32 partial and their sum are exact integers,
+    so the one fp16 rounding matches the oracle's bit for bit (|C| stays far
+    below the fp16 range: at most 4096 * 3 * 2)."""
+    case = wl.exact_int_24_f16(np.random.default_rng(70 + splits), 512, 4096, 1024)
+    vals, meta = lib.w24_pack_f16(case["Wp"])
+    C = H(lib.w24_gemm_f16_splitk(T(case["A"]), T(vals), T(meta.view(np.int32)), splits))
+    _exact_f16(C, case["A"], case["Wp"], f"w24 f16 shard fc2 exact splits={splits}")
+    C = H(lib.dense_gemm_f16_splitk(T(case["A"]), T(case["W"].T), splits))
+    _exact_f16(C, case["A"], case["W"], f"dense f16 shard fc2 exact splits={splits}")

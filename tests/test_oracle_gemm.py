@@ -192,6 +192,53 @@ def test_strict_bound_catches_one_dropped_term():
     assert not oracle.strict_ok_f16(Cd, C_ref, S, 384)
 
 
+def check_abs_gemm(fn, seed=0, trials=5):
+    """True iff fn(A, W) is S = |A| . |W| (the error scale of the strict bound):
+    a hand-computed 2 x 2 case whose products have mixed signs, then the
+    exact rational sum of |a| |w| on tiny random inputs."""
+    A = np.array([[1, -2], [3, 4]], np.float16)
+    W = np.array([[-1, 0.5], [2, 0.25]], np.float16)
+    # |A|.|W| by hand: [[1*1 + 2*2, 1*0.5 + 2*0.25], [3*1 + 4*2, 3*0.5 + 4*0.25]]
+    if not np.array_equal(np.asarray(fn(A, W), dtype=np.float64), np.array([[5.0, 1.0], [11.0, 2.5]])):
+        return False
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        M, K, N = rng.integers(1, 6), 4 * rng.integers(1, 5), rng.integers(1, 6)
+        case = wl.random_24_f16(rng, M, K, N, std_w=0.5)
+        got = np.asarray(fn(case["A"], case["Wp"]), dtype=np.float64)
+        Aa = [[abs(Fraction(float(x))) for x in row] for row in case["A"].tolist()]
+        Wa = [[abs(Fraction(float(x))) for x in row] for row in case["Wp"].tolist()]
+        for m in range(M):
+            for n in range(N):
+                ex = sum((Aa[m][k] * Wa[k][n] for k in range(K)), Fraction(0))
+                if abs(Fraction(float(got[m, n])) - ex) > Fraction(K * 2.0 ** -52) * ex:
+                    return False
+    return True
+
+
+def test_abs_gemm_pinned():
+    assert check_abs_gemm(oracle.ref_abs_gemm)
+    # S bounds |C_ref| everywhere and equals it when every operand is nonnegative
+    rng = np.random.default_rng(3)
+    case = wl.random_24_f16(rng, 16, 64, 24)
+    S = oracle.ref_abs_gemm(case["A"], case["Wp"])
+    C = oracle.ref_gemm_f64(case["A"], case["Wp"])
+    assert (S >= np.abs(C)).all()
+    Ap, Wpp = np.abs(case["A"]), np.abs(case["Wp"])
+    assert np.array_equal(oracle.ref_abs_gemm(Ap, Wpp), oracle.ref_gemm_f64(Ap, Wpp))
+
+
+@pytest.mark.parametrize("mutant", [
+    lambda A, W: np.abs(A.astype(np.float64)) @ W.astype(np.float64),   # abs on A only
+    lambda A, W: A.astype(np.float64) @ np.abs(W.astype(np.float64)),   # abs on W only
+    lambda A, W: np.abs(A.astype(np.float64) @ W.astype(np.float64)),   # abs of the sum
+    lambda A, W: 2.0 * oracle.ref_abs_gemm(A, W),                       # loosened by a factor
+    lambda A, W: np.abs(A.astype(np.float64)) @ np.abs(W.astype(np.float64))[::-1],  # rows of W reversed
+])
+def test_abs_gemm_pin_catches_planted_mistakes(mutant):
+    assert not check_abs_gemm(mutant)
+
+
 def test_loose_rejects_nan():
     assert not oracle.loose_ok(np.array([np.nan, 1.0]), np.array([1.0, 1.0]))
     assert oracle.loose_err(np.zeros(3), np.zeros(3)) == 0.0
