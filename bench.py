@@ -628,8 +628,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true", help="table mode: every workload and kernel")
     ap.add_argument("--workloads", default="",
-                    help="table mode: comma list from " + ",".join(WORKLOADS) +
-                         " or vit_large:<qkv|proj|fc1|fc2> for one layer-0 GEMM (default: all)")
+                    help="table mode: comma list from " + ",".join(WORKLOADS + SUB_WORKLOADS) +
+                         " (vit_large:<gemm>: one layer-0 GEMM; default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--no-sclk", action="store_true",
                     help="skip the shader-clock reading (2 s of extra replays; for profiled runs)")
@@ -652,6 +652,8 @@ def main(argv=None):
     ap.add_argument("--profile-steps", type=int, default=20, help="--steps of the profiled command (dispatch groups)")
     ap.add_argument("--profile-warmup", type=int, default=5, help="--warmup of the profiled command")
     ap.add_argument("--bench-log", help="stdout of the profiled command (its bench line is quoted in the summary)")
+    ap.add_argument("--k-stages", type=int, default=0,
+                    help="--summarize-profile: K stages per output tile, to report cycles per K-stage")
     a = ap.parse_args(argv)
     if a.summarize_profile:
         return summarize_profile(a)
@@ -836,6 +838,11 @@ def summarize_profile(a):
         # is busy / (GUI_ACTIVE x 128)
         out.append(f"target '{a.kernel}': SQ_VALU_MFMA_BUSY_CYCLES {busy:.0f}, GRBM_GUI_ACTIVE {gui:.0f} "
                    f"({nb} dispatches); MFMA busy fraction = busy / (GUI_ACTIVE x 128) = {busy / (gui * 128):.3f}")
+        if a.k_stages:
+            # one round of output tiles (at most one workgroup per CU): the
+            # kernel's cycles per XCD over its K stages
+            out.append(f"  cycles per K-stage (GRBM_GUI_ACTIVE / 8 XCDs / {a.k_stages} stages, one round of "
+                       f"tiles): {gui / 8 / a.k_stages:.0f}")
     out.append(f"copy of {COPY_BYTES} B: FETCH_SIZE {cf} KiB ({ncf}), WRITE_SIZE {cw} KiB ({ncw})")
     if None not in (cf, cw, tf, tw) and cf > 0 and cw > 0:
         kf, kw = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
@@ -1020,6 +1027,9 @@ def patterns(torch, ssg, perf, wl, timer, steps, warmup, emit):
 
 WORKLOADS = ("small", "vit_base_fc1", "bert_base_fc1", "bert_large_ffn", "vit_large", "vit_large_stack",
              "bert_base_fc1_i8", "patterns", "vit_large_shard8")
+# table-mode selectors beside WORKLOADS: one GEMM of a workload (for profiling one kernel launch shape)
+SUB_WORKLOADS = ("bert_large_fc1", "bert_large_fc2", "vit_large:qkv", "vit_large:proj", "vit_large:fc1",
+                 "vit_large:fc2")
 
 
 def table(a, torch, ssg, perf, wl, timer):
@@ -1068,9 +1078,9 @@ def table(a, torch, ssg, perf, wl, timer):
     tw_cases = []
     if "bert_base_fc1" in want:
         tw_cases.append(wl.make_bert_base_fc1_tw())
-    if "bert_large_ffn" in want:
+    if want & {"bert_large_ffn", "bert_large_fc1", "bert_large_fc2"}:
         c4 = wl.make_bert_large_ffn_tw()
-        tw_cases += [c4["fc1"], c4["fc2"]]
+        tw_cases += [c4[g] for g in ("fc1", "fc2") if want & {"bert_large_ffn", "bert_large_" + g}]
     for c in tw_cases:
         r = tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate, extras=not a.no_tw_extras)
         emit(dict(workload=c["name"] + "_tw_f16", shape=[c["M"], c["K"], c["N"]], **r,

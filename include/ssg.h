@@ -281,8 +281,12 @@ int w24_gemm_i8_splitk(const int8_t *A, const int8_t *vals, const uint32_t *meta
  * contiguous reads (the tile-wise slides transpose A to avoid uncoalesced
  * access).  The packed arrays are tw_pack_f16's, in device memory, with
  * T = ceil(N/G).  Every column of C is written: kept columns get the tile
- * product, pruned columns +0.  Requires G % 16 == 0, G <= 128, N % G == 0,
- * M % 8 == 0, K >= 1. */
+ * product, pruned columns +0.  Requires G % 16 == 0, G <= 256, N % G == 0,
+ * M >= 0, K >= 1; At, vals and C 16-byte aligned.  Any M is accepted: when M
+ * is not a multiple of 8 the rows of At are not 16-byte aligned and the
+ * kernel gathers them through registers (slower than the direct-to-LDS
+ * loads of the aligned case); tiles wider than 128 columns run a wider
+ * configuration (two workgroups per CU instead of three). */
 int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_k,
                 const int32_t *offset_n, const int32_t *v_ptr, const int32_t *k_ptr,
                 const int32_t *n_ptr, const int32_t *tile_order, int32_t T, int32_t G,
@@ -325,8 +329,9 @@ int tw_gemm_f16_ex(const void *At, const void *vals, const int32_t *offset_k,
  * and bias NULL), otherwise y = float(acc) * scale[n] (+ bias[n]) stored as
  * fp32, fp16 or saturated int8 (scale, bias: fp32 [N], 16-byte aligned).
  * Every column of C is written: pruned columns get the epilogue of a zero
- * accumulator (0 * scale[n] + bias[n]).  Requires G % 16 == 0, G <= 128,
- * N % G == 0, M % 16 == 0, K >= 1. */
+ * accumulator (0 * scale[n] + bias[n]).  Requires G % 16 == 0, G <= 256,
+ * N % G == 0, M >= 0, K >= 1 (when M is not a multiple of 16 the rows of At
+ * are gathered through registers, as for tw_gemm_f16). */
 int tw_gemm_i8(const int8_t *At, const int8_t *vals, const int32_t *offset_k,
                const int32_t *offset_n, const int32_t *v_ptr, const int32_t *k_ptr,
                const int32_t *n_ptr, const int32_t *tile_order, int32_t T, int32_t G,

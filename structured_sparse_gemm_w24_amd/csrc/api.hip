@@ -252,11 +252,10 @@ int tw_run(const char *fn, const void *At, const void *vals, const int32_t *offs
     if (M < 0 || N <= 0 || K <= 0 || !fits_int(M) || !fits_int(N) || !fits_int(K))
         return ssg::fail(SSG_EINVAL, "%s: bad shape M=%lld N=%lld K=%lld", fn, (long long)M, (long long)N,
                          (long long)K);
-    if (G <= 0 || G % 16 || G > 128)
-        return ssg::fail(SSG_EINVAL, "%s: G=%d must be a positive multiple of 16, at most 128", fn, G);
+    if (G <= 0 || G % 16 || G > 256)
+        return ssg::fail(SSG_EINVAL, "%s: G=%d must be a positive multiple of 16, at most 256", fn, G);
     if (N % G) return ssg::fail(SSG_EINVAL, "%s: N=%lld must be a multiple of G=%d", fn, (long long)N, G);
     if (T != N / G) return ssg::fail(SSG_EINVAL, "%s: T=%d must equal N/G=%lld", fn, T, (long long)(N / G));
-    if (M % 8) return ssg::fail(SSG_EINVAL, "%s: M=%lld must be a multiple of 8", fn, (long long)M);
     if (t_first < 0 || t_count < 1 || int64_t(t_first) + t_count > T)
         return ssg::fail(SSG_EINVAL, "%s: tile range [%d, %d + %d) outside [0, %d)", fn, t_first, t_first, t_count, T);
     if (flags & ~(SSG_TW_OUT_T | SSG_TW_A_ROWMAJOR)) return ssg::fail(SSG_EINVAL, "%s: unknown flags 0x%x", fn, flags);
@@ -302,11 +301,10 @@ SSG_API int tw_gemm_i8(const int8_t *At, const int8_t *vals, const int32_t *offs
     if (M < 0 || N <= 0 || K <= 0 || !fits_int(M) || !fits_int(N) || !fits_int(K))
         return ssg::fail(SSG_EINVAL, "%s: bad shape M=%lld N=%lld K=%lld", fn, (long long)M, (long long)N,
                          (long long)K);
-    if (G <= 0 || G % 16 || G > 128)
-        return ssg::fail(SSG_EINVAL, "%s: G=%d must be a positive multiple of 16, at most 128", fn, G);
+    if (G <= 0 || G % 16 || G > 256)
+        return ssg::fail(SSG_EINVAL, "%s: G=%d must be a positive multiple of 16, at most 256", fn, G);
     if (N % G) return ssg::fail(SSG_EINVAL, "%s: N=%lld must be a multiple of G=%d", fn, (long long)N, G);
     if (T != N / G) return ssg::fail(SSG_EINVAL, "%s: T=%d must equal N/G=%lld", fn, T, (long long)(N / G));
-    if (M % 16) return ssg::fail(SSG_EINVAL, "%s: M=%lld must be a multiple of 16", fn, (long long)M);
     if (!fits_int((M + 127) / 128 * int64_t(T))) return ssg::fail(SSG_EINVAL, "%s: too many work items", fn);
     int rc = check_i8_epilogue(fn, scale, bias, out_type);
     if (rc) return rc;

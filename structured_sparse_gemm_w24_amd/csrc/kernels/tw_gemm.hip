@@ -83,8 +83,8 @@ __device__ __forceinline__ void tw_read_b2(uint32_t addr, u32x2 &b0, u32x2 &b1) 
 
 // BK picked rows per stage (32 or 64), NB stage buffers, KCAP offset_k
 // entries held in LDS at a time, WPE waves per SIMD the register allocation
-// must allow (two workgroups per CU need 4).
-template <int BK_, int NB_, int KCAP_, int WPE_>
+// must allow (two workgroups per CU need 4), GMAX the widest tile.
+template <int BK_, int NB_, int KCAP_, int WPE_, int GMAX_ = 128>
 struct TwCfg {
     static constexpr int NW = 8, NT = NW * 64;
     static constexpr int BM = 128;   // tokens per work item (8 blocks of 16)
@@ -93,7 +93,7 @@ struct TwCfg {
     static constexpr int NB = NB_;
     static constexpr int KCAP = KCAP_;
     static constexpr int WPE = WPE_;
-    static constexpr int GMAX = 128;  // widest supported tile
+    static constexpr int GMAX = GMAX_;  // widest supported tile
     static constexpr int A_STAGE = BK * BM * 2;    // [BK][BM] halves
     static constexpr int W_STAGE = GMAX * BK * 2;  // [GMAX][BK] halves
     static constexpr int STAGE = A_STAGE + W_STAGE;
@@ -121,15 +121,24 @@ __device__ __forceinline__ int tw_swz_w(int j, int c) {
     else return c ^ ((j >> 1) & 3);
 }
 
+// How the At stage reaches LDS.
+//   A_DMA    K-major At [K][M], M a multiple of 8: 16-byte direct-to-LDS loads;
+//   A_ROW    row-major A [M][K] (the slides' "without transpose" case): the
+//            picked k of a token are scattered 2-byte elements of its row, so
+//            each stage is gathered through registers, 8 elements per thread,
+//            into the same K-major LDS layout; every element is its own
+//            memory request;
+//   A_KGATH  K-major At with M not a multiple of 8: a picked row's 16-byte
+//            pieces are not 16-byte aligned, so each thread gathers 8
+//            consecutive tokens of one picked row through registers (2-byte
+//            loads, bounds-checked against M) into the same LDS layout.
+enum AMode { A_DMA = 0, A_ROW = 1, A_KGATH = 2 };
+
 // OUTT: write C transposed, Ct [N][M] (token-contiguous rows), which is the
 // K-major input of a following tile-wise layer (the transpose fused into the
 // producing GEMM); otherwise C [M][N].  Cw points at the tile's first output
 // column (row, for OUTT).
-// AROW: A is row-major [M][K] (the slides' "without transpose" case): the
-// picked k of a token are scattered 2-byte elements of its row, so each stage
-// is gathered through registers, 8 elements per thread, into the same
-// K-major LDS layout; every element is its own memory request.
-template <class CF, int NJ, bool OUTT, bool AROW>
+template <class CF, int NJ, bool OUTT, int AM>
 __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restrict__ At,
                                         const uint16_t *__restrict__ vt, const int32_t *__restrict__ offk,
                                         const int32_t *__restrict__ offn, int kt, int nt, int G, int m0,
@@ -145,7 +154,7 @@ __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restric
     const int ld = (kt + 7) & ~7;
     // V_t loads per stage: NJ*16 rows of 2*BK bytes = NJ*KS KiB, round-robin over waves
     const int lw = (NJ * KS - wave + NW - 1) / NW;
-    const int per_stage = (AROW ? 0 : LA) + lw;  // direct-to-LDS loads per stage
+    const int per_stage = (AM == A_DMA ? LA : 0) + lw;  // direct-to-LDS loads per stage
 
     // A loads: instruction j of the wave covers stage rows 4q .. 4q+3 (q = j*NW + wave);
     // lane -> row 4q + lane/16, stored chunk lane%16.
@@ -185,7 +194,25 @@ __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restric
 
             auto issue = [&](int s) {
                 uint8_t *base = smem + (s % NB) * STAGE;
-                if constexpr (AROW) {
+                if constexpr (AM == A_KGATH) {
+                    static_assert(BK * BM == NT * 8, "gather mapping: one 8-token piece per thread");
+                    // thread -> picked row r, stored 16-byte chunk p (source chunk tw_swz_a(r, p))
+                    const int r = tid / (BM / 8), p = tid % (BM / 8);
+                    const int kk = s * BK + r;
+                    const int tok = m0 + tw_swz_a(r, p) * 8;
+                    const bool row_ok = kk < ck;
+                    const int64_t rb = row_ok ? int64_t(s_idx[kk]) * M : 0;
+                    uint16_t v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = (row_ok && tok + e < M) ? At[rb + tok + e] : uint16_t(0);
+                    u32x4 w;
+                    w.x = uint32_t(v[0]) | (uint32_t(v[1]) << 16);
+                    w.y = uint32_t(v[2]) | (uint32_t(v[3]) << 16);
+                    w.z = uint32_t(v[4]) | (uint32_t(v[5]) << 16);
+                    w.w = uint32_t(v[6]) | (uint32_t(v[7]) << 16);
+                    *reinterpret_cast<u32x4 *>(base + r * (BM * 2) + p * 16) = w;
+                }
+                if constexpr (AM == A_ROW) {
                     static_assert(BK == 32 && NT == 4 * BM, "gather mapping: 4 threads x 8 picked rows per token");
                     const int tok = tid >> 2, kg = (tid & 3) * 8;
                     const int m = m0 + tok;
@@ -203,7 +230,7 @@ __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restric
                     }
                 }
 #pragma unroll
-                for (int j = 0; j < (AROW ? 0 : LA); ++j) {
+                for (int j = 0; j < (AM == A_DMA ? LA : 0); ++j) {
                     const int q = j * NW + wave;
                     const int r = 4 * q + a_sub;  // stage row
                     const int kk = s * BK + r;    // picked row inside the chunk
@@ -237,17 +264,24 @@ __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restric
                 for (int k32 = 0; k32 < KS; ++k32) {
                     const half8 bf = __builtin_bit_cast(
                         half8, __builtin_shufflevector(b[2 * k32], b[2 * k32 + 1], 0, 1, 2, 3));
-                    u32x4 wf[NJ];
+                    // V_t fragments in batches of at most 8 column blocks (register budget of wide tiles)
+                    constexpr int JC = NJ > 8 ? 8 : NJ;
 #pragma unroll
-                    for (int jb = 0; jb < NJ; ++jb) {
-                        const int row = jb * 16 + j16;
-                        wf[jb] = *reinterpret_cast<const u32x4 *>(bW + row * (BK * 2) +
-                                                                  tw_swz_w<BK>(row, k32 * 4 + g16) * 16);
+                    for (int j0 = 0; j0 < NJ; j0 += JC) {
+                        u32x4 wf[JC];
+#pragma unroll
+                        for (int jj = 0; jj < JC; ++jj) {
+                            const int row = (j0 + jj) * 16 + j16;
+                            if (j0 + jj < NJ)
+                                wf[jj] = *reinterpret_cast<const u32x4 *>(bW + row * (BK * 2) +
+                                                                          tw_swz_w<BK>(row, k32 * 4 + g16) * 16);
+                        }
+#pragma unroll
+                        for (int jj = 0; jj < JC; ++jj)
+                            if (j0 + jj < NJ)
+                                acc[j0 + jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    __builtin_bit_cast(half8, wf[jj]), bf, acc[j0 + jj], 0, 0, 0);
                     }
-#pragma unroll
-                    for (int jb = 0; jb < NJ; ++jb)
-                        acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, wf[jb]), bf,
-                                                                         acc[jb], 0, 0, 0);
                 }
             }
         }
@@ -301,17 +335,27 @@ __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restric
             }
         }
         __syncthreads();
-        for (int c = tid; c < G * TCH; c += NT) {
-            const int row = c / TCH, ch = c % TCH;
-            const int m = m0 + ch * 8;  // M % 8 == 0: a chunk is all in or all out
-            if (m < M)
-                tw_store16(Cw + int64_t(row) * M + m, *reinterpret_cast<const u32x4 *>(win + row * TROW + ch * 16));
+        if (M % 8 == 0) {
+            for (int c = tid; c < G * TCH; c += NT) {
+                const int row = c / TCH, ch = c % TCH;
+                const int m = m0 + ch * 8;  // a chunk is all in or all out
+                if (m < M)
+                    tw_store16(Cw + int64_t(row) * M + m,
+                               *reinterpret_cast<const u32x4 *>(win + row * TROW + ch * 16));
+            }
+        } else {
+            // rows of Ct are not 16-byte aligned: one 2-byte store per token
+            for (int c = tid; c < G * BM; c += NT) {
+                const int row = c / BM, tk = c % BM;
+                const int m = m0 + tk;
+                if (m < M) Cw[int64_t(row) * M + m] = *reinterpret_cast<const uint16_t *>(win + row * TROW + tk * 2);
+            }
         }
     }
 }
 
 // Work items: token block mb x tiles tile_order[t_first .. t_first + t_count).
-template <class CF, bool OUTT, bool AROW>
+template <class CF, bool OUTT, int AM>
 __global__ void __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(CF::WPE)))
 tw_gemm_kernel(const uint16_t *__restrict__ At, const uint16_t *__restrict__ vals, const int32_t *__restrict__ offset_k,
                const int32_t *__restrict__ offset_n, const int32_t *__restrict__ v_ptr,
@@ -330,10 +374,15 @@ tw_gemm_kernel(const uint16_t *__restrict__ At, const uint16_t *__restrict__ val
     const int32_t *offn = offset_n + np0;
     uint16_t *Cw = OUTT ? C + int64_t(t) * G * M : C + int64_t(t) * G;
     const int m0 = mb * CF::BM;
+    // (a tile of at most GMAX columns has at most GMAX/16 column blocks)
     switch ((nt + 15) >> 4) {
 #define TW_CASE(J) \
-    case J: tw_item<CF, J, OUTT, AROW>(smem, At, vt, offk, offn, kt, nt, G, m0, Cw, M, N, K); break;
+    case J:                                                                                  \
+        if constexpr (J <= CF::GMAX / 16)                                                    \
+            tw_item<CF, J, OUTT, AM>(smem, At, vt, offk, offn, kt, nt, G, m0, Cw, M, N, K); \
+        break;
         TW_CASE(0) TW_CASE(1) TW_CASE(2) TW_CASE(3) TW_CASE(4) TW_CASE(5) TW_CASE(6) TW_CASE(7) TW_CASE(8)
+        TW_CASE(9) TW_CASE(10) TW_CASE(11) TW_CASE(12) TW_CASE(13) TW_CASE(14) TW_CASE(15) TW_CASE(16)
 #undef TW_CASE
         default: break;
     }
@@ -342,18 +391,36 @@ tw_gemm_kernel(const uint16_t *__restrict__ At, const uint16_t *__restrict__ val
 // 32-row stages, three buffers, 512 picked rows per index chunk: 51.7 KiB of
 // LDS and at most 85 VGPRs (6 waves per SIMD), so three workgroups share a CU.
 using TwProd = TwCfg<32, 3, 512, 6>;
+// Tiles wider than 128 columns (up to 256): 75 KiB of LDS (two workgroups per
+// CU) and up to 16 column blocks of accumulators per wave.
+using TwWide = TwCfg<32, 3, 512, 4, 256>;
+
+template <class CF>
+static hipError_t launch_tw_cfg(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
+                                const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
+                                const int32_t *tile_order, int t_first, int t_count, int G, bool out_t,
+                                bool a_rowmajor, void *C, int M, int N, int K, hipStream_t st) {
+    const int n_mb = (M + CF::BM - 1) / CF::BM;
+    const int am = a_rowmajor ? A_ROW : (M % 8 ? A_KGATH : A_DMA);
+    auto kern = out_t ? (am == A_ROW ? tw_gemm_kernel<CF, true, A_ROW>
+                         : am == A_KGATH ? tw_gemm_kernel<CF, true, A_KGATH> : tw_gemm_kernel<CF, true, A_DMA>)
+                      : (am == A_ROW ? tw_gemm_kernel<CF, false, A_ROW>
+                         : am == A_KGATH ? tw_gemm_kernel<CF, false, A_KGATH> : tw_gemm_kernel<CF, false, A_DMA>);
+    hipLaunchKernelGGL(kern, dim3(n_mb * t_count), dim3(CF::NT), 0, st, static_cast<const uint16_t *>(At),
+                       static_cast<const uint16_t *>(vals), offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order,
+                       t_first, t_count, G, static_cast<uint16_t *>(C), M, N, K);
+    return hipGetLastError();
+}
 
 hipError_t launch_tw_f16(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
                          const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
                          const int32_t *tile_order, int t_first, int t_count, int G, bool out_t, bool a_rowmajor,
                          void *C, int M, int N, int K, hipStream_t st) {
-    const int n_mb = (M + TwProd::BM - 1) / TwProd::BM;
-    auto kern = a_rowmajor ? (out_t ? tw_gemm_kernel<TwProd, true, true> : tw_gemm_kernel<TwProd, false, true>)
-                           : (out_t ? tw_gemm_kernel<TwProd, true, false> : tw_gemm_kernel<TwProd, false, false>);
-    hipLaunchKernelGGL(kern, dim3(n_mb * t_count), dim3(TwProd::NT), 0, st, static_cast<const uint16_t *>(At),
-                       static_cast<const uint16_t *>(vals), offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order,
-                       t_first, t_count, G, static_cast<uint16_t *>(C), M, N, K);
-    return hipGetLastError();
+    if (G > TwProd::GMAX)
+        return launch_tw_cfg<TwWide>(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, t_first,
+                                     t_count, G, out_t, a_rowmajor, C, M, N, K, st);
+    return launch_tw_cfg<TwProd>(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, t_first, t_count, G,
+                                 out_t, a_rowmajor, C, M, N, K, st);
 }
 
 }  // namespace ssg

@@ -58,13 +58,16 @@ __device__ __forceinline__ int tw8_swz_a(int r, int c) { return c ^ ((r ^ (r >> 
 // V_t stage: row j (channel), 16-byte chunk c (16 k) of a 64-byte row.
 __device__ __forceinline__ int tw8_swz_w(int j, int c) { return c ^ ((j >> 1) & 3); }
 
+// GMAX: widest tile; WPE: waves per SIMD the register allocation must allow.
+template <int GMAX_, int WPE_>
 struct Tw8Cfg {
     static constexpr int NW = 8, NT = NW * 64;
     static constexpr int BM = 128;   // tokens per work item (8 blocks of 16)
     static constexpr int BK = 64;    // picked rows per stage
     static constexpr int NB = 3;     // stage buffers
     static constexpr int KCAP = 512;  // offset_k entries held in LDS at a time
-    static constexpr int GMAX = 128;
+    static constexpr int GMAX = GMAX_;
+    static constexpr int WPE = WPE_;
     static constexpr int A_STAGE = BK * BM;     // bytes
     static constexpr int W_STAGE = GMAX * BK;   // bytes
     static constexpr int STAGE = A_STAGE + W_STAGE;
@@ -93,12 +96,15 @@ __device__ __forceinline__ uint32_t tw8_out(float y) {
     }
 }
 
-template <int NJ, int EPI>
+// KGATH: M is not a multiple of 16, so a picked row's 16-byte pieces are not
+// 16-byte aligned; each thread then gathers 16 consecutive tokens of one
+// picked row through registers (byte loads, bounds-checked against M) into
+// the LDS layout the direct-to-LDS loads produce.
+template <class CF, int NJ, int EPI, bool KGATH>
 __device__ __forceinline__ void tw8_item(uint8_t *smem, const int8_t *__restrict__ At, const int8_t *__restrict__ vt,
                                          const int32_t *__restrict__ offk, const int32_t *__restrict__ offn,
                                          const float *__restrict__ scale, const float *__restrict__ bias, int kt,
                                          int nt, int t, int G, int m0, uint8_t *__restrict__ Cw, int M, int N) {
-    using CF = Tw8Cfg;
     constexpr int NW = CF::NW, NT = CF::NT, BM = CF::BM, BK = CF::BK, NB = CF::NB, KCAP = CF::KCAP;
     constexpr int A_STAGE = CF::A_STAGE, STAGE = CF::STAGE;
     constexpr int OB = (EPI == OUT_F16) ? 2 : (EPI == OUT_I8 ? 1 : 4);  // output bytes
@@ -112,7 +118,7 @@ __device__ __forceinline__ void tw8_item(uint8_t *smem, const int8_t *__restrict
     const int lane = tid & 63, wave = tid >> 6;
     const int ld = (kt + 15) & ~15;
     const int lw = (NJ - wave + NW - 1) / NW;  // V_t loads per stage for this wave (NJ KiB in all)
-    const int per_stage = 1 + lw;
+    const int per_stage = (KGATH ? 0 : 1) + lw;  // direct-to-LDS loads per stage
 
     // per-column epilogue data: kept columns' scale and bias, and the output of a
     // zero accumulator for every window column
@@ -170,7 +176,28 @@ __device__ __forceinline__ void tw8_item(uint8_t *smem, const int8_t *__restrict
 
             auto issue = [&](int s) {
                 uint8_t *base = smem + (s % NB) * STAGE;
-                {
+                if constexpr (KGATH) {
+                    static_assert(BK * BM == NT * 16, "gather mapping: one 16-token piece per thread");
+                    // thread -> picked row r, stored 16-byte chunk p (source chunk tw8_swz_a(r, p))
+                    const int r = tid / (BM / 16), p = tid % (BM / 16);
+                    const int kk = s * BK + r;
+                    const int tok = m0 + tw8_swz_a(r, p) * 16;
+                    const bool row_ok = kk < ck;
+                    const int64_t rb = row_ok ? int64_t(s_idx[kk]) * M : 0;
+                    uint32_t w[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uint32_t x = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int m = tok + 4 * q + e;
+                            const uint32_t b = (row_ok && m < M) ? uint32_t(uint8_t(At[rb + m])) : 0u;
+                            x |= b << (8 * e);
+                        }
+                        w[q] = x;
+                    }
+                    *reinterpret_cast<u32x4 *>(base + r * BM + p * 16) = u32x4{w[0], w[1], w[2], w[3]};
+                } else {
                     const int kk = s * BK + a_row;
                     const int tok = m0 + tw8_swz_a(a_row, a_pos) * 16;
                     const void *src = g_tw8_zero;
@@ -196,12 +223,21 @@ __device__ __forceinline__ void tw8_item(uint8_t *smem, const int8_t *__restrict
                 u32x2 b0, b1;
                 tw8_read_b(smem_addr + stage_off + b_off, b0, b1);
                 const i32x4 bv = __builtin_bit_cast(i32x4, __builtin_shufflevector(b0, b1, 0, 1, 2, 3));
+                // V_t fragments in batches of at most 8 column blocks (register budget of wide tiles)
+                constexpr int JC = NJ > 8 ? 8 : NJ;
 #pragma unroll
-                for (int jb = 0; jb < NJ; ++jb) {
-                    const int row = jb * 16 + j16;
-                    const i32x4 wv =
-                        *reinterpret_cast<const i32x4 *>(bW + row * BK + tw8_swz_w(row, g16) * 16);
-                    acc[jb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv, bv, acc[jb], 0, 0, 0);
+                for (int j0 = 0; j0 < NJ; j0 += JC) {
+                    i32x4 wv[JC];
+#pragma unroll
+                    for (int jj = 0; jj < JC; ++jj) {
+                        const int row = (j0 + jj) * 16 + j16;
+                        if (j0 + jj < NJ)
+                            wv[jj] = *reinterpret_cast<const i32x4 *>(bW + row * BK + tw8_swz_w(row, g16) * 16);
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < JC; ++jj)
+                        if (j0 + jj < NJ)
+                            acc[j0 + jj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[jj], bv, acc[j0 + jj], 0, 0, 0);
                 }
             }
         }
@@ -259,16 +295,16 @@ __device__ __forceinline__ void tw8_item(uint8_t *smem, const int8_t *__restrict
     }
 }
 
-template <int EPI>
-__global__ void __launch_bounds__(Tw8Cfg::NT) __attribute__((amdgpu_waves_per_eu(6)))
+template <class CF, int EPI, bool KGATH>
+__global__ void __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(CF::WPE)))
 tw_gemm_i8_kernel(const int8_t *__restrict__ At, const int8_t *__restrict__ vals, const int32_t *__restrict__ offset_k,
                   const int32_t *__restrict__ offset_n, const int32_t *__restrict__ v_ptr,
                   const int32_t *__restrict__ k_ptr, const int32_t *__restrict__ n_ptr,
                   const int32_t *__restrict__ tile_order, int T, int G, const float *__restrict__ scale,
                   const float *__restrict__ bias, uint8_t *__restrict__ C, int M, int N) {
     constexpr int OB = (EPI == OUT_F16) ? 2 : (EPI == OUT_I8 ? 1 : 4);
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[Tw8Cfg::SMEM];
-    const int n_mb = (M + Tw8Cfg::BM - 1) / Tw8Cfg::BM;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[CF::SMEM];
+    const int n_mb = (M + CF::BM - 1) / CF::BM;
     const int item = xcd_remap(blockIdx.x, n_mb * T);
     const int mb = item / T;
     const int t = tile_order[item % T];
@@ -276,14 +312,41 @@ tw_gemm_i8_kernel(const int8_t *__restrict__ At, const int8_t *__restrict__ vals
     const int np0 = n_ptr[t], nt = n_ptr[t + 1] - np0;
     const int8_t *vt = vals + v_ptr[t];
     uint8_t *Cw = C + int64_t(t) * G * OB;
-    const int m0 = mb * Tw8Cfg::BM;
+    const int m0 = mb * CF::BM;
+    // (a tile of at most GMAX columns has at most GMAX/16 column blocks)
     switch ((nt + 15) >> 4) {
-#define TW8_CASE(J) \
-    case J: tw8_item<J, EPI>(smem, At, vt, offset_k + kp0, offset_n + np0, scale, bias, kt, nt, t, G, m0, Cw, M, N); break;
+#define TW8_CASE(J)                                                                                               \
+    case J:                                                                                                       \
+        if constexpr (J <= CF::GMAX / 16)                                                                         \
+            tw8_item<CF, J, EPI, KGATH>(smem, At, vt, offset_k + kp0, offset_n + np0, scale, bias, kt, nt, t, G, \
+                                        m0, Cw, M, N);                                                            \
+        break;
         TW8_CASE(0) TW8_CASE(1) TW8_CASE(2) TW8_CASE(3) TW8_CASE(4) TW8_CASE(5) TW8_CASE(6) TW8_CASE(7) TW8_CASE(8)
+        TW8_CASE(9) TW8_CASE(10) TW8_CASE(11) TW8_CASE(12) TW8_CASE(13) TW8_CASE(14) TW8_CASE(15) TW8_CASE(16)
 #undef TW8_CASE
         default: break;
     }
+}
+
+// Tiles up to 128 columns: 52 KiB of LDS and at most 85 VGPRs, three
+// workgroups per CU.  Wider tiles (up to 256 columns): 78 KiB, two per CU.
+using Tw8Prod = Tw8Cfg<128, 6>;
+using Tw8Wide = Tw8Cfg<256, 4>;
+
+template <class CF, bool KGATH>
+hipError_t launch_i8_cfg(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
+                         const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr, const int32_t *tile_order,
+                         int T, int G, const float *scale, const float *bias, void *C, int out, int M, int N,
+                         hipStream_t st) {
+    const int n_mb = (M + CF::BM - 1) / CF::BM;
+    auto kern = out == OUT_I32 ? tw_gemm_i8_kernel<CF, OUT_I32, KGATH>
+              : out == OUT_F32 ? tw_gemm_i8_kernel<CF, OUT_F32, KGATH>
+              : out == OUT_F16 ? tw_gemm_i8_kernel<CF, OUT_F16, KGATH>
+                               : tw_gemm_i8_kernel<CF, OUT_I8, KGATH>;
+    hipLaunchKernelGGL(kern, dim3(n_mb * T), dim3(CF::NT), 0, st, static_cast<const int8_t *>(At),
+                       static_cast<const int8_t *>(vals), offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G,
+                       scale, bias, static_cast<uint8_t *>(C), M, N);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -292,15 +355,19 @@ hipError_t launch_tw_i8(const void *At, const void *vals, const int32_t *offset_
                         const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr, const int32_t *tile_order,
                         int T, int G, const float *scale, const float *bias, void *C, int out, int M, int N,
                         hipStream_t st) {
-    const int n_mb = (M + Tw8Cfg::BM - 1) / Tw8Cfg::BM;
-    auto kern = out == OUT_I32 ? tw_gemm_i8_kernel<OUT_I32>
-              : out == OUT_F32 ? tw_gemm_i8_kernel<OUT_F32>
-              : out == OUT_F16 ? tw_gemm_i8_kernel<OUT_F16>
-                               : tw_gemm_i8_kernel<OUT_I8>;
-    hipLaunchKernelGGL(kern, dim3(n_mb * T), dim3(Tw8Cfg::NT), 0, st, static_cast<const int8_t *>(At),
-                       static_cast<const int8_t *>(vals), offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G,
-                       scale, bias, static_cast<uint8_t *>(C), M, N);
-    return hipGetLastError();
+    const bool gath = M % 16 != 0;
+    if (G > Tw8Prod::GMAX) {
+        if (gath)
+            return launch_i8_cfg<Tw8Wide, true>(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G,
+                                                scale, bias, C, out, M, N, st);
+        return launch_i8_cfg<Tw8Wide, false>(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G,
+                                             scale, bias, C, out, M, N, st);
+    }
+    if (gath)
+        return launch_i8_cfg<Tw8Prod, true>(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G,
+                                            scale, bias, C, out, M, N, st);
+    return launch_i8_cfg<Tw8Prod, false>(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, T, G, scale,
+                                         bias, C, out, M, N, st);
 }
 
 }  // namespace ssg

@@ -76,12 +76,12 @@ def has_device(lib):
     (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 1, 2, 0, _p(16), 8, 32, 64, None), "tile range"),
     (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 0, 0, _p(16), 8, 32, 64, None), "tile range"),
     (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 2, 4, _p(16), 8, 32, 64, None), "unknown flags"),
-    (lambda r: r.tw_gemm_i8(*[_p(16)] * 8, 2, 16, _p(16), None, _p(16), 2, 24, 32, 64, None), "multiple of 16"),
+    (lambda r: r.tw_gemm_i8(*[_p(16)] * 8, 2, 272, _p(16), None, _p(16), 2, 24, 544, 64, None), "at most 256"),
     (lambda r: r.tw_gemm_i8(*[_p(16)] * 8, 2, 16, None, None, _p(16), 2, 32, 32, 64, None), "needs scale"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 24, _p(16), 8, 48, 64, None), "G=24"),
-    (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 256, _p(16), 8, 512, 64, None), "at most 128"),
+    (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 272, _p(16), 8, 544, 64, None), "at most 256"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 3, 16, _p(16), 8, 32, 64, None), "T=3"),
-    (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 16, _p(16), 12, 32, 64, None), "multiple of 8"),
+    (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 16, _p(16), -3, 32, 64, None), "bad shape"),
     (lambda r: r.ssg_transpose_f16(_p(16), _p(16), 12, 16, None), "multiples of 8"),
     (lambda r: r.w24_gemm_f16_splitk(*[_p(16)] * 4, 8, 64, 128, 3, _p(16), 1 << 20, None), "splits=3"),
     (lambda r: r.w24_gemm_f16_splitk(*[_p(16)] * 4, 8, 64, 128, 0, _p(16), 1 << 20, None), "splits=0"),

@@ -560,6 +560,53 @@ def test_tw_multi_stream_schedule(lib, gpu):
     check_f16_exact(H(lib.tw_gemm_f16_streams(Atx, px, streams)), ex["A"], ex["Wp"], "tw streams exact")
 
 
+# ---------------------------------------------------------------- tile-wise limits: any M >= 1, tiles up to 256 columns
+# (M, K, N, G, densities): token counts that are not multiples of 8 or 16 (the
+# K-major At is then gathered through registers) and 256-column tiles (the
+# wide configuration), alone and together
+TW_LIMITS = [(1, 256, 512, 256, [0.3, 0.7]), (17, 300, 256, 128, [0.5, 0.2]),
+             (129, 512, 768, 256, [0.1, 0.4, 1.0]), (7, 64, 64, 32, [0.5, 1.0]),
+             (200, 384, 512, 256, [0.25, 0.9]), (136, 200, 512, 256, [0.6, 0.0])]
+
+
+def _at(A):
+    return T(np.ascontiguousarray(A.T))
+
+
+@pytest.mark.parametrize("M,K,N,G,d", TW_LIMITS)
+def test_tw_limits_f16(lib, gpu, M, K, N, G, d):
+    import torch
+    case = wl.random_tw_f16(np.random.default_rng(M * 3 + K + G), M, K, N, G, d)
+    packed = lib.tw_pack_f16(case["Wp"], G).to("cuda")
+    At = _at(case["A"])
+    C = H(lib.tw_gemm_f16(At, packed, out=torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")))
+    check_f16(C, case["A"], case["Wp"], tw_terms(case["Wp"], G), f"tw {M}x{K}x{N} G={G}")
+    Ct = H(lib.tw_gemm_f16_ex(At, packed, out_t=True,
+                              out=torch.full((N, M), float("nan"), dtype=torch.float16, device="cuda")))
+    assert np.array_equal(Ct.T.view(np.uint16), C.view(np.uint16))
+    Cr = H(lib.tw_gemm_f16_ex(T(case["A"]), packed, a_rowmajor=True))
+    assert np.array_equal(Cr.view(np.uint16), C.view(np.uint16))
+    ex = wl.exact_int_tw_f16(np.random.default_rng(M + G), M, K, N, G, d)
+    px = lib.tw_pack_f16(ex["Wp"], G).to("cuda")
+    check_f16_exact(H(lib.tw_gemm_f16(_at(ex["A"]), px)), ex["A"], ex["Wp"], f"tw exact {M}x{K}x{N} G={G}")
+    check_f16_exact(H(lib.tw_gemm_f16_ex(_at(ex["A"]), px, out_t=True)).T.copy(), ex["A"], ex["Wp"],
+                    f"tw exact transposed out {M}x{K}x{N} G={G}")
+
+
+@pytest.mark.parametrize("out", ["i32", "f16", "i8"])
+@pytest.mark.parametrize("M,K,N,G,d", TW_LIMITS)
+def test_tw_limits_i8(lib, gpu, M, K, N, G, d, out):
+    rng = np.random.default_rng(M * 5 + K + G)
+    case = wl.random_tw_i8(rng, M, K, N, G, d)
+    scale = {"i32": None, "f16": case["scale"] * np.float32(20.0),
+             "i8": rng.uniform(2e-4, 2e-3, size=N).astype(np.float32)}[out]
+    bias = None if out == "i32" else rng.normal(0, 3.0, size=N).astype(np.float32)
+    C = run_tw_i8(lib, case["A"], case["Wp"], G, scale, bias, out)
+    ref = oracle.ref_gemm_i8_out(case["A"], case["Wp"], scale, bias, out)
+    bad = np.flatnonzero(_bits(C) != _bits(ref))
+    assert bad.size == 0, f"{bad.size} mismatches, first at {np.unravel_index(bad[0], C.shape)}"
+
+
 # ---------------------------------------------------------------- transpose, determinism, errors
 @pytest.mark.parametrize("M,K", [(8, 8), (136, 200), (4096, 768), (1000, 1024)])
 def test_transpose_bit_exact(lib, gpu, M, K):
