@@ -276,6 +276,22 @@ int w24_gemm_i8_splitk(const int8_t *A, const int8_t *vals, const uint32_t *meta
                        const float *bias, void *C, int32_t out_type, int64_t M, int64_t N, int64_t K,
                        int32_t splits, void *ws, int64_t ws_bytes, void *stream);
 
+/* Allocation-free variant of w24_gemm_f16_splitk, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The partial
+ * accumulators go to a static device array of SSG_STATIC_SCRATCH_BYTES
+ * (32 MiB) that the library holds on every GPU it runs on until the process
+ * ends; the call itself allocates nothing.  Arguments, results and errors as
+ * w24_gemm_f16_splitk, without ws / ws_bytes; splits * M * N * 4 above the
+ * scratch size is SSG_EINVAL.  Every call on one GPU shares that GPU's
+ * scratch: calls that may overlap in time on one GPU (different streams,
+ * or threads) race and must be ordered by the caller; calls on one stream
+ * are ordered by the stream.  The scratch needs no clearing: each split
+ * writes its whole slice before the reduction reads it. */
+#define SSG_STATIC_SCRATCH_BYTES (32 << 20)
+int w24_gemm_f16_splitk_static(const void *A, const void *vals, const uint32_t *meta, void *C,
+                               int64_t M, int64_t N, int64_t K, int32_t splits, void *stream);
+
 /* Tile-wise GEMM, fp16 in, fp32 accumulate, fp16 out.  At is A stored
  * K-major ([K][M], M contiguous) so that the rows picked by offset_k are
  * contiguous reads (the tile-wise slides transpose A to avoid uncoalesced

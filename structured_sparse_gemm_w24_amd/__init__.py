@@ -38,6 +38,8 @@ from ._lib import (  # noqa: F401
     w24_gemm_f16_splitk,
     dense_gemm_i8_splitk,
     w24_gemm_i8_splitk,
+    w24_gemm_f16_splitk_static,
+    SSG_STATIC_SCRATCH_BYTES,
     splitk_suggest,
     tile_choice,
     splitk_workspace_bytes,

@@ -67,6 +67,7 @@ SIGNATURES = {
     "w24_gemm_f16_splitk": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _I64, _P],
     "dense_gemm_i8_splitk": [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _I64, _P],
     "w24_gemm_i8_splitk": [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _I64, _P],
+    "w24_gemm_f16_splitk_static": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P],
     "ssg_splitk_suggest": [_I32, _I64, _I64, _I64],
     "ssg_tile_choice": [_I32, _I64, _I64, _I64],
 }
@@ -506,6 +507,26 @@ def dense_gemm_f16_splitk(A, Wt, splits, workspace=None, out=None):
 def w24_gemm_f16_splitk(A, vals, meta, splits, workspace=None, out=None):
     """w24_gemm_f16 with K split `splits` ways (see dense_gemm_f16_splitk)."""
     return w24_gemm_f16(A, vals, meta, out=out, splits=splits, workspace=workspace)
+
+
+SSG_STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def w24_gemm_f16_splitk_static(A, vals, meta, splits, out=None):
+    """w24_gemm_f16_splitk without a workspace: the partials go to the library's
+    static per-GPU scratch (splits * M * N * 4 <= SSG_STATIC_SCRATCH_BYTES).
+    Calls that may overlap on one GPU race on that scratch."""
+    torch = _torch()
+    M, K = A.shape
+    N = vals.shape[0]
+    _dev(A, torch.float16, (M, K), "A")
+    _dev(vals, torch.float16, (N, K // 2), "vals")
+    _dev(meta, torch.int32, (N, -(-K // 32)), "meta")
+    C = _out(out, (M, N), torch.float16, A)
+    with _on(A, vals, meta, C):
+        _check(load().w24_gemm_f16_splitk_static(_ptr(A), _ptr(vals), _ptr(meta), _ptr(C), M, N, K, int(splits),
+                                                 _stream(A)))
+    return C
 
 
 def dense_gemm_i8_splitk(A, Wt, scale, bias=None, out_type="f16", splits=1, workspace=None, out=None):

@@ -243,6 +243,66 @@ SSG_API int w24_gemm_i8_splitk(const int8_t *A, const int8_t *vals, const uint32
                      stream);
 }
 
+// ---- allocation-free split K.  The partial accumulators live in a
+// file-scope device array (one copy per GPU, allocated with the code object
+// when the library's kernels are first loaded on that GPU and held until the
+// process ends).  In host code `scratch` names a host-side stand-in, so its
+// device address is looked up once per device with hipGetSymbolAddress and
+// only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[SSG_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {nullptr};
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with the device current).
+int scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return ssg::fail(SSG_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return ssg::fail(SSG_ENODEV, "device id %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return ssg::fail(SSG_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return SSG_OK;
+}
+
+}  // namespace
+
+SSG_API int w24_gemm_f16_splitk_static(const void *A, const void *vals, const uint32_t *meta, void *C, int64_t M,
+                                       int64_t N, int64_t K, int32_t splits, void *stream) {
+    const char *fn = "w24_gemm_f16_splitk_static";
+    // shapes first (so the byte count below cannot overflow), then the scratch limit
+    int rc = check_gemm(fn, A, vals, C, M, N, K, 64, 64);
+    if (rc) return rc;
+    const int stages = ssg::gemm_k_stages(1, int(K));
+    if (splits < 1 || splits > 64 || stages % splits)
+        return ssg::fail(SSG_EINVAL, "%s: splits=%d must be in 1..64 and divide the %d K stages", fn, int(splits),
+                         stages);
+    if (splits > 1 && M > 0) {
+        const int64_t per_split = M * N * 4;  // M, N < 2^31 and M * N / 4096 < 2^31
+        if (per_split > int64_t(SSG_STATIC_SCRATCH_BYTES) / splits)
+            return ssg::fail(SSG_EINVAL, "%s: splits * M * N * 4 = %d * %lld bytes exceeds the %d-byte static "
+                             "scratch (use w24_gemm_f16_splitk with a workspace)", fn, int(splits),
+                             (long long)per_split, int(SSG_STATIC_SCRATCH_BYTES));
+    }
+    void *ws = nullptr;
+    if (splits > 1 && M > 0) {
+        if ((rc = check_device())) return rc;
+        if ((rc = scratch_address(&ws))) return rc;
+    }
+    return split_run(fn, 1, A, vals, meta, nullptr, nullptr, C, 0, M, N, K, splits, ws,
+                     int64_t(SSG_STATIC_SCRATCH_BYTES), stream);
+}
+
 namespace {
 
 int tw_run(const char *fn, const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,

@@ -82,6 +82,9 @@ def has_device(lib):
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 272, _p(16), 8, 544, 64, None), "at most 256"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 3, 16, _p(16), 8, 32, 64, None), "T=3"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 16, _p(16), -3, 32, 64, None), "bad shape"),
+    (lambda r: r.w24_gemm_f16_splitk_static(*[_p(16)] * 4, 4096, 1024, 4096, 8, None), "static scratch"),
+    (lambda r: r.w24_gemm_f16_splitk_static(*[_p(16)] * 4, 8, 64, 128, 3, None), "splits=3"),
+    (lambda r: r.w24_gemm_f16_splitk_static(*[_p(16)] * 4, 8, 64, 128, 0, None), "splits=0"),
     (lambda r: r.ssg_transpose_f16(_p(16), _p(16), 12, 16, None), "multiples of 8"),
     (lambda r: r.w24_gemm_f16_splitk(*[_p(16)] * 4, 8, 64, 128, 3, _p(16), 1 << 20, None), "splits=3"),
     (lambda r: r.w24_gemm_f16_splitk(*[_p(16)] * 4, 8, 64, 128, 0, _p(16), 1 << 20, None), "splits=0"),
