@@ -78,10 +78,22 @@ def lib_path():
 
 
 def load():
-    """Load libssg.so once (raises if it has not been built)."""
+    """Load libssg.so once (raises if it has not been built).
+
+    torch (which holds the device memory and streams of the GEMM calls) is
+    imported first when it is installed: its wheel carries its own HIP
+    runtime, and the library then binds to that one instead of loading the
+    system runtime beside it.  Two HIP runtimes initialised in one process
+    leave the second without a device (the library's calls fail with
+    SSG_ENODEV, or torch reports no GPU), which is what happens when the
+    library is loaded before torch."""
     global _LIB
     with _LOCK:
         if _LIB is None:
+            try:
+                import torch  # noqa: F401
+            except ImportError:
+                pass
             path = lib_path()
             if not os.path.exists(path):
                 raise RuntimeError(f"{path} is missing: build it with "

@@ -26,7 +26,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.
+# -ffp-contract=off: the int8 epilogues compute float(acc) * scale, then
+# + bias, each rounded on its own; HIP's __fmul_rn / __fadd_rn are plain
+# operators, which the default contraction may fuse into one multiply-add
+# (one rounding), changing results at fp16 / int8 rounding boundaries.
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+             "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra"]

@@ -248,3 +248,17 @@ def test_vendor_baseline_is_outside_the_product():
             continue  # the build step is what builds the separate bench library
         text = open(path, errors="replace").read()
         assert "libssg_vendor" not in text and "hipsparselt" not in text.lower(), path
+
+
+def test_single_hip_runtime_after_load():
+    """Loading the library (before anything touched torch) leaves one HIP
+    runtime in the process: the binding imports torch first, so the library
+    binds to the runtime torch carries instead of loading a second one."""
+    import subprocess
+    import sys
+    code = ("import structured_sparse_gemm_w24_amd as s; s.load(); "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert out.returncode == 0, out.stderr
+    libs = eval(out.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1, libs

@@ -44,20 +44,43 @@ def _kernels(asm):
 
 
 @pytest.fixture(scope="module")
-def kernels():
+def assembly():
+    """source -> gfx950 assembly, compiled with the library's own flags."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    found = {}
+    from structured_sparse_gemm_w24_amd.build import HIP_FLAGS
+    flags = [f for f in HIP_FLAGS if f not in ("-fPIC", "-fvisibility=hidden")]
+    asm = {}
     with tempfile.TemporaryDirectory() as d:
         for src in SOURCES:
             out = os.path.join(d, src + ".s")
-            cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
-                   "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                   "-Wno-unused-command-line-argument", os.path.join(KDIR, src), "-o", out]
+            cmd = [HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(KDIR, src), "-o", out]
             p = subprocess.run(cmd, capture_output=True, text=True)
             assert p.returncode == 0, p.stderr
-            found.update(_kernels(open(out).read()))
+            asm[src] = open(out).read()
+    return asm
+
+
+@pytest.fixture(scope="module")
+def kernels(assembly):
+    found = {}
+    for text in assembly.values():
+        found.update(_kernels(text))
     return found
+
+
+def test_no_fused_multiply_add(assembly):
+    """The epilogues round the product and the sum separately (float(acc) *
+    scale, then + bias): no fp32 fused multiply-add may appear, except the
+    compiler's own 64-bit integer division sequence (the 2^32 scalings)."""
+    fma = re.compile(r"^\s*(v_(pk_)?fma(c|mk|ak)?_f32\S*|v_ma[cd]_f32\S*|v_fma_mix\S*)\s+(.*)$", re.M)
+    bad = {}
+    for src, text in assembly.items():
+        hits = [m.group(0).strip() for m in fma.finditer(text)
+                if "0x4f800000" not in m.group(4) and "0xcf800000" not in m.group(4)]
+        if hits:
+            bad[src] = hits[:3]
+    assert bad == {}
 
 
 def test_every_kernel_was_found(kernels):
