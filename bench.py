@@ -41,6 +41,8 @@ METRIC = "effective TFLOPS/TOPS of sparse GEMM + speedup vs dense MFMA GEMM, sam
 # (every replay a timed region of exactly K steps); medians are reported.
 HEADLINE_ROUNDS = 25
 HEADLINE_WARM_S = 1.5
+# table mode: each graph replays this long (untimed) before its 5 timed replays
+TABLE_WARM_S = 0.3
 CACHE_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w24_gemm_i8_vit_base_fc1.txt")
 
@@ -95,10 +97,11 @@ class Timer:
     Python.  `reps` replays are timed one by one; the call returns the median
     per-step time and `stats` also gives p10 / p90 over the replays."""
 
-    def __init__(self, torch, graph=True, reps=1):
+    def __init__(self, torch, graph=True, reps=1, warm_s=0.0):
         self.torch = torch
         self.graph = graph
         self.reps = reps
+        self.warm_s = warm_s  # untimed replays of the graph, in seconds, before the timed ones
 
     def __call__(self, fn, steps, warmup):
         return self.stats(fn, steps, warmup)["ms"]
@@ -122,6 +125,11 @@ class Timer:
             torch.cuda.current_stream().wait_stream(stream)
             g.replay()  # warm replay
             torch.cuda.synchronize()
+            # the shader clock is power-managed: keep the GPU busy until it settles
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < self.warm_s:
+                g.replay()
+                torch.cuda.synchronize()
             for _ in range(reps):
                 s.record()
                 g.replay()
@@ -1037,6 +1045,7 @@ def table(a, torch, ssg, perf, wl, timer):
     steps, warmup = a.steps, a.warmup
     want = set(a.workloads.split(",")) if a.workloads else set(WORKLOADS)
     timer.reps = 5
+    timer.warm_s = TABLE_WARM_S
 
     vendor = not a.no_vendor
 

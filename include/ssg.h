@@ -260,8 +260,11 @@ int32_t ssg_splitk_suggest(int32_t kind, int64_t M, int64_t N, int64_t K);
  * has fewer than 64 stages (64 K elements per stage for fp16, 128 for int8),
  * else 64 x 64 (64 x 128 for the fp16 kinds when 64 x 64 tiles would
  * outnumber the 256 CUs);
- * otherwise 128 x 128 or 128 x 256.  Host-only; 0 for an invalid kind or
- * shape. */
+ * otherwise 128 x 128 or 128 x 256.  This is the tile of the unsplit launch
+ * (the plain GEMM calls, and the *_splitk calls with splits == 1); a split
+ * launch of the fp16 kinds may take 128 x 128 (8 splits) or 64 x 128 (4
+ * splits) tiles instead, as ssg_splitk_suggest describes.  Host-only; 0 for
+ * an invalid kind or shape. */
 int32_t ssg_tile_choice(int32_t kind, int64_t M, int64_t N, int64_t K);
 
 int dense_gemm_f16_splitk(const void *A, const void *Wt, void *C, int64_t M, int64_t N, int64_t K,
