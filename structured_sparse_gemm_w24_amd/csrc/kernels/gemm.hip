@@ -24,6 +24,12 @@
 //     fetched while stage s+1 is read into registers and stage s feeds the
 //     matrix cores.  One explicit wait on the vector-memory counter plus one
 //     barrier per stage hand a stage over;
+//   * the sparse kinds' metadata either travels with each stage or, on the
+//     tiles that use it, is fetched in blocks of several stages into a ring
+//     of its own (fewer, longer row segments per load);
+//   * on some tiles (SmallP, the sparse T64N) a second group of waves does
+//     all the loading and the compute waves only read LDS and issue matrix
+//     instructions; both groups meet at the same per-stage barrier;
 //   * fragments are double-buffered in registers: the LDS reads of the next
 //     k-step are issued between the matrix instructions of the current one
 //     (scheduling hints interleave them), so one wave per SIMD keeps its
@@ -190,37 +196,58 @@ __device__ __forceinline__ void store16(void *p, u32x4 v) {
 // throughput is limited per wavefront (about 4 bytes per clock each on
 // gfx950), so a CU needs 8 or more issuing waves to feed the sparse matrix
 // cores.
-template <int WM_, int WN_, int TM_, int TN_, int STAGES_, int GM_, bool NTS_, bool ROT_>
+// MP: K stages per metadata block of the sparse kinds (0: each stage's
+// metadata travels with the stage).  PROD: the workgroup has as many
+// loader waves as compute waves; the loader waves issue every direct-to-LDS
+// load and the compute waves only read LDS and run the matrix instructions.
+template <int WM_, int WN_, int TM_, int TN_, int STAGES_, int GM_, bool NTS_, bool ROT_, int MP_ = 0,
+          bool PROD_ = false>
 struct Cfg {
     static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_, STAGES = STAGES_, GM = GM_;
-    static constexpr bool NTS = NTS_, ROT = ROT_;
+    static constexpr bool NTS = NTS_, ROT = ROT_, PROD = PROD_;
+    static constexpr int MP = MP_;
 };
 
 template <int KIND, class CF>
 struct Layout {
     using KT = KindTraits<KIND>;
-    static constexpr int NW = CF::WM * CF::WN;  // waves
-    static constexpr int NT = NW * kWave;
+    static constexpr int NW = CF::WM * CF::WN;           // compute waves (and loader waves)
+    static constexpr int NT = NW * kWave * (CF::PROD ? 2 : 1);  // threads
     static constexpr int BM = CF::WM * CF::TM * 32;
     static constexpr int BN = CF::WN * CF::TN * 32;
     static constexpr int WB = KT::kWB;
     static constexpr int MW = KT::kMW;
     static constexpr int A_STAGE = BM * 128;
     static constexpr int W_STAGE = BN * WB;
-    static constexpr int M_STAGE = BN * MW * 4;
+    static constexpr int M_BYTES = BN * MW * 4;  // metadata bytes of one stage
+    // Metadata blocks (MP > 0): the metadata of MP consecutive stages sits
+    // in one block of its own ring instead of in the stage buffers, stored
+    // row-major [BN][MP * MW] words, so that every 256-byte load covers
+    // MP * MW * 4 contiguous bytes of a row (8 rows) rather than 8 or 16
+    // bytes of 32 or 16 rows: the loads touch MP times fewer cache lines.
+    // A block is fetched in MP parts, one with each of the MP stage loads
+    // before its first stage; MSLOTS blocks are kept so that a part never
+    // overwrites a block that a stage still in the ring reads.
+    static constexpr int MP = KT::kSparse ? CF::MP : 0;
+    static constexpr int M_STAGE = MP ? 0 : M_BYTES;
     static constexpr int STAGE = A_STAGE + W_STAGE + M_STAGE;
+    static constexpr int RW = MP * MW;  // words per row in a block
+    static constexpr int MBLK = MP * M_BYTES;
+    static constexpr int MSLOTS = MP ? 2 + (CF::STAGES - 2 + MP - 1) / MP : 0;
+    static constexpr int MRING = MSLOTS * MBLK;
+    static_assert(MP == 0 || (64 % RW == 0 && BN % MP == 0), "metadata block shape");
     // direct-to-LDS instructions per wave per stage (each moves 1 KiB, or
     // 256 bytes for the 4-byte meta loads).  A 64-channel fp16 tile has 2
     // meta chunks of 256 bytes for 4 waves: then waves w and w + MCH load the
     // same chunk into the same LDS bytes (identical data), so that every wave
     // issues the same number of loads per stage and one counter value means
     // "stage complete" for all of them.
-    static constexpr int MCH = M_STAGE / 256;
+    static constexpr int MCH = M_BYTES / 256;
     static constexpr int LA = A_STAGE / 1024 / NW;
     static constexpr int LW = W_STAGE / 1024 / NW;
     static constexpr int LM = MCH >= NW ? MCH / NW : (MCH > 0 ? 1 : 0);
     static constexpr int L = LA + LW + LM;
-    static_assert(LA * NW * 1024 == A_STAGE && LW * NW * 1024 == W_STAGE && MCH * 256 == M_STAGE &&
+    static_assert(LA * NW * 1024 == A_STAGE && LW * NW * 1024 == W_STAGE && MCH * 256 == M_BYTES &&
                       (MCH == 0 || MCH % NW == 0 || NW % MCH == 0),
                   "stage does not split evenly over the waves");
     // meta chunk of this wave's j-th meta load (no modulo unless chunks are
@@ -230,10 +257,15 @@ struct Layout {
         if constexpr (MCH >= NW) return j * NW + wave;
         else return wave % (MCH > 0 ? MCH : 1);
     }
+    // word position of (row, w) inside a metadata block: XOR-swizzled so that
+    // the 32 rows of one fragment read fall into distinct banks
+    static __device__ __forceinline__ int mword(int row, int w) {
+        return row * RW + (w ^ ((row * RW / 32) & (RW - 1)));
+    }
 };
 
 template <int KIND, int EPI, class CF>
-__global__ void __launch_bounds__(CF::WM *CF::WN * 64)
+__global__ void __launch_bounds__(CF::WM *CF::WN * 64 * (CF::PROD ? 2 : 1))
 gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const uint32_t *__restrict__ meta,
             const float *__restrict__ scale, const float *__restrict__ bias, void *__restrict__ C, int M, int N,
             int K, int stages) {
@@ -251,13 +283,18 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     constexpr int EWAVE = 32 * EROW;
     constexpr int EPASS = (TM * EWAVE * LY::NW <= CF::STAGES * STAGE) ? TM : 1;
     constexpr int SMEM_EPI = EPASS * EWAVE * LY::NW;
-    constexpr int SMEM = (CF::STAGES * STAGE > SMEM_EPI) ? CF::STAGES * STAGE : SMEM_EPI;
+    constexpr int SMEM_MAIN = CF::STAGES * STAGE + LY::MRING;
+    constexpr int SMEM = (SMEM_MAIN > SMEM_EPI) ? SMEM_MAIN : SMEM_EPI;
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // With loader waves (PROD), waves NW.. load and waves 0..NW-1 compute;
+    // `wave` is a wave's index within its group.
+    constexpr bool PROD = CF::PROD;
+    const bool loader = PROD && (tid >> 6) >= LY::NW;
+    const int wave = loader ? (tid >> 6) - LY::NW : tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
     const int h = lane >> 5, r = lane & 31;
 
@@ -309,6 +346,7 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
         const int row = word / (MW > 0 ? MW : 1), w = word % (MW > 0 ? MW : 1);
         om[j] = (uint32_t(min(n0 + row, N - 1)) * uint32_t(m_row) + w) * 4;
     }
+    constexpr int RW = LY::MP ? LY::RW : 1;
     const uint8_t *meta_b = reinterpret_cast<const uint8_t *>(meta);
 
     // Where a tile starts its K loop.  From stage 0, the tiles in flight on an
@@ -324,6 +362,30 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     const __amdgpu_buffer_rsrc_t bufA = buffer_of(A, uint32_t(int64_t(M) * a_row));
     const __amdgpu_buffer_rsrc_t bufW = buffer_of(Wv, uint32_t(int64_t(N) * w_row));
     const __amdgpu_buffer_rsrc_t bufM = buffer_of(meta_b, KT::kSparse ? uint32_t(int64_t(N) * m_row * 4) : 0u);
+    // Part t - (c - 1) * MP - 1 of metadata block c = ceil(t / MP), loaded
+    // with the loads of stage t (t < 0: the prologue's parts of block 0).
+    // Each part is MCH 256-byte chunks, BN / MP rows.  Lane's word is (row,
+    // stored position p) of the block; it holds word w = p ^ swizzle of the
+    // row's metadata for block stage q = w / MW, i.e. local stage c * MP + q
+    // (past the last stage: any valid word, never read).
+    auto issue_meta = [&](int t) {
+        if constexpr (LY::MP > 0) {
+            constexpr int MPr = LY::MP > 0 ? LY::MP : 1;
+            const int c = (t + MPr - 1) / MPr;  // ceil(t / MP); t + MP - 1 >= 0
+            const int part = t - (c * MPr - MPr + 1);
+            uint8_t *blk = smem + NB * STAGE + (c % LY::MSLOTS) * LY::MBLK;
+#pragma unroll
+            for (int j = 0; j < LY::LM; ++j) {
+                const int row = (part * LY::MCH + LY::mchunk(j, wave)) * (64 / RW) + lane / RW;
+                const int w = (lane % RW) ^ ((row * RW / 32) & (RW - 1));
+                const int sl = min(c * MPr + w / MW, S - 1);
+                const int sg = ks0 + ((sl + rot < S) ? sl + rot : sl + rot - S);
+                const uint32_t off =
+                    (uint32_t(min(n0 + row, N - 1)) * uint32_t(m_row) + uint32_t(sg * MW + w % MW)) * 4;
+                dma4(bufM, off, blk + (part * LY::MCH + LY::mchunk(j, wave)) * 256);
+            }
+        }
+    };
     auto issue = [&](int s) {
         uint8_t *base = smem + (s % NB) * STAGE;
         const int sg = ks0 + ((s + rot < S) ? s + rot : s + rot - S);  // global K stage
@@ -332,9 +394,13 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
 #pragma unroll
         for (int j = 0; j < LY::LW; ++j)
             dma16(bufW, ow[j] + uint32_t(sg * WB), base + A_STAGE + (j * LY::NW + wave) * 1024);
+        if constexpr (LY::MP == 0) {
 #pragma unroll
-        for (int j = 0; j < LY::LM; ++j)
-            dma4(bufM, om[j] + uint32_t(sg * MW * 4), base + A_STAGE + W_STAGE + LY::mchunk(j, wave) * 256);
+            for (int j = 0; j < LY::LM; ++j)
+                dma4(bufM, om[j] + uint32_t(sg * MW * 4), base + A_STAGE + W_STAGE + LY::mchunk(j, wave) * 256);
+        } else {
+            issue_meta(s);
+        }
     };
 
     // Fragments of one k-step (one matrix instruction deep) for the wave's
@@ -348,11 +414,17 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
         const uint8_t *bA = smem + (s % NB) * STAGE;
         const uint8_t *bW = bA + A_STAGE;
         const uint32_t *bM = reinterpret_cast<const uint32_t *>(bA + A_STAGE + W_STAGE);
+        constexpr int MPr = LY::MP > 0 ? LY::MP : 1;
+        const uint32_t *bB =
+            reinterpret_cast<const uint32_t *>(smem + NB * STAGE + ((s / MPr) % (LY::MP ? LY::MSLOTS : 1)) * LY::MBLK);
+        const int q = (s % MPr) * MW;  // first word of stage s in a block row
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
             const int row = wn * TN * 32 + tn * 32 + r;
             F.w[tn] = lds16(bW + row * WB + swzw<WB>(row, 2 * kk + h) * 16);
-            if constexpr (KIND == W24_F16) F.idx[tn] = bM[row * MW + kk] >> (16 * h);
+            if constexpr (LY::MP > 0 && KIND == W24_F16) F.idx[tn] = bB[LY::mword(row, q + kk)] >> (16 * h);
+            else if constexpr (LY::MP > 0 && KIND == W24_I8) F.idx[tn] = bB[LY::mword(row, q + 2 * kk + h)];
+            else if constexpr (KIND == W24_F16) F.idx[tn] = bM[row * MW + kk] >> (16 * h);
             else if constexpr (KIND == W24_I8) F.idx[tn] = bM[row * MW + 2 * kk + h];
             else F.idx[tn] = 0;
         }
@@ -401,41 +473,56 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     // instructions; the stage hand-off (wait + barrier) sits before the last
     // k-step's instructions so that the next stage's first fragments overlap
     // them too.
+    if (!PROD || loader) {
+        if constexpr (LY::MP > 1)
+            for (int t = 1 - LY::MP; t < 0; ++t) issue_meta(t);
 #pragma unroll
-    for (int s = 0; s < NB; ++s)
-        if (s < S) issue(s);
+        for (int s = 0; s < NB; ++s)
+            if (s < S) issue(s);
+    }
     if (NB < S) wait_vm_barrier<(NB - 1) * LY::L>();
     else wait_vm_barrier<0>();
-    Frag F[2];
-    load_frag(0, 0, F[0]);
-
-    // One stage; STEADY: the ring still has a stage to fetch (s + NB < S).
-    // The next stage's first fragments are read unconditionally: on the last
-    // stage this reads a valid, stale buffer whose values are never used.
-    auto stage = [&](int s, auto steady) {
-#pragma unroll
-        for (int kk = 0; kk < KT::kNI; ++kk) {
-            Frag &cur = F[kk & 1];
-            Frag &nxt = F[(kk + 1) & 1];
-            if (kk + 1 < KT::kNI) {
-                load_frag(s, kk + 1, nxt);
-            } else {
-                // stage s is fully in registers; stage s+1 must be complete
-                if constexpr (decltype(steady)::value) {
-                    wait_lgkm_vm_barrier<(NB - 2) * LY::L>();
-                    issue(s + NB);  // reuses stage s's buffer
-                } else {
-                    wait_lgkm_vm_barrier<0>();
-                }
-                load_frag(s + 1, 0, nxt);
-            }
-            mma_frag(cur);
-            interleave();
+    if (loader) {
+        // the same barriers as the compute waves' stages: after the one that
+        // ends stage s, stage s's buffer is free for stage s + NB
+        int s = 0;
+        for (; s + NB < S; ++s) {
+            wait_vm_barrier<(NB - 2) * LY::L>();
+            issue(s + NB);
         }
-    };
-    int s = 0;
-    for (; s + NB < S; ++s) stage(s, std::true_type{});
-    for (; s < S; ++s) stage(s, std::false_type{});
+        for (; s < S; ++s) wait_vm_barrier<0>();
+    } else {
+        Frag F[2];
+        load_frag(0, 0, F[0]);
+
+        // One stage; STEADY: the ring still has a stage to fetch (s + NB < S).
+        // The next stage's first fragments are read unconditionally: on the last
+        // stage this reads a valid, stale buffer whose values are never used.
+        auto stage = [&](int s, auto steady) {
+#pragma unroll
+            for (int kk = 0; kk < KT::kNI; ++kk) {
+                Frag &cur = F[kk & 1];
+                Frag &nxt = F[(kk + 1) & 1];
+                if (kk + 1 < KT::kNI) {
+                    load_frag(s, kk + 1, nxt);
+                } else {
+                    // stage s is fully in registers; stage s+1 must be complete
+                    if constexpr (decltype(steady)::value) {
+                        wait_lgkm_vm_barrier<(NB - 2) * LY::L>();
+                        if constexpr (!PROD) issue(s + NB);  // reuses stage s's buffer
+                    } else {
+                        wait_lgkm_vm_barrier<0>();
+                    }
+                    load_frag(s + 1, 0, nxt);
+                }
+                mma_frag(cur);
+                interleave();
+            }
+        };
+        int s = 0;
+        for (; s + NB < S; ++s) stage(s, std::true_type{});
+        for (; s < S; ++s) stage(s, std::false_type{});
+    }
 
     // ---- epilogue.  Lane (h, r) holds, for 32x32 block (tn, tm) and q = 0..3,
     // channels n = tn*32 + 8q + 4h .. +3 of token m = tm*32 + r.
@@ -495,34 +582,38 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     static_assert(RPI * CPR == kWave, "row segment must tile a wave");
     __syncthreads();  // every wave is done reading the stage buffers
     uint8_t *const Cb = reinterpret_cast<uint8_t *>(C) + (EPI == EPI_PART ? int64_t(blockIdx.y) * M * N * OB : 0);
-    uint8_t *ew = smem + wave * EPASS * EWAVE;
+    uint8_t *ew = smem + wave * EPASS * EWAVE;  // (compute waves)
     const int nw = n0 + wn * TN * 32;  // first channel of the wave
 #pragma unroll
     for (int tp = 0; tp < TM; tp += EPASS) {
+        if (!loader) {
 #pragma unroll
-        for (int e = 0; e < EPASS; ++e) {
-            uint8_t *slab = ew + e * EWAVE + r * EROW;
+            for (int e = 0; e < EPASS; ++e) {
+                uint8_t *slab = ew + e * EWAVE + r * EROW;
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
+                for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int c = tn * 32 + q * 8 + h * 4;
-                    const u32x4 o = convert(acc[tn][tp + e], q, nw + c);
-                    if constexpr (OB == 1) *reinterpret_cast<uint32_t *>(slab + c) = o.x;
-                    else if constexpr (OB == 2) *reinterpret_cast<u32x2 *>(slab + c * 2) = u32x2{o.x, o.y};
-                    else *reinterpret_cast<u32x4 *>(slab + c * 4) = o;
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        const int c = tn * 32 + q * 8 + h * 4;
+                        const u32x4 o = convert(acc[tn][tp + e], q, nw + c);
+                        if constexpr (OB == 1) *reinterpret_cast<uint32_t *>(slab + c) = o.x;
+                        else if constexpr (OB == 2) *reinterpret_cast<u32x2 *>(slab + c * 2) = u32x2{o.x, o.y};
+                        else *reinterpret_cast<u32x4 *>(slab + c * 4) = o;
+                    }
+            }
         }
         __syncthreads();
+        if (!loader) {
 #pragma unroll
-        for (int e = 0; e < EPASS; ++e) {
+            for (int e = 0; e < EPASS; ++e) {
 #pragma unroll
-            for (int i = 0; i < 32 / RPI; ++i) {
-                const int row = i * RPI + lane / CPR, ch = lane % CPR;
-                const int m = m0 + wm * TM * 32 + (tp + e) * 32 + row;
-                const int n = nw + ch * (16 / OB);
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(ew + e * EWAVE + row * EROW + ch * 16);
-                if (m < M && n < N) store16<CF::NTS>(Cb + (int64_t(m) * N + n) * OB, v);
+                for (int i = 0; i < 32 / RPI; ++i) {
+                    const int row = i * RPI + lane / CPR, ch = lane % CPR;
+                    const int m = m0 + wm * TM * 32 + (tp + e) * 32 + row;
+                    const int n = nw + ch * (16 / OB);
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(ew + e * EWAVE + row * EROW + ch * 16);
+                    if (m < M && n < N) store16<CF::NTS>(Cb + (int64_t(m) * N + n) * OB, v);
+                }
             }
         }
         if (tp + EPASS < TM) __syncthreads();
@@ -547,12 +638,34 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 //          many tiles as CUs and K is long enough to amortise the prologue;
 //   Mid    128 x 256, 4 waves, 2 stages (two workgroups per CU) -- short-K
 //          int8 GEMMs with one to two such tiles per CU;
-//   Small  128 x 128, 4 waves, 3 stages (two workgroups per CU) -- narrow
-//          outputs (N = 1024) that would leave CUs idle with big tiles;
+//   Small  128 x 128, 4 waves, 3 stages (two workgroups per CU) -- long-K
+//          int8 GEMMs with more than 256 (dense: 576) such tiles, and the
+//          8-way K splits of few-tile fp16 GEMMs;
+//   SmallP the same tile with 4 more waves that only load (one workgroup
+//          per CU) and, for the sparse kinds, metadata blocks of 4 (fp16) or
+//          2 (int8) stages -- narrow outputs (N = 1024) that would leave CUs
+//          idle with big tiles: every fp16 GEMM without enough Big tiles, and
+//          the long-K int8 ones up to 256 tiles (dense: 576).  Against Small,
+//          graph-timed on cold input sets: fp16 2:4 4096 x 1024 x 4096
+//          (M x N x K) 42.3 -> 38.9 us, 4096 x 768 x 3072 31.5 -> 28.4,
+//          6144 x 1024 x 4096 (384 tiles) 67.6 -> 63.4, 6144 x 1536 x 4096
+//          (576) 96.8 -> 87.0; dense fp16 4096 x 1024 x 4096 43.1 -> 41.5;
+//          int8 2:4 4096 x 768 x 3072 17.5 -> 16.5 us, but 6144 x 1024 x
+//          4096 37.0 -> 39.0.  Neither part pays alone (fp16 2:4 4096 x 1024
+//          x 4096: metadata blocks 46.6-46.9 us, loader waves 45-46, both
+//          41.5, Small 44.7-45.2 in that session): the metadata blocks cut
+//          the cache lines the loads touch (a copy of the kernel without
+//          fragment reads and matrix instructions ran 40.1 -> 34.8 us), and
+//          only with the loads moved off the compute waves does the full
+//          kernel follow;
 //   Small2 128 x 128, 4 waves, 2 stages (three int8 workgroups per CU) --
 //          short-K int8 GEMMs whose Mid tiles would fill the chip more than
 //          twice or less than once, and the dense int8 GEMMs at short K;
 //   T64    64 x 64 and T64N 64 x 128, 4 waves of 32 x 32 / 32 x 64, 3 stages
+//          (the sparse fp16 T64N with 4 loader waves and 4-stage metadata
+//          blocks: 512 x 3072 x 1024 9.6 -> 9.1 us, 512 x 4096 x 1024
+//          10.6 -> 10.0, 2048 x 1024 x 4096 32.0 -> 27.7; the dense one runs
+//          slower so, 10.4 -> 11.0 us at 512 x 3072 x 1024)
 //          -- GEMMs with at most 128 tiles of 128 x 128 (half the CUs; int8
 //          with K <= 1024: 192), e.g. one GPU's share of a token-sharded
 //          layer (M = 512).  With so few
@@ -593,16 +706,20 @@ template <bool NTS>
 using CfgMid = Cfg<2, 2, 2, 4, 2, 8, NTS, false>;
 template <bool NTS, bool ROT>
 using CfgSmall = Cfg<2, 2, 2, 2, 3, 8, NTS, ROT>;
+template <bool NTS, bool ROT, int MP>
+using CfgSmallP = Cfg<2, 2, 2, 2, 3, 8, NTS, ROT, MP, true>;
 template <bool NTS, bool ROT>
 using CfgSmall2 = Cfg<2, 2, 2, 2, 2, 8, NTS, ROT>;
 template <bool NTS, bool ROT>
 using CfgT64 = Cfg<2, 2, 1, 1, 3, 8, NTS, ROT>;
 template <bool NTS, bool ROT>
 using CfgT64N = Cfg<2, 2, 1, 2, 3, 8, NTS, ROT>;
+template <bool NTS, bool ROT>
+using CfgT64NP = Cfg<2, 2, 1, 2, 3, 8, NTS, ROT, 4, true>;
 template <bool NTS>
 using CfgT32 = Cfg<1, 1, 1, 1, 4, 8, NTS, false>;
 
-enum Shape { SHAPE_BIG, SHAPE_MID, SHAPE_SMALL, SHAPE_SMALL2, SHAPE_T64, SHAPE_T64N, SHAPE_T32 };
+enum Shape { SHAPE_BIG, SHAPE_MID, SHAPE_SMALL, SHAPE_SMALLP, SHAPE_SMALL2, SHAPE_T64, SHAPE_T64N, SHAPE_T32 };
 
 static long tiles(int M, int N, int bm, int bn) { return long((M + bm - 1) / bm) * long((N + bn - 1) / bn); }
 
@@ -628,7 +745,7 @@ static Shape pick_f16(int M, int N, int K) {
         if (tiny(M, N, K / 64)) return SHAPE_T32;
         return tiles(M, N, 64, 64) <= 256 ? SHAPE_T64 : SHAPE_T64N;
     }
-    return tiles(M, N, 256, 256) >= 192 ? SHAPE_BIG : SHAPE_SMALL;
+    return tiles(M, N, 256, 256) >= 192 ? SHAPE_BIG : SHAPE_SMALLP;
 }
 
 // int8 kinds.  Short K (<= 1024): the per-tile prologue and the output
@@ -652,7 +769,8 @@ static Shape pick_i8(int M, int N, int K, bool dense) {
         const long mid = tiles(M, N, 128, 256);
         return (mid >= 256 && mid <= 512) ? SHAPE_MID : SHAPE_SMALL2;
     }
-    return tiles(M, N, 256, 256) >= 192 ? SHAPE_BIG : SHAPE_SMALL;
+    if (tiles(M, N, 256, 256) >= 192) return SHAPE_BIG;
+    return tiles(M, N, 128, 128) <= (dense ? 576 : 256) ? SHAPE_SMALLP : SHAPE_SMALL;
 }
 
 template <int KIND, int EPI, bool NTS, bool DENSE>
@@ -671,9 +789,17 @@ static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const ui
         return launch<KIND, EPI, CfgT64<NTS, ROT64>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     }
     if (sh == SHAPE_T32) return launch<KIND, EPI, CfgT32<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
-    if constexpr (!KindTraits<KIND>::kI8)  // (only the fp16 kinds pick T64N)
-        if (sh == SHAPE_T64N)
-            return launch<KIND, EPI, CfgT64N<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
+    if (sh == SHAPE_SMALLP) {
+        constexpr int MP = !KindTraits<KIND>::kSparse ? 0 : KindTraits<KIND>::kI8 ? 2 : 4;
+        return launch<KIND, EPI, CfgSmallP<NTS, ROT, MP>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
+    }
+    if constexpr (!KindTraits<KIND>::kI8) {  // (only the fp16 kinds pick T64N)
+        if (sh == SHAPE_T64N) {
+            if constexpr (KindTraits<KIND>::kSparse)
+                return launch<KIND, EPI, CfgT64NP<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
+            else return launch<KIND, EPI, CfgT64N<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
+        }
+    }
     if constexpr (KindTraits<KIND>::kI8)  // (only the int8 kinds pick Small2)
         if (sh == SHAPE_SMALL2)
             return launch<KIND, EPI, CfgSmall2<NTS, KindTraits<KIND>::kSparse>>(A, Wv, meta, scale, bias, C, M, N, K,

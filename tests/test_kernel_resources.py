@@ -95,7 +95,19 @@ def test_no_kernel_spills_to_scratch(kernels):
     assert {k: v["scratch"] for k, v in kernels.items() if v["scratch"]} == {}
 
 
+# gemm_kernel<KIND, EPI, Cfg<WM, WN, TM, TN, STAGES, GM, NTS, ROT, MP, PROD>>:
+# PROD (a group of loader waves beside the compute waves) is the last argument
+_CFG = re.compile(r"CfgI(?:Li-?\d+E){6}(?:Lb[01]E){2}(?:Li-?\d+E)?(?:Lb([01])E)?E")
+
+
+def _loader_waves(name):
+    m = _CFG.search(name)
+    return bool(m and m.group(1) == "1")
+
+
 def test_registers_never_limit_occupancy_below_lds(kernels):
+    """Tiles with loader waves are meant to run one workgroup per CU (their
+    tile counts are chosen for that); they need registers for one."""
     bad = {}
     for name, v in kernels.items():
         waves = v["wg"] // 64
@@ -105,6 +117,11 @@ def test_registers_never_limit_occupancy_below_lds(kernels):
         # them one by one)
         by_regs = SIMDS_PER_CU * (VGPRS_PER_SIMD_LANE // alloc) // waves
         by_lds = LDS_PER_CU // v["lds"] if v["lds"] else 8
-        if by_regs < min(by_lds, 8):
+        want = 1 if _loader_waves(name) else min(by_lds, 8)
+        if by_regs < want:
             bad[name] = dict(v, workgroups_by_registers=by_regs, workgroups_by_lds=by_lds)
     assert bad == {}
+
+
+def test_loader_wave_kernels_were_found(kernels):
+    assert sum(_loader_waves(k) for k in kernels if "gemm_kernel" in k) >= 8
