@@ -200,12 +200,13 @@ __device__ __forceinline__ void store16(void *p, u32x4 v) {
 // metadata travels with the stage).  PROD: the workgroup has as many
 // loader waves as compute waves; the loader waves issue every direct-to-LDS
 // load and the compute waves only read LDS and run the matrix instructions.
+// NLD (without PROD): only compute waves 0..NLD-1 issue the loads (0: all).
 template <int WM_, int WN_, int TM_, int TN_, int STAGES_, int GM_, bool NTS_, bool ROT_, int MP_ = 0,
-          bool PROD_ = false>
+          bool PROD_ = false, int NLD_ = 0>
 struct Cfg {
     static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_, STAGES = STAGES_, GM = GM_;
     static constexpr bool NTS = NTS_, ROT = ROT_, PROD = PROD_;
-    static constexpr int MP = MP_;
+    static constexpr int MP = MP_, NLD = NLD_;
 };
 
 template <int KIND, class CF>
@@ -243,18 +244,20 @@ struct Layout {
     // issues the same number of loads per stage and one counter value means
     // "stage complete" for all of them.
     static constexpr int MCH = M_BYTES / 256;
-    static constexpr int LA = A_STAGE / 1024 / NW;
-    static constexpr int LW = W_STAGE / 1024 / NW;
-    static constexpr int LM = MCH >= NW ? MCH / NW : (MCH > 0 ? 1 : 0);
+    // waves that issue the loads (the loader group, or the first NLD compute waves)
+    static constexpr int NL = CF::PROD || CF::NLD == 0 ? NW : CF::NLD;
+    static constexpr int LA = A_STAGE / 1024 / NL;
+    static constexpr int LW = W_STAGE / 1024 / NL;
+    static constexpr int LM = MCH >= NL ? MCH / NL : (MCH > 0 ? 1 : 0);
     static constexpr int L = LA + LW + LM;
-    static_assert(LA * NW * 1024 == A_STAGE && LW * NW * 1024 == W_STAGE && MCH * 256 == M_BYTES &&
-                      (MCH == 0 || MCH % NW == 0 || NW % MCH == 0),
+    static_assert(LA * NL * 1024 == A_STAGE && LW * NL * 1024 == W_STAGE && MCH * 256 == M_BYTES &&
+                      (MCH == 0 || MCH % NL == 0 || NL % MCH == 0),
                   "stage does not split evenly over the waves");
     // meta chunk of this wave's j-th meta load (no modulo unless chunks are
     // shared: on the 128 x 256 int8 tiles it cost the registers that keep
     // two workgroups per CU)
     static __device__ __forceinline__ int mchunk(int j, int wave) {
-        if constexpr (MCH >= NW) return j * NW + wave;
+        if constexpr (MCH >= NL) return j * NL + wave;
         else return wave % (MCH > 0 ? MCH : 1);
     }
     // word position of (row, w) inside a metadata block: XOR-swizzled so that
@@ -328,14 +331,14 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
     uint32_t oa[LY::LA];
 #pragma unroll
     for (int j = 0; j < LY::LA; ++j) {
-        const int byte = (j * LY::NW + wave) * 1024 + lane * 16;
+        const int byte = (j * LY::NL + wave) * 1024 + lane * 16;
         const int row = byte / 128, pos = (byte / 16) % 8;
         oa[j] = uint32_t(min(m0 + row, M - 1)) * uint32_t(a_row) + swz128(row, pos) * 16;
     }
     uint32_t ow[LY::LW];
 #pragma unroll
     for (int j = 0; j < LY::LW; ++j) {
-        const int byte = (j * LY::NW + wave) * 1024 + lane * 16;
+        const int byte = (j * LY::NL + wave) * 1024 + lane * 16;
         const int row = byte / WB, pos = (byte / 16) % (WB / 16);
         ow[j] = uint32_t(min(n0 + row, N - 1)) * uint32_t(w_row) + swzw<WB>(row, pos) * 16;
     }
@@ -386,14 +389,16 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
             }
         }
     };
+    const bool issuer = LY::NL == LY::NW || wave < LY::NL;  // (with PROD: the loaders)
     auto issue = [&](int s) {
+        if (!issuer) return;
         uint8_t *base = smem + (s % NB) * STAGE;
         const int sg = ks0 + ((s + rot < S) ? s + rot : s + rot - S);  // global K stage
 #pragma unroll
-        for (int j = 0; j < LY::LA; ++j) dma16(bufA, oa[j] + uint32_t(sg * 128), base + (j * LY::NW + wave) * 1024);
+        for (int j = 0; j < LY::LA; ++j) dma16(bufA, oa[j] + uint32_t(sg * 128), base + (j * LY::NL + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < LY::LW; ++j)
-            dma16(bufW, ow[j] + uint32_t(sg * WB), base + A_STAGE + (j * LY::NW + wave) * 1024);
+            dma16(bufW, ow[j] + uint32_t(sg * WB), base + A_STAGE + (j * LY::NL + wave) * 1024);
         if constexpr (LY::MP == 0) {
 #pragma unroll
             for (int j = 0; j < LY::LM; ++j)
@@ -634,8 +639,11 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 
 // Tile shapes (measured on MI355X at the ViT / BERT / ViT-Base shapes):
 //   Big    256 x 256, 8 waves of 64 tokens x 128 channels, one workgroup per
-//          CU with eight load-issuing waves -- best once there are about as
-//          many tiles as CUs and K is long enough to amortise the prologue;
+//          CU -- best once there are about as many tiles as CUs and K is long
+//          enough to amortise the prologue.  On the fp16 2:4 tile only waves
+//          0..3 issue the loads, so each SIMD keeps one wave whose matrix
+//          work no load waits behind (ViT-L qkv 27.5 -> 26.3 us, fc1 31.5 ->
+//          30.8; with two of the eight waves loading, no gain);
 //   Mid    128 x 256, 4 waves, 2 stages (two workgroups per CU) -- short-K
 //          int8 GEMMs with one to two such tiles per CU;
 //   Small  128 x 128, 4 waves, 3 stages (two workgroups per CU) -- long-K
@@ -698,8 +706,8 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 // 2:4 512 x 1024 x 3072 6.6 vs 6.9 us on 64 x 64; 32 x 32 with a 4-stage ring:
 // fp16 2:4 512 x 1024 x 1024 5.7 vs 6.5 us, int8 2:4 512 x 4096 x 1024 9.1 vs
 // 10.6 us against the rotated 3-stage form).
-template <bool NTS>
-using CfgBig = Cfg<4, 2, 2, 4, 3, 8, NTS, false>;
+template <bool NTS, int NLD = 0>
+using CfgBig = Cfg<4, 2, 2, 4, 3, 8, NTS, false, 0, false, NLD>;
 template <bool NTS>
 using CfgBigDense = Cfg<4, 2, 2, 4, 2, 8, NTS, false>;
 template <bool NTS>
@@ -778,7 +786,8 @@ static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const ui
                                const float *bias, void *C, int M, int N, int K, hipStream_t st, int splits = 1) {
     if (sh == SHAPE_BIG) {
         if constexpr (DENSE) return launch<KIND, EPI, CfgBigDense<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
-        else return launch<KIND, EPI, CfgBig<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
+        else return launch<KIND, EPI, CfgBig<NTS, KIND == W24_F16 ? 4 : 0>>(A, Wv, meta, scale, bias, C, M, N, K, st,
+                                                                          splits);
     }
     if (sh == SHAPE_MID) return launch<KIND, EPI, CfgMid<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     constexpr bool ROT = KindTraits<KIND>::kSparse;

@@ -13,8 +13,10 @@ that start at a rotated stage (every multi-tile sparse launch on these
 tiles), ragged M and N, explicit K splits (each split starts its blocks at
 its own first stage), one-hot weights (a metadata word read for the wrong
 row or stage selects the wrong activation column), and every int8 output
-kind.  Bars as in the other parity tests: int8 bit-exact, fp16 within the
-strict per-element bound, and bit-exact on exact-integer inputs.
+kind.  Also here: the fp16 2:4 256 x 256 tile, whose loads only its first
+four of eight waves issue.  Bars as in the other parity tests: int8
+bit-exact, fp16 within the strict per-element bound, and bit-exact on
+exact-integer inputs.
 """
 
 import numpy as np
@@ -55,7 +57,9 @@ F16_CASES = [(2000, 832, 1088, (128, 128)),   # 16 x 9 tiles, 13 stages: last bl
              (2000, 64, 1088, (128, 128)),    # a single stage
              (1300, 1024, 3008, (128, 128)),  # 11 x 24 tiles (264), 16 stages
              (1000, 704, 1088, (64, 128)),    # sparse 64 x 128 tile, 11 stages
-             (1000, 192, 1088, (64, 128))]    # 3 stages
+             (1000, 192, 1088, (64, 128)),    # 3 stages
+             (4000, 832, 3008, (256, 256)),   # 16 x 12 tiles of 256 x 256, half the waves load
+             (4000, 64, 3008, (256, 256))]    # a single stage
 
 
 @pytest.mark.parametrize("M,K,N,tile", F16_CASES)
@@ -65,7 +69,7 @@ def test_w24_f16_loader_tiles(lib, gpu, M, K, N, tile):
     _check_f16(_w24_f16(lib, case["A"], case["Wp"]), case["A"], case["Wp"], f"w24 f16 {M}x{K}x{N}")
 
 
-@pytest.mark.parametrize("M,K,N,tile", F16_CASES[:2] + F16_CASES[4:5])
+@pytest.mark.parametrize("M,K,N,tile", F16_CASES[:2] + F16_CASES[4:5] + F16_CASES[6:7])
 def test_w24_f16_loader_tiles_exact(lib, gpu, M, K, N, tile):
     assert lib.tile_choice(lib.SSG_KIND_W24_F16, M, N, K) == tile
     case = wl.exact_int_24_f16(np.random.default_rng(K + N), M, K, N)
@@ -74,7 +78,7 @@ def test_w24_f16_loader_tiles_exact(lib, gpu, M, K, N, tile):
     assert np.array_equal(C.view(np.uint16), C16.view(np.uint16))
 
 
-@pytest.mark.parametrize("M,K,N,tile", [F16_CASES[0], F16_CASES[4]])
+@pytest.mark.parametrize("M,K,N,tile", [F16_CASES[0], F16_CASES[4], F16_CASES[6]])
 def test_w24_f16_loader_tiles_one_hot(lib, gpu, M, K, N, tile):
     assert lib.tile_choice(lib.SSG_KIND_W24_F16, M, N, K) == tile
     case = wl.one_hot_24(np.random.default_rng(5), M, K, N)
