@@ -640,10 +640,13 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 // Tile shapes (measured on MI355X at the ViT / BERT / ViT-Base shapes):
 //   Big    256 x 256, 8 waves of 64 tokens x 128 channels, one workgroup per
 //          CU -- best once there are about as many tiles as CUs and K is long
-//          enough to amortise the prologue.  On the fp16 2:4 tile only waves
-//          0..3 issue the loads, so each SIMD keeps one wave whose matrix
-//          work no load waits behind (ViT-L qkv 27.5 -> 26.3 us, fc1 31.5 ->
-//          30.8; with two of the eight waves loading, no gain);
+//          enough to amortise the prologue.  On the fp16 2:4 tile and the
+//          dense tiles only waves 0..3 issue the loads, so each SIMD keeps
+//          one wave whose matrix work no load waits behind (fp16 2:4 ViT-L
+//          qkv 27.5 -> 26.3 us, fc1 31.5 -> 30.8; dense fp16 28.9 -> 28.1
+//          and 37.3 -> 36.2; with two of the eight waves loading, no gain;
+//          the int8 2:4 tile would spill, and the int8 Small2 tile with two
+//          of four waves loading ran the headline 46.0 -> 48.7 us);
 //   Mid    128 x 256, 4 waves, 2 stages (two workgroups per CU) -- short-K
 //          int8 GEMMs with one to two such tiles per CU;
 //   Small  128 x 128, 4 waves, 3 stages (two workgroups per CU) -- long-K
@@ -709,7 +712,7 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 template <bool NTS, int NLD = 0>
 using CfgBig = Cfg<4, 2, 2, 4, 3, 8, NTS, false, 0, false, NLD>;
 template <bool NTS>
-using CfgBigDense = Cfg<4, 2, 2, 4, 2, 8, NTS, false>;
+using CfgBigDense = Cfg<4, 2, 2, 4, 2, 8, NTS, false, 0, false, 4>;
 template <bool NTS>
 using CfgMid = Cfg<2, 2, 2, 4, 2, 8, NTS, false>;
 template <bool NTS, bool ROT>
