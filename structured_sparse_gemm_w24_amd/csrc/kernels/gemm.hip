@@ -192,10 +192,9 @@ __device__ __forceinline__ void store16(void *p, u32x4 v) {
 
 // Tile configuration: WM x WN waves, TM x TN 32x32 blocks per wave, STAGES
 // LDS stage buffers (prefetch distance), GM tile-rows per L2 group,
-// nontemporal C stores, ROT: each tile starts its K loop at its own stage.  Direct-to-LDS loads are issued by every wave: their
-// throughput is limited per wavefront (about 4 bytes per clock each on
-// gfx950), so a CU needs 8 or more issuing waves to feed the sparse matrix
-// cores.
+// nontemporal C stores, ROT: each tile starts its K loop at its own stage.
+// By default every wave issues an equal share of each stage's direct-to-LDS
+// loads.
 // MP: K stages per metadata block of the sparse kinds (0: each stage's
 // metadata travels with the stage).  PROD: the workgroup has as many
 // loader waves as compute waves; the loader waves issue every direct-to-LDS
