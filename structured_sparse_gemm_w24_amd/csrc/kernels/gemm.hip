@@ -654,8 +654,9 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 //   SmallP the same tile with 4 more waves that only load (one workgroup
 //          per CU) and, for the sparse kinds, metadata blocks of 4 (fp16) or
 //          2 (int8) stages -- narrow outputs (N = 1024) that would leave CUs
-//          idle with big tiles: every fp16 GEMM without enough Big tiles, and
-//          the long-K int8 ones up to 256 tiles (dense: 576).  Against Small,
+//          idle with big tiles: every fp16 GEMM without enough Big tiles
+//          (other than the few-tile ones of T64 / T32 below), and the long-K
+//          int8 ones up to 256 tiles (dense: 576).  Against Small,
 //          graph-timed on cold input sets: fp16 2:4 4096 x 1024 x 4096
 //          (M x N x K) 42.3 -> 38.9 us, 4096 x 768 x 3072 31.5 -> 28.4,
 //          6144 x 1024 x 4096 (384 tiles) 67.6 -> 63.4, 6144 x 1536 x 4096
