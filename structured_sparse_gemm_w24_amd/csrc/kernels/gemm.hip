@@ -112,11 +112,14 @@ struct KindTraits<W24_I8> {
 
 // 16-byte chunk swizzles (see header comment).
 __device__ __forceinline__ int swz128(int row, int col) { return col ^ ((row ^ (row >> 3)) & 7); }
+__device__ __forceinline__ int swz256(int row, int col) { return col ^ (row & 15); }
 __device__ __forceinline__ int swz64(int row, int col) { return col ^ (((row >> 1) ^ (row >> 3)) & 3); }
-template <int WB>
+// swizzle of a row of RB bytes (64, 128 or 256)
+template <int RB>
 __device__ __forceinline__ int swzw(int row, int col) {
-    if constexpr (WB == 64) return swz64(row, col);
-    else return swz128(row, col);
+    if constexpr (RB == 64) return swz64(row, col);
+    else if constexpr (RB == 128) return swz128(row, col);
+    else return swz256(row, col);
 }
 
 template <int KIND>
@@ -200,12 +203,13 @@ __device__ __forceinline__ void store16(void *p, u32x4 v) {
 // loader waves as compute waves; the loader waves issue every direct-to-LDS
 // load and the compute waves only read LDS and run the matrix instructions.
 // NLD (without PROD): only compute waves 0..NLD-1 issue the loads (0: all).
+// DK: K depth of a stage in units of 128 bytes of an A row.
 template <int WM_, int WN_, int TM_, int TN_, int STAGES_, int GM_, bool NTS_, bool ROT_, int MP_ = 0,
-          bool PROD_ = false, int NLD_ = 0>
+          bool PROD_ = false, int NLD_ = 0, int DK_ = 1>
 struct Cfg {
     static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_, STAGES = STAGES_, GM = GM_;
     static constexpr bool NTS = NTS_, ROT = ROT_, PROD = PROD_;
-    static constexpr int MP = MP_, NLD = NLD_;
+    static constexpr int MP = MP_, NLD = NLD_, DK = DK_;
 };
 
 template <int KIND, class CF>
@@ -215,9 +219,12 @@ struct Layout {
     static constexpr int NT = NW * kWave * (CF::PROD ? 2 : 1);  // threads
     static constexpr int BM = CF::WM * CF::TM * 32;
     static constexpr int BN = CF::WN * CF::TN * 32;
-    static constexpr int WB = KT::kWB;
-    static constexpr int MW = KT::kMW;
-    static constexpr int A_STAGE = BM * 128;
+    static constexpr int DK = CF::DK;
+    static constexpr int AB = 128 * DK;      // A bytes per row per stage
+    static constexpr int NI = KT::kNI * DK;  // matrix instructions (k-steps) per stage
+    static constexpr int WB = KT::kWB * DK;
+    static constexpr int MW = KT::kMW * DK;
+    static constexpr int A_STAGE = BM * AB;
     static constexpr int W_STAGE = BN * WB;
     static constexpr int M_BYTES = BN * MW * 4;  // metadata bytes of one stage
     // Metadata blocks (MP > 0): the metadata of MP consecutive stages sits
@@ -331,8 +338,8 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
 #pragma unroll
     for (int j = 0; j < LY::LA; ++j) {
         const int byte = (j * LY::NL + wave) * 1024 + lane * 16;
-        const int row = byte / 128, pos = (byte / 16) % 8;
-        oa[j] = uint32_t(min(m0 + row, M - 1)) * uint32_t(a_row) + swz128(row, pos) * 16;
+        const int row = byte / LY::AB, pos = (byte / 16) % (LY::AB / 16);
+        oa[j] = uint32_t(min(m0 + row, M - 1)) * uint32_t(a_row) + swzw<LY::AB>(row, pos) * 16;
     }
     uint32_t ow[LY::LW];
 #pragma unroll
@@ -394,7 +401,8 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
         uint8_t *base = smem + (s % NB) * STAGE;
         const int sg = ks0 + ((s + rot < S) ? s + rot : s + rot - S);  // global K stage
 #pragma unroll
-        for (int j = 0; j < LY::LA; ++j) dma16(bufA, oa[j] + uint32_t(sg * 128), base + (j * LY::NL + wave) * 1024);
+        for (int j = 0; j < LY::LA; ++j)
+            dma16(bufA, oa[j] + uint32_t(sg * LY::AB), base + (j * LY::NL + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < LY::LW; ++j)
             dma16(bufW, ow[j] + uint32_t(sg * WB), base + A_STAGE + (j * LY::NL + wave) * 1024);
@@ -437,11 +445,11 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
             const int row = wm * TM * 32 + tm * 32 + r;
             if constexpr (KT::kSparse) {
                 // two 16-byte pieces of the 64-byte window: bytes 16h.. and 32+16h..
-                const u32x4 lo = lds16(bA + row * 128 + swz128(row, 4 * kk + h) * 16);
-                const u32x4 hi = lds16(bA + row * 128 + swz128(row, 4 * kk + 2 + h) * 16);
+                const u32x4 lo = lds16(bA + row * LY::AB + swzw<LY::AB>(row, 4 * kk + h) * 16);
+                const u32x4 hi = lds16(bA + row * LY::AB + swzw<LY::AB>(row, 4 * kk + 2 + h) * 16);
                 F.a[tm] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             } else {
-                const u32x4 lo = lds16(bA + row * 128 + swz128(row, 2 * kk + h) * 16);
+                const u32x4 lo = lds16(bA + row * LY::AB + swzw<LY::AB>(row, 2 * kk + h) * 16);
                 F.a[tm] = __builtin_shufflevector(lo, lo, 0, 1, 2, 3, 0, 1, 2, 3);
             }
         }
@@ -504,10 +512,10 @@ gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ Wv, const
         // stage this reads a valid, stale buffer whose values are never used.
         auto stage = [&](int s, auto steady) {
 #pragma unroll
-            for (int kk = 0; kk < KT::kNI; ++kk) {
+            for (int kk = 0; kk < LY::NI; ++kk) {
                 Frag &cur = F[kk & 1];
                 Frag &nxt = F[(kk + 1) & 1];
-                if (kk + 1 < KT::kNI) {
+                if (kk + 1 < LY::NI) {
                     load_frag(s, kk + 1, nxt);
                 } else {
                     // stage s is fully in registers; stage s+1 must be complete
@@ -629,7 +637,7 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
                          const float *bias, void *C, int M, int N, int K, hipStream_t st, int splits = 1) {
     using LY = Layout<KIND, CF>;
     const int nb = ((M + LY::BM - 1) / LY::BM) * ((N + LY::BN - 1) / LY::BN);
-    const int stages = K * (KindTraits<KIND>::kI8 ? 1 : 2) / 128 / splits;
+    const int stages = K * (KindTraits<KIND>::kI8 ? 1 : 2) / (128 * CF::DK) / splits;
     hipLaunchKernelGGL((gemm_kernel<KIND, EPI, CF>), dim3(nb, splits), dim3(LY::NT), 0, st,
                        static_cast<const uint8_t *>(A), static_cast<const uint8_t *>(Wv), meta, scale, bias, C, M, N,
                        K, stages);
@@ -662,7 +670,12 @@ static hipError_t launch(const void *A, const void *Wv, const uint32_t *meta, co
 //          6144 x 1024 x 4096 (384 tiles) 67.6 -> 63.4, 6144 x 1536 x 4096
 //          (576) 96.8 -> 87.0; dense fp16 4096 x 1024 x 4096 43.1 -> 41.5;
 //          int8 2:4 4096 x 768 x 3072 17.5 -> 16.5 us, but 6144 x 1024 x
-//          4096 37.0 -> 39.0.  Neither part pays alone (fp16 2:4 4096 x 1024
+//          4096 37.0 -> 39.0.  The int8 2:4 tile (unsplit, K a multiple of
+//          256) takes stages twice as deep in K, 256 k with the metadata in
+//          the stage (int8 2:4 4096 x 1024 x 4096 23.5 -> 20.8 us, 4096 x
+//          768 x 3072 16.6 -> 16.0, 3072 x 1024 x 4096 20.7 -> 19.8); the
+//          fp16 tiles run slower so (4096 x 1024 x 4096 37.7 -> 43.6), and
+//          the dense ones, with two such stages, too.  Neither part pays alone (fp16 2:4 4096 x 1024
 //          x 4096: metadata blocks 46.6-46.9 us, loader waves 45-46, both
 //          41.5, Small 44.7-45.2 in that session): the metadata blocks cut
 //          the cache lines the loads touch (a copy of the kernel without
@@ -719,6 +732,8 @@ template <bool NTS, bool ROT>
 using CfgSmall = Cfg<2, 2, 2, 2, 3, 8, NTS, ROT>;
 template <bool NTS, bool ROT, int MP>
 using CfgSmallP = Cfg<2, 2, 2, 2, 3, 8, NTS, ROT, MP, true>;
+template <bool NTS, bool ROT>
+using CfgSmallPD2 = Cfg<2, 2, 2, 2, 3, 8, NTS, ROT, 0, true, 0, 2>;
 template <bool NTS, bool ROT>
 using CfgSmall2 = Cfg<2, 2, 2, 2, 2, 8, NTS, ROT>;
 template <bool NTS, bool ROT>
@@ -802,6 +817,10 @@ static hipError_t launch_shape(Shape sh, const void *A, const void *Wv, const ui
     }
     if (sh == SHAPE_T32) return launch<KIND, EPI, CfgT32<NTS>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     if (sh == SHAPE_SMALLP) {
+        // the int8 2:4 tile takes stages of 256 k when K allows (unsplit launches)
+        if constexpr (KIND == W24_I8 && EPI != EPI_PART)
+            if (K % 256 == 0)
+                return launch<KIND, EPI, CfgSmallPD2<NTS, ROT>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
         constexpr int MP = !KindTraits<KIND>::kSparse ? 0 : KindTraits<KIND>::kI8 ? 2 : 4;
         return launch<KIND, EPI, CfgSmallP<NTS, ROT, MP>>(A, Wv, meta, scale, bias, C, M, N, K, st, splits);
     }

@@ -13,8 +13,11 @@ that start at a rotated stage (every multi-tile sparse launch on these
 tiles), ragged M and N, explicit K splits (each split starts its blocks at
 its own first stage), one-hot weights (a metadata word read for the wrong
 row or stage selects the wrong activation column), and every int8 output
-kind.  Also here: the fp16 2:4 256 x 256 tile, whose loads only its first
-four of eight waves issue.  Bars as in the other parity tests: int8
+kind.  The int8 2:4 tile runs stages of 256 k when K is a multiple of 256
+(unsplit launches), of 128 k otherwise; both are covered, and the split
+launches (128-k stages) are checked against the unsplit call.  Also here:
+the fp16 2:4 256 x 256 tile, whose loads only its first four of eight
+waves issue.  Bars as in the other parity tests: int8
 bit-exact, fp16 within the strict per-element bound, and bit-exact on
 exact-integer inputs.
 """
@@ -104,9 +107,10 @@ def test_dense_f16_loader_tile(lib, gpu):
     _check_f16(C, case["A"], case["W"], "dense f16 loader tile", dense=True)
 
 
-# int8: K stages of 128 k; the long-K rules (K > 1024) pick these tiles
-I8_CASES = [(2000, 1152, 1088),   # 9 stages: last block of 2 partial
-            (2000, 1280, 1088)]   # 10 stages
+# int8: the long-K rules (K > 1024) pick these tiles
+I8_CASES = [(2000, 1152, 1088),   # 9 stages of 128 k: last metadata block of 2 partial
+            (2000, 1280, 1088),   # 5 stages of 256 k
+            (2000, 1536, 1088)]   # 6 stages of 256 k
 
 
 @pytest.mark.parametrize("out", ["i32", "f32", "f16", "i8"])

@@ -95,9 +95,9 @@ def test_no_kernel_spills_to_scratch(kernels):
     assert {k: v["scratch"] for k, v in kernels.items() if v["scratch"]} == {}
 
 
-# gemm_kernel<KIND, EPI, Cfg<WM, WN, TM, TN, STAGES, GM, NTS, ROT, MP, PROD, NLD>>:
+# gemm_kernel<KIND, EPI, Cfg<WM, WN, TM, TN, STAGES, GM, NTS, ROT, MP, PROD, NLD, DK>>:
 # PROD (a group of loader waves beside the compute waves) is the tenth argument
-_CFG = re.compile(r"CfgI(?:Li-?\d+E){6}(?:Lb[01]E){2}(?:Li-?\d+E)?(?:Lb([01])E)?(?:Li-?\d+E)?E")
+_CFG = re.compile(r"CfgI(?:Li-?\d+E){6}(?:Lb[01]E){2}(?:Li-?\d+E)?(?:Lb([01])E)?(?:Li-?\d+E){0,2}E")
 
 
 def _loader_waves(name):
