@@ -313,8 +313,9 @@ int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_k,
 
 /* Flags of tw_gemm_f16_ex. */
 enum {
-    SSG_TW_OUT_T = 1,     /* write C transposed: Ct [N][M], M contiguous            */
-    SSG_TW_A_ROWMAJOR = 2 /* the A argument is row-major A [M][K], not At [K][M]    */
+    SSG_TW_OUT_T = 1,      /* write C transposed: Ct [N][M], M contiguous            */
+    SSG_TW_A_ROWMAJOR = 2, /* the A argument is row-major A [M][K], not At [K][M]    */
+    SSG_TW_NARROW = 4      /* the caller promises every tile keeps <= 64 columns     */
 };
 
 /* Tile-wise GEMM over a range of tiles, optionally with transposed output.
@@ -333,6 +334,17 @@ enum {
  *     (16-byte aligned), read without a transpose: the slides' "without
  *     transpose" case, whose gathered activations are scattered 2-byte
  *     accesses (it exists to measure that cost; K-major At is the fast path).
+ *   - flags & SSG_TW_NARROW: the caller states that every tile it runs keeps
+ *     at most 64 columns (n_ptr[t+1] - n_ptr[t] <= 64; the host packer knows
+ *     this, the library cannot see it without reading device memory).  The
+ *     kernel then sizes its stage buffers and registers for 64 columns, so
+ *     more work items share a CU (and, in launches of at most two items per
+ *     CU with K-major At, M % 8 == 0, it takes 64 picked rows per stage).
+ *     Honoured for G <= 128 and ignored for wider tiles.  A tile that keeps
+ *     more than 64 columns despite the flag gets its whole output window
+ *     written as quiet NaN (0x7e00), never a partial or stale result.
+ *     Otherwise the results are bit-identical to the call without the flag:
+ *     the same matrix instructions run over the same k order.
  * Unknown flag bits or an empty or out-of-range tile range give SSG_EINVAL. */
 int tw_gemm_f16_ex(const void *At, const void *vals, const int32_t *offset_k,
                    const int32_t *offset_n, const int32_t *v_ptr, const int32_t *k_ptr,

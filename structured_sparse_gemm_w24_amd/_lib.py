@@ -185,6 +185,7 @@ class TwPacked:
     k_ptr: object
     n_ptr: object
     tile_order: object
+    max_nt: int = -1  # most kept columns of any tile (-1: not known)
 
     def arrays(self):
         return dict(vals=self.vals, offset_k=self.offset_k, offset_n=self.offset_n, v_ptr=self.v_ptr,
@@ -197,7 +198,12 @@ class TwPacked:
         def conv(a):
             t = torch.from_numpy(np.ascontiguousarray(a))
             return t.to(device) if t.numel() else torch.zeros(1, dtype=t.dtype, device=device)
-        return TwPacked(self.K, self.N, self.G, self.T, *[conv(a) for a in self.arrays().values()])
+        return TwPacked(self.K, self.N, self.G, self.T, *[conv(a) for a in self.arrays().values()],
+                        max_nt=self.max_nt)
+
+    def narrow(self):
+        """True when every tile is known to keep at most 64 columns (SSG_TW_NARROW)."""
+        return 0 <= self.max_nt <= 64
 
 
 def _tw_fns(dtype):
@@ -232,7 +238,8 @@ def _tw_pack(W, G, dt, q, pk):
     order = np.empty(sz.T, np.int32)
     _check(getattr(load(), pk)(_np_ptr(W), K, N, G, ct.byref(sz), _np_ptr(vals), _np_ptr(ok), _np_ptr(on),
                                _np_ptr(vp), _np_ptr(kp), _np_ptr(np_), _np_ptr(order)))
-    return TwPacked(K, N, G, int(sz.T), vals, ok, on, vp, kp, np_, order)
+    return TwPacked(K, N, G, int(sz.T), vals, ok, on, vp, kp, np_, order,
+                    max_nt=int(np.diff(np_).max()) if sz.T > 0 else 0)
 
 
 def tw_pack_f16(W, G):
@@ -553,7 +560,11 @@ def w24_gemm_i8_splitk(A, vals, meta, scale, bias=None, out_type="f16", splits=1
 
 
 def tw_gemm_f16(At, packed: TwPacked, out=None):
-    """Tile-wise GEMM; At [K, M] fp16 (K-major A), packed arrays on the device."""
+    """Tile-wise GEMM; At [K, M] fp16 (K-major A), packed arrays on the device.  When
+    the packer found every tile at most 64 columns wide, the call goes through
+    tw_gemm_f16_ex with SSG_TW_NARROW (the same result from the narrow-tile kernels)."""
+    if packed.narrow():
+        return tw_gemm_f16_ex(At, packed, out=out)
     torch = _torch()
     K, M = At.shape
     if K != packed.K:
@@ -601,11 +612,16 @@ SSG_TW_OUT_T = 1
 SSG_TW_A_ROWMAJOR = 2
 
 
-def tw_gemm_f16_ex(At, packed: TwPacked, t_first=0, t_count=None, out_t=False, a_rowmajor=False, out=None):
+SSG_TW_NARROW = 4
+
+
+def tw_gemm_f16_ex(At, packed: TwPacked, t_first=0, t_count=None, out_t=False, a_rowmajor=False, out=None,
+                   narrow=None):
     """Tile-wise GEMM over tiles tile_order[t_first : t_first + t_count]; with out_t the
     result is written transposed, Ct [N, M] (the K-major input of a next tile-wise layer).
     With a_rowmajor the first argument is row-major A [M, K] (the slides' "without
-    transpose" case).  Only the selected tiles' column windows of the output are written."""
+    transpose" case).  Only the selected tiles' column windows of the output are written.
+    narrow: pass SSG_TW_NARROW (None: when the packer found every tile <= 64 columns)."""
     torch = _torch()
     if a_rowmajor:
         M, K = At.shape
@@ -621,7 +637,10 @@ def tw_gemm_f16_ex(At, packed: TwPacked, t_first=0, t_count=None, out_t=False, a
     for key in ("offset_k", "offset_n", "v_ptr", "k_ptr", "n_ptr", "tile_order"):
         _dev(arrs[key], torch.int32, None, key)
     C = _out(out, (packed.N, M) if out_t else (M, packed.N), torch.float16, At)
-    flags = (SSG_TW_OUT_T if out_t else 0) | (SSG_TW_A_ROWMAJOR if a_rowmajor else 0)
+    if narrow is None:
+        narrow = packed.narrow()
+    flags = ((SSG_TW_OUT_T if out_t else 0) | (SSG_TW_A_ROWMAJOR if a_rowmajor else 0)
+             | (SSG_TW_NARROW if narrow else 0))
     with _on(At, C, *arrs.values()):
         _check(load().tw_gemm_f16_ex(_ptr(At), _ptr(arrs["vals"]), _ptr(arrs["offset_k"]), _ptr(arrs["offset_n"]),
                                      _ptr(arrs["v_ptr"]), _ptr(arrs["k_ptr"]), _ptr(arrs["n_ptr"]),

@@ -83,8 +83,9 @@ __device__ __forceinline__ void tw_read_b2(uint32_t addr, u32x2 &b0, u32x2 &b1) 
 
 // BK picked rows per stage (32 or 64), NB stage buffers, KCAP offset_k
 // entries held in LDS at a time, WPE waves per SIMD the register allocation
-// must allow (two workgroups per CU need 4), GMAX the widest tile.
-template <int BK_, int NB_, int KCAP_, int WPE_, int GMAX_ = 128>
+// must allow (two workgroups per CU need 4), GMAX the widest tile, NTMAX the
+// most kept columns of a tile (rows of a stage's V_t part).
+template <int BK_, int NB_, int KCAP_, int WPE_, int GMAX_ = 128, int NTMAX_ = GMAX_>
 struct TwCfg {
     static constexpr int NW = 8, NT = NW * 64;
     static constexpr int BM = 128;   // tokens per work item (8 blocks of 16)
@@ -93,9 +94,10 @@ struct TwCfg {
     static constexpr int NB = NB_;
     static constexpr int KCAP = KCAP_;
     static constexpr int WPE = WPE_;
-    static constexpr int GMAX = GMAX_;  // widest supported tile
-    static constexpr int A_STAGE = BK * BM * 2;    // [BK][BM] halves
-    static constexpr int W_STAGE = GMAX * BK * 2;  // [GMAX][BK] halves
+    static constexpr int GMAX = GMAX_;    // widest supported tile
+    static constexpr int NTMAX = NTMAX_;  // most kept columns per tile
+    static constexpr int A_STAGE = BK * BM * 2;     // [BK][BM] halves
+    static constexpr int W_STAGE = NTMAX * BK * 2;  // [NTMAX][BK] halves
     static constexpr int STAGE = A_STAGE + W_STAGE;
     static constexpr int LA = A_STAGE / 1024 / NW;  // A loads per wave per stage
     static constexpr int WROWS = 1024 / (BK * 2);   // V_t rows per direct-to-LDS load
@@ -106,7 +108,9 @@ struct TwCfg {
     static_assert(BK == 32 || BK == 64, "stage depth");
     static_assert(LA >= 1 && LA * NW * 1024 == A_STAGE, "A stage must split over the waves");
     static_assert(KCAP % NT == 0, "index chunk must split over the threads");
-    static_assert(BM * WIN_ROW <= NB * STAGE, "output window must fit in the stage ring");
+    // the output window may extend over the index chunk, which the epilogue no longer reads
+    static_assert(BM * WIN_ROW <= NB * STAGE + KCAP * 4, "output window must fit in the stage ring");
+    static_assert(NTMAX % 16 == 0 && NTMAX <= GMAX, "kept-column capacity");
     static_assert(NB >= 2 && NB <= 4, "ring depth");
 };
 
@@ -319,7 +323,8 @@ __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restric
     } else {
         // transposed window [G][BM]: row = tile-local channel, tokens contiguous
         constexpr int TROW = BM * 2 + 16;
-        static_assert(CF::GMAX * TROW <= CF::NB * CF::STAGE, "transposed window must fit in the stage ring");
+        static_assert(CF::GMAX * TROW <= CF::NB * CF::STAGE + CF::KCAP * 4,
+                      "transposed window must fit in the stage ring and index chunk");
         constexpr int TCH = BM / 8;  // 16-byte chunks per row
         for (int c = tid; c < G * TCH; c += NT)
             *reinterpret_cast<u32x4 *>(win + (c / TCH) * TROW + (c % TCH) * 16) = u32x4{0, 0, 0, 0};
@@ -354,6 +359,22 @@ __device__ __forceinline__ void tw_item(uint8_t *smem, const uint16_t *__restric
     }
 }
 
+// An item whose tile keeps more columns than the configuration holds (a
+// caller that promised narrow tiles and passed a wider one): its whole output
+// window is written as quiet NaN, so the broken promise shows in C instead of
+// leaving stale values there.
+template <class CF, bool OUTT>
+__device__ __forceinline__ void tw_nan_window(int G, int m0, uint16_t *__restrict__ Cw, int M, int N) {
+    constexpr uint16_t kNaN = 0x7e00;
+    const int tid = threadIdx.x;
+    const int rows = min(CF::BM, M - m0);
+    if constexpr (!OUTT) {
+        for (int c = tid; c < rows * G; c += CF::NT) Cw[int64_t(m0 + c / G) * N + c % G] = kNaN;
+    } else {
+        for (int c = tid; c < G * rows; c += CF::NT) Cw[int64_t(c / rows) * M + m0 + c % rows] = kNaN;
+    }
+}
+
 // Work items: token block mb x tiles tile_order[t_first .. t_first + t_count).
 template <class CF, bool OUTT, int AM>
 __global__ void __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(CF::WPE)))
@@ -378,8 +399,10 @@ tw_gemm_kernel(const uint16_t *__restrict__ At, const uint16_t *__restrict__ val
     switch ((nt + 15) >> 4) {
 #define TW_CASE(J) \
     case J:                                                                                  \
-        if constexpr (J <= CF::GMAX / 16)                                                    \
+        if constexpr (J <= CF::NTMAX / 16)                                                   \
             tw_item<CF, J, OUTT, AM>(smem, At, vt, offk, offn, kt, nt, G, m0, Cw, M, N, K); \
+        else                                                                                 \
+            tw_nan_window<CF, OUTT>(G, m0, Cw, M, N);                                        \
         break;
         TW_CASE(0) TW_CASE(1) TW_CASE(2) TW_CASE(3) TW_CASE(4) TW_CASE(5) TW_CASE(6) TW_CASE(7) TW_CASE(8)
         TW_CASE(9) TW_CASE(10) TW_CASE(11) TW_CASE(12) TW_CASE(13) TW_CASE(14) TW_CASE(15) TW_CASE(16)
@@ -394,6 +417,17 @@ using TwProd = TwCfg<32, 3, 512, 6>;
 // Tiles wider than 128 columns (up to 256): 75 KiB of LDS (two workgroups per
 // CU) and up to 16 column blocks of accumulators per wave.
 using TwWide = TwCfg<32, 3, 512, 4, 256>;
+// Narrow tiles (at most 64 kept columns, the caller's promise): the stage's
+// V_t part holds 64 rows and a wave at most 4 column blocks of accumulators,
+// which takes the kernel to 38.5 KiB of LDS and under 64 VGPRs, so four
+// workgroups share a CU (BERT-large fc1, 1536 items: 22.7 vs 24.1 us).
+using TwNarrow = TwCfg<32, 3, 512, 8, 128, 64>;
+// Narrow tiles in launches with at most two items per CU, where each item's
+// chain of K stages sets the time rather than the items sharing a CU:
+// 64-row stages halve the chain (two buffers, 50.5 KiB, three workgroups per
+// CU; BERT-large fc2, 384 items of 1311 picked rows: 22.0 vs 25.8 us).
+using TwNarrowDeep = TwCfg<64, 2, 512, 6, 128, 64>;
+constexpr int kTwCUs = 256;  // compute units of an MI355X
 
 template <class CF>
 static hipError_t launch_tw_cfg(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
@@ -402,10 +436,13 @@ static hipError_t launch_tw_cfg(const void *At, const void *vals, const int32_t 
                                 bool a_rowmajor, void *C, int M, int N, int K, hipStream_t st) {
     const int n_mb = (M + CF::BM - 1) / CF::BM;
     const int am = a_rowmajor ? A_ROW : (M % 8 ? A_KGATH : A_DMA);
-    auto kern = out_t ? (am == A_ROW ? tw_gemm_kernel<CF, true, A_ROW>
-                         : am == A_KGATH ? tw_gemm_kernel<CF, true, A_KGATH> : tw_gemm_kernel<CF, true, A_DMA>)
-                      : (am == A_ROW ? tw_gemm_kernel<CF, false, A_ROW>
-                         : am == A_KGATH ? tw_gemm_kernel<CF, false, A_KGATH> : tw_gemm_kernel<CF, false, A_DMA>);
+    auto kern = out_t ? tw_gemm_kernel<CF, true, A_DMA> : tw_gemm_kernel<CF, false, A_DMA>;
+    if constexpr (CF::BK == 32) {  // the register gathers are written for 32-row stages
+        if (am == A_ROW) kern = out_t ? tw_gemm_kernel<CF, true, A_ROW> : tw_gemm_kernel<CF, false, A_ROW>;
+        if (am == A_KGATH) kern = out_t ? tw_gemm_kernel<CF, true, A_KGATH> : tw_gemm_kernel<CF, false, A_KGATH>;
+    } else if (am != A_DMA) {
+        return hipErrorInvalidValue;
+    }
     hipLaunchKernelGGL(kern, dim3(n_mb * t_count), dim3(CF::NT), 0, st, static_cast<const uint16_t *>(At),
                        static_cast<const uint16_t *>(vals), offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order,
                        t_first, t_count, G, static_cast<uint16_t *>(C), M, N, K);
@@ -415,7 +452,16 @@ static hipError_t launch_tw_cfg(const void *At, const void *vals, const int32_t 
 hipError_t launch_tw_f16(const void *At, const void *vals, const int32_t *offset_k, const int32_t *offset_n,
                          const int32_t *v_ptr, const int32_t *k_ptr, const int32_t *n_ptr,
                          const int32_t *tile_order, int t_first, int t_count, int G, bool out_t, bool a_rowmajor,
-                         void *C, int M, int N, int K, hipStream_t st) {
+                         bool narrow, void *C, int M, int N, int K, hipStream_t st) {
+    if (narrow && G <= TwNarrow::GMAX) {
+        const int64_t items = int64_t((M + TwNarrow::BM - 1) / TwNarrow::BM) * t_count;
+        // (the 64-row stages take only the direct-to-LDS gather of 16-byte aligned At rows)
+        if (!a_rowmajor && M % 8 == 0 && items <= 2 * kTwCUs)
+            return launch_tw_cfg<TwNarrowDeep>(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order,
+                                               t_first, t_count, G, out_t, false, C, M, N, K, st);
+        return launch_tw_cfg<TwNarrow>(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, t_first,
+                                       t_count, G, out_t, a_rowmajor, C, M, N, K, st);
+    }
     if (G > TwProd::GMAX)
         return launch_tw_cfg<TwWide>(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, t_first,
                                      t_count, G, out_t, a_rowmajor, C, M, N, K, st);

@@ -75,7 +75,8 @@ def has_device(lib):
     (lambda r: r.dense_gemm_i8_out(*[_p(16)] * 4, _p(16), 1, 8, 64, 100, None), "multiple of 128"),
     (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 1, 2, 0, _p(16), 8, 32, 64, None), "tile range"),
     (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 0, 0, _p(16), 8, 32, 64, None), "tile range"),
-    (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 2, 4, _p(16), 8, 32, 64, None), "unknown flags"),
+    (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 2, 8, _p(16), 8, 32, 64, None), "unknown flags"),
+    (lambda r: r.tw_gemm_f16_ex(*[_p(16)] * 8, 2, 16, 0, 2, 4 | 16, _p(16), 8, 32, 64, None), "unknown flags"),
     (lambda r: r.tw_gemm_i8(*[_p(16)] * 8, 2, 272, _p(16), None, _p(16), 2, 24, 544, 64, None), "at most 256"),
     (lambda r: r.tw_gemm_i8(*[_p(16)] * 8, 2, 16, None, None, _p(16), 2, 32, 32, 64, None), "needs scale"),
     (lambda r: r.tw_gemm_f16(*[_p(16)] * 8, 2, 24, _p(16), 8, 48, 64, None), "G=24"),
