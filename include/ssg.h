@@ -339,7 +339,8 @@ enum {
  *     this, the library cannot see it without reading device memory).  The
  *     kernel then sizes its stage buffers and registers for 64 columns, so
  *     more work items share a CU (and, in launches of at most two items per
- *     CU with K-major At, M % 8 == 0, it takes 64 picked rows per stage).
+ *     CU with K >= 2048, K-major At and M % 8 == 0, it takes 64 picked rows
+ *     per stage).
  *     Honoured for G <= 128 and ignored for wider tiles.  A tile that keeps
  *     more than 64 columns despite the flag gets its whole output window
  *     written as quiet NaN (0x7e00), never a partial or stale result.

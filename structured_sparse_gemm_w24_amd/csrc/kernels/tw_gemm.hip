@@ -422,10 +422,12 @@ using TwWide = TwCfg<32, 3, 512, 4, 256>;
 // which takes the kernel to 38.5 KiB of LDS and under 64 VGPRs, so four
 // workgroups share a CU (BERT-large fc1, 1536 items: 22.7 vs 24.1 us).
 using TwNarrow = TwCfg<32, 3, 512, 8, 128, 64>;
-// Narrow tiles in launches with at most two items per CU, where each item's
-// chain of K stages sets the time rather than the items sharing a CU:
-// 64-row stages halve the chain (two buffers, 50.5 KiB, three workgroups per
-// CU; BERT-large fc2, 384 items of 1311 picked rows: 22.0 vs 25.8 us).
+// Narrow tiles in launches with at most two items per CU and a long K, where
+// each item's chain of K stages sets the time rather than the items sharing a
+// CU: 64-row stages halve the chain (two buffers, 50.5 KiB, three workgroups
+// per CU; BERT-large fc2, 384 items of 1311 picked rows: 22.0 vs 25.8 us).
+// With short chains the single buffer in flight costs more than the halving
+// gains (BERT-large fc1 as one 48-item launch per tile: 120 vs 94 us).
 using TwNarrowDeep = TwCfg<64, 2, 512, 6, 128, 64>;
 constexpr int kTwCUs = 256;  // compute units of an MI355X
 
@@ -456,7 +458,7 @@ hipError_t launch_tw_f16(const void *At, const void *vals, const int32_t *offset
     if (narrow && G <= TwNarrow::GMAX) {
         const int64_t items = int64_t((M + TwNarrow::BM - 1) / TwNarrow::BM) * t_count;
         // (the 64-row stages take only the direct-to-LDS gather of 16-byte aligned At rows)
-        if (!a_rowmajor && M % 8 == 0 && items <= 2 * kTwCUs)
+        if (!a_rowmajor && M % 8 == 0 && items <= 2 * kTwCUs && K >= 2048)
             return launch_tw_cfg<TwNarrowDeep>(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order,
                                                t_first, t_count, G, out_t, false, C, M, N, K, st);
         return launch_tw_cfg<TwNarrow>(At, vals, offset_k, offset_n, v_ptr, k_ptr, n_ptr, tile_order, t_first,

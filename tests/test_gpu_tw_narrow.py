@@ -65,11 +65,16 @@ def items(M, T_):
 SHAPES = [(1, 256, 256, 128, [0.1, 0.2]), (17, 300, 256, 64, [0.5, 0.9, 0.2, 1.0]),
           (129, 512, 384, 128, [0.05, 0.25, 0.15]), (200, 96, 128, 32, [1.0, 0.0, 0.5, 0.3]),
           (256, 768, 512, 128, [0.1, 0.2, 0.25, 0.02]), (4096 + 136, 512, 1024, 128, 0.1),
-          (8192 + 8, 256, 1024, 64, 0.3)]
+          (8192 + 8, 256, 1024, 64, 0.3), (1024, 2048, 512, 128, [0.05, 0.1, 0.2, 0.15]),
+          (264, 4096, 256, 64, [0.1, 0.3, 0.02, 0.5])]
+
+
+def deep_form(M, K, N, G):
+    return items(M, N // G) <= 2 * N_CUS and M % 8 == 0 and K >= 2048
 
 
 def test_shapes_cover_both_narrow_forms():
-    deep = [items(M, N // G) <= 2 * N_CUS and M % 8 == 0 for M, K, N, G, d in SHAPES]
+    deep = [deep_form(M, K, N, G) for M, K, N, G, d in SHAPES]
     assert any(deep) and not all(deep)
 
 
@@ -96,7 +101,8 @@ def test_narrow_transposed_output(lib, gpu, M, K, N, G, d):
 @pytest.mark.parametrize("M,K,N,G,d", [(17, 300, 256, 64, [0.5, 0.9, 0.2, 1.0]),
                                        (136, 512, 384, 128, [0.05, 0.2, 0.1]),
                                        (2048, 640, 512, 128, [0.2, 0.1, 0.15, 0.05]),
-                                       (6000, 320, 2048, 128, 0.2)])  # 752 items: the four-per-CU form
+                                       (6000, 320, 2048, 128, 0.2),  # 752 items: the four-per-CU form
+                                       (512, 2048, 256, 64, [0.02, 0.01, 0.02, 0.015])])  # 64-row stages
 def test_narrow_exact_integers(lib, gpu, M, K, N, G, d):
     ex = wl.exact_int_tw_f16(np.random.default_rng(M + 7), M, K, N, G, d)
     assert np.diff(oracle.ref_tw_pack(ex["Wp"], G)["k_ptr"]).max() <= 341  # every partial sum stays exact
@@ -111,8 +117,7 @@ def test_narrow_exact_integers(lib, gpu, M, K, N, G, d):
 def test_narrow_bert_large_ffn(lib, gpu, which):
     # fc1: 1536 items (the four-per-CU form); fc2: 384 items (64-row stages)
     c = wl.make_bert_large_ffn_tw()[which]
-    n_items = items(c["M"], c["N"] // c["G"])
-    assert (n_items <= 2 * N_CUS) == (which == "fc2")
+    assert deep_form(c["M"], c["K"], c["N"], c["G"]) == (which == "fc2")
     (Cn, Cg), packed = run_both(lib, c["A"], c["Wp"], c["G"])
     assert packed.max_nt == 40
     assert np.array_equal(Cn.view(np.uint16), Cg.view(np.uint16))
@@ -134,12 +139,12 @@ def test_narrow_row_major_a(lib, gpu):
     assert oracle.loose_err(Cr, C_ref) <= 1e-2
 
 
-@pytest.mark.parametrize("M", [64, 5504 + 8])  # 12 items (64-row stages); 528 items (four per CU)
-def test_narrow_flag_with_a_wide_tile_gives_nan_window(lib, gpu, M):
+@pytest.mark.parametrize("M,K", [(64, 2048), (64, 256), (5504 + 8, 256)])  # 64-row stages; four per CU
+def test_narrow_flag_with_a_wide_tile_gives_nan_window(lib, gpu, M, K):
     # tile 1 keeps 128 columns (density 1.0) although the caller promises <= 64:
     # its whole window is NaN; the narrow tiles around it are computed normally
     import torch
-    G, K, N = 128, 256, 12 * 128
+    G, N = 128, 12 * 128
     case = wl.random_tw_f16(np.random.default_rng(M), M, K, N, G, [0.1, 1.0] + [0.2] * 10)
     packed = lib.tw_pack_f16(case["Wp"], G)
     assert np.diff(packed.n_ptr).tolist()[1] == 128
