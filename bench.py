@@ -556,7 +556,8 @@ def tw_case(torch, ssg, perf, c, steps, warmup, timer, rotate=True, extras=True)
     out = dict(t_sparse_ms=st["ms"], t_sparse_p10_ms=st["p10"], t_sparse_p90_ms=st["p90"],
                t_transpose_ms=timer(tr, steps, warmup), t_dense_ms=timer(de, steps, warmup),
                t_torch_ms=timer(tm, steps, warmup), rotate_sets=R, bytes=bytes_, ops=perf.tw_ops(M, nnz),
-               union_rows=union, t_pack_host_ms=t_pack)
+               union_rows=union, t_pack_host_ms=t_pack, max_kept_columns=host.max_nt,
+               tw_kernel="narrow (SSG_TW_NARROW)" if host.narrow() and G <= 128 else "general")
     if not extras:
         return out
     # fused transpose: the same GEMM writing Ct [N][M], the next tile-wise layer's At
