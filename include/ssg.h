@@ -305,7 +305,10 @@ int w24_gemm_f16_splitk_static(const void *A, const void *vals, const uint32_t *
  * is not a multiple of 8 the rows of At are not 16-byte aligned and the
  * kernel gathers them through registers (slower than the direct-to-LDS
  * loads of the aligned case); tiles wider than 128 columns run a wider
- * configuration (two workgroups per CU instead of three). */
+ * configuration (two workgroups per CU instead of three).  A caller that
+ * knows every tile keeps at most 64 columns gets the faster narrow-tile
+ * kernels through tw_gemm_f16_ex with SSG_TW_NARROW (same result, bit for
+ * bit). */
 int tw_gemm_f16(const void *At, const void *vals, const int32_t *offset_k,
                 const int32_t *offset_n, const int32_t *v_ptr, const int32_t *k_ptr,
                 const int32_t *n_ptr, const int32_t *tile_order, int32_t T, int32_t G,
