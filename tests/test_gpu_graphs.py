@@ -135,6 +135,17 @@ def test_graph_tw_f16(lib, gpu):
                    lambda x, out=None: lib.tw_gemm_f16(x["At"], p, out=out))
 
 
+@pytest.mark.parametrize("K", [768, 2048])  # narrow-tile kernels: 32-row stages; 64-row stages (K >= 2048)
+@pytest.mark.parametrize("out_t", [False, True])
+def test_graph_tw_f16_narrow(lib, gpu, K, out_t):
+    M, N, G = 256, 384, 128
+    W = wl.prune_tilewise(wl.f16_normal(np.random.default_rng(110), (K, N), 0.02), G, [0.2, 0.1, 0.25])
+    p = lib.tw_pack_f16(W, G).to("cuda")
+    assert p.narrow()
+    _graph_replays(lambda s: {"At": _dev(np.ascontiguousarray(_f16(s, (M, K)).T))},
+                   lambda x, out=None: lib.tw_gemm_f16_ex(x["At"], p, out_t=out_t, out=out))
+
+
 @pytest.mark.parametrize("mode", ["out_t", "a_rowmajor"])
 def test_graph_tw_f16_ex(lib, gpu, mode):
     M, K, N, G = 200, 512, 384, 128
