@@ -327,6 +327,77 @@ def rotation(bytes_per_set):
 _VENDOR = []
 
 
+# ---------------------------------------------------------------- measured matrix-core rates
+_PEAK = []
+# (name, kind of the probe, dense-equivalent operations per instruction)
+PEAK_KINDS = (("dense_f16", 0, 32768), ("w24_f16", 1, 65536), ("dense_i8", 2, 65536), ("w24_i8", 3, 131072))
+
+
+def mfma_peak_measured(torch, iters=1000, blocks=1536, reps=5, warm_s=0.3):
+    """The rate this device sustains for each matrix instruction the GEMMs use
+    (dense-equivalent TFLOP/s or TOPS), from libssg_peak.so (bench only: every
+    wave issues the instruction back to back on four independent accumulators;
+    1536 workgroups of 256 threads, `iters` x 4 instructions per wave).  Each kind
+    runs warm for `warm_s` seconds, then `reps` launches are timed with HIP events
+    on the current stream and the median is kept.  None when the probe library
+    is missing or fails."""
+    if _PEAK:
+        return _PEAK[0]
+    import ctypes as ct
+    path = os.path.join(ROOT, "structured_sparse_gemm_w24_amd", "libssg_peak.so")
+    res = None
+    if os.path.exists(path):
+        try:
+            lib = ct.CDLL(path)
+            fn = lib.ssg_bench_mfma_peak
+            fn.restype = ct.c_int
+            fn.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_void_p, ct.c_void_p]
+            out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            st = torch.cuda.current_stream()
+            res = {}
+            for name, kind, ops in PEAK_KINDS:
+                def launch():
+                    rc = fn(kind, iters, blocks, ct.c_void_p(out.data_ptr()), ct.c_void_p(st.cuda_stream))
+                    if rc:
+                        raise RuntimeError(f"probe launch status {rc}")
+                t0 = time.perf_counter()
+                while time.perf_counter() - t0 < warm_s:
+                    launch()
+                    torch.cuda.synchronize()
+                times = []
+                for _ in range(reps):
+                    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    s0.record()
+                    launch()
+                    s1.record()
+                    torch.cuda.synchronize()
+                    times.append(s0.elapsed_time(s1) * 1e-3)
+                res[name] = blocks * 4 * iters * 4 * ops / float(np.median(times)) / 1e12
+            res["unit"] = "dense-equivalent TFLOP/s (fp16) / TOPS (int8)"
+            res["source"] = (f"libssg_peak.so: {blocks} workgroups x 4 waves, each issuing {iters * 4} back-to-back "
+                             f"instructions on 4 accumulators; median of {reps} launches after {warm_s:g} s warm")
+        except (OSError, RuntimeError, AttributeError) as e:
+            log(f"matrix-core rate probe not used: {e}")
+            res = None
+    _PEAK.append(res)
+    return res
+
+
+def measured_mfma_frac(d, peak):
+    """For a table line of a 2:4 or tile-wise GEMM: the fraction of the measured
+    matrix-core rate its kernel reached (ideal time at the measured rate / time)."""
+    if not peak or "t_sparse_ms" not in d:
+        return None
+    w = d.get("workload", "")
+    if "tflops_dense_eq" in d and w.endswith("_w24_f16"):
+        return d["tflops_dense_eq"] / peak["w24_f16"]
+    if "tops_dense_eq" in d and "_w24_i8" in w:
+        return d["tops_dense_eq"] / peak["w24_i8"]
+    if "tflops_nonzero" in d and w.endswith("_tw_f16"):  # the tile-wise kernel runs dense instructions
+        return d["tflops_nonzero"] / peak["dense_f16"]
+    return None
+
+
 def vendor_lib():
     """AMD's hipSPARSELt through libssg_vendor.so (built beside libssg when the
     hipSPARSELt headers are installed), or None.  Bench only: the product never
@@ -701,6 +772,7 @@ def main(argv=None):
     bytes_ = perf.w24_bytes(M, N, K, 1, 1, 4, scale=True)
     achieved = bytes_ / t / 1e9
     traffic = read_traffic()
+    peak = mfma_peak_measured(torch) if not a.eager else None
     line = {
         "metric": METRIC,
         "value": nz / t / 1e12,
@@ -736,6 +808,8 @@ def main(argv=None):
         "eager_ms_per_step": t_eager,
         "sclk": sclk,
         "roofline": perf.roofline(achieved, perf.PEAK_HBM_GBS, "GB/s", "hbm", traffic),
+        "mfma_peak_measured": peak,
+        "mfma_frac_of_measured_peak": (de / t / 1e12 / peak["w24_i8"]) if peak else None,
         "cpu_baseline": None,
     }
     # one more launch of the timed step on set 0 (the dense timing shares the
@@ -1050,9 +1124,16 @@ def table(a, torch, ssg, perf, wl, timer):
 
     vendor = not a.no_vendor
 
+    peak = mfma_peak_measured(torch)
+    if peak:
+        print(json.dumps(dict(workload="mfma_peak_measured", **peak)), flush=True)
+
     def emit(d):
         if "t_vendor_sparse_ms" in d:
             d["speedup_vs_vendor_sparse"] = d["t_vendor_sparse_ms"] / d["t_sparse_ms"]
+        f = measured_mfma_frac(d, peak)
+        if f is not None:
+            d["mfma_frac_of_measured_peak"] = f
         print(json.dumps(d), flush=True)
 
     if "small" in want:

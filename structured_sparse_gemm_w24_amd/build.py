@@ -72,6 +72,7 @@ def build(jobs=8, save_temps=False, verbose=False):
           *[_obj(s) for s in HOST_SOURCES + HIP_SOURCES]])
     os.replace(tmp, LIB)
     build_vendor()
+    build_peak()
     return LIB
 
 
@@ -96,6 +97,23 @@ def build_vendor():
         return None
     os.replace(tmp, VENDOR_LIB)
     return VENDOR_LIB
+
+
+PEAK_LIB = os.path.join(PKG, "libssg_peak.so")
+
+
+def build_peak():
+    """The bench's matrix-core rate probe (a separate library that libssg never
+    loads).  A failure here is reported and leaves the product build alone (the
+    bench then reports no measured MFMA peak)."""
+    tmp = PEAK_LIB + ".tmp"
+    try:
+        _run([HIPCC, *HIP_FLAGS, "-shared", os.path.join(CSRC, "bench", "mfma_peak.hip"), "-o", tmp])
+    except RuntimeError as e:
+        print(f"note: matrix-core rate probe not built ({str(e).splitlines()[0]})", file=sys.stderr)
+        return None
+    os.replace(tmp, PEAK_LIB)
+    return PEAK_LIB
 
 
 def main(argv=None):

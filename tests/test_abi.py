@@ -251,6 +251,32 @@ def test_vendor_baseline_is_outside_the_product():
         assert "libssg_vendor" not in text and "hipsparselt" not in text.lower(), path
 
 
+def test_mfma_peak_probe_is_outside_the_product():
+    """The bench's matrix-core rate probe is a separate library with one export;
+    libssg neither exports it nor names the probe library."""
+    import ctypes as ct
+    import glob
+    import subprocess
+    import structured_sparse_gemm_w24_amd as ssg
+    pkg = os.path.dirname(ssg.__file__)
+    probe = os.path.join(pkg, "libssg_peak.so")
+    assert os.path.exists(probe), "build() builds the probe beside libssg"
+    syms = subprocess.run(["nm", "-D", "--defined-only", probe], capture_output=True, text=True).stdout
+    assert "ssg_bench_mfma_peak" in syms
+    main = subprocess.run(["nm", "-D", "--defined-only", os.path.join(pkg, "libssg.so")],
+                          capture_output=True, text=True).stdout
+    assert "ssg_bench_mfma_peak" not in main
+    for path in glob.glob(os.path.join(pkg, "*.py")) + glob.glob(os.path.join(pkg, "csrc", "*.*")) + \
+            glob.glob(os.path.join(pkg, "csrc", "kernels", "*.*")):
+        if path.endswith("build.py"):
+            continue
+        assert "libssg_peak" not in open(path, errors="replace").read(), path
+    # invalid arguments are refused before any launch (no device needed for that)
+    fn = ct.CDLL(probe).ssg_bench_mfma_peak
+    fn.argtypes = [ct.c_int, ct.c_int, ct.c_int, ct.c_void_p, ct.c_void_p]
+    assert fn(4, 1, 1, None, None) != 0 and fn(0, 0, 1, None, None) != 0
+
+
 def test_single_hip_runtime_after_load():
     """Loading the library (before anything touched torch) leaves one HIP
     runtime in the process: the binding imports torch first, so the library
