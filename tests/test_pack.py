@@ -179,3 +179,18 @@ def test_tw_unpack_rejects_bad_prefix_sums_and_lengths(lib):
     ptrs[1] = None
     rc = raw.tw_unpack_f16(*ptrs, 32, 32, 16, W.ctypes.data_as(ct.c_void_p))
     assert rc == 1 and "null array" in raw.ssg_last_error().decode()
+
+
+@pytest.mark.parametrize("G,d,narrow", [(128, [0.1, 0.25], True), (128, [0.1, 0.26], False),
+                                        (64, [1.0, 0.5], True), (32, 1.0, True), (256, [0.05, 0.06], True),
+                                        (128, [0.0, 0.0], True)])
+def test_tw_pack_reports_widest_tile(lib, G, d, narrow):
+    """The host pack records the most kept columns of any tile (what the binding's
+    SSG_TW_NARROW choice rests on): max over tiles of n_ptr[t+1] - n_ptr[t]."""
+    case = wl.random_tw_f16(np.random.default_rng(G), 16, 256, 2 * G, G, d)
+    packed = lib.tw_pack_f16(case["Wp"], G)
+    ref = oracle.ref_tw_pack(case["Wp"], G)
+    assert packed.max_nt == int(np.diff(ref["n_ptr"]).max())
+    assert packed.narrow() == narrow == (packed.max_nt <= 64)
+    # a hand-built pack with no column count known takes the general path
+    assert not lib.TwPacked(packed.K, packed.N, packed.G, packed.T, *packed.arrays().values()).narrow()
